@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for every workload (no arithmetic of the method).
+
+Both the HIP path and the float64 oracle receive tensors made here; this module
+computes no attention, lambda or normalisation.  All draws come from a CPU
+torch.Generator seeded per call, in a fixed order:
+q1, k1, q2, k2, v, then the four lambda vectors (lq1, lk1, lq2, lk2), then the
+upstream gradient dy; for the V2 decode: q, k_cache, v_cache, lam.
+Each tensor is drawn in float32 one batch entry at a time, multiplied by its
+scale, and (for bf16 workloads) rounded once to bfloat16 (round to nearest
+even).  The oracle upcasts those same rounded values exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+__all__ = ["AttnConfig", "DecodeConfig", "CONFIGS", "make_attn_inputs",
+           "make_decode_inputs", "worked_example_inputs"]
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnConfig:
+    """A DIFF V1 attention workload ([batch, seq, head, channel] layout)."""
+    name: str
+    batch: int
+    seqlen: int
+    heads: int
+    head_dim: int
+    v_dim: int
+    dtype: torch.dtype
+    causal: bool
+    layer: int                 # layer index l >= 1 for lambda_init
+    input_scale: float         # q/k/v ~ N(0, 1) * input_scale
+    lambda_vec_dim: int = 0    # 0: lambda fixed at lambda_fixed
+    lambda_vec_std: float = 0.1
+    lambda_fixed: float = 0.8
+    with_dy: bool = False      # draw an upstream gradient dy ~ N(0, 1)
+    eps: float = 1e-5
+
+    @property
+    def pairs(self) -> int:
+        """(query, key) pairs per (batch, head) that the mask leaves in."""
+        s = self.seqlen
+        return s * (s + 1) // 2 if self.causal else s * s
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    """A DIFF V2 decode workload: one query token per sequence."""
+    name: str
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    kv_len: int
+    dtype: torch.dtype
+    input_scale: float
+    lam_shape: str = "per_head"   # "per_head" ([Hq/2]) or "per_batch_head"
+
+
+CONFIGS = {
+    # Tiny single-head check in float32 (lambda fixed at 0.8, layer 1).
+    "tiny_f32": AttnConfig("tiny_f32", 1, 64, 1, 8, 16, torch.float32, True, 1, 1.0),
+    # 3B-class layer forward: 12 heads, d 64, value width 128, 4K causal.
+    "prefill_4k": AttnConfig("prefill_4k", 4, 4096, 12, 64, 128, torch.bfloat16, True, 12,
+                             1.0 / math.sqrt(64), lambda_vec_dim=64),
+    # Long-context forward: 64K causal, 16 heads.
+    "prefill_64k": AttnConfig("prefill_64k", 1, 65536, 16, 64, 128, torch.bfloat16, True, 24,
+                              1.0 / 8.0, lambda_vec_dim=64),
+    # Training step (forward + backward) at 8K, 16 heads.
+    "train_8k": AttnConfig("train_8k", 2, 8192, 16, 64, 128, torch.bfloat16, True, 12,
+                           1.0 / 8.0, lambda_vec_dim=64, with_dy=True),
+    # DIFF V2 decode: 32 query heads over 16 KV heads, cache length 8192.
+    "v2_decode": DecodeConfig("v2_decode", 64, 32, 16, 128, 8192, torch.bfloat16,
+                              1.0 / math.sqrt(128)),
+}
+
+
+def _draw(gen: torch.Generator, shape, scale: float, dtype: torch.dtype) -> torch.Tensor:
+    """N(0, 1) * scale, drawn in float32 per leading index, cast once to dtype."""
+    out = torch.empty(shape, dtype=dtype)
+    for i in range(shape[0]):
+        x = torch.randn(shape[1:], generator=gen, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        out[i] = x.to(dtype)
+    return out
+
+
+def make_attn_inputs(cfg: AttnConfig | str, seed: int = 0, *, seqlen: int | None = None,
+                     batch: int | None = None, heads: int | None = None) -> dict:
+    """Inputs of a DIFF V1 workload on the CPU.
+
+    Optional overrides shrink a workload (same recipe, fewer rows) for tests.
+    Returns q1, k1, q2, k2 [B,S,H,d]; v [B,S,H,dv]; lambda_vecs (four float32
+    vectors) or None; dy [B,S,H,dv] or None; and the config itself.
+    """
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    B = cfg.batch if batch is None else batch
+    S = cfg.seqlen if seqlen is None else seqlen
+    H = cfg.heads if heads is None else heads
+    gen = torch.Generator().manual_seed(seed)
+    t = {}
+    for name in ("q1", "k1", "q2", "k2"):
+        t[name] = _draw(gen, (B, S, H, cfg.head_dim), cfg.input_scale, cfg.dtype)
+    t["v"] = _draw(gen, (B, S, H, cfg.v_dim), cfg.input_scale, cfg.dtype)
+    if cfg.lambda_vec_dim:
+        t["lambda_vecs"] = tuple(
+            torch.randn(cfg.lambda_vec_dim, generator=gen, dtype=torch.float32) * cfg.lambda_vec_std
+            for _ in range(4))
+    else:
+        t["lambda_vecs"] = None
+    t["dy"] = _draw(gen, (B, S, H, cfg.v_dim), 1.0, cfg.dtype) if cfg.with_dy else None
+    t["cfg"] = cfg
+    return t
+
+
+def make_decode_inputs(cfg: DecodeConfig | str = "v2_decode", seed: int = 0, *,
+                       batch: int | None = None, kv_len: int | None = None) -> dict:
+    """Inputs of a DIFF V2 decode workload on the CPU: q [B,Hq,D],
+    k_cache/v_cache [B,S_kv,Hkv,D], lam float32 [Hq/2] (or [B,Hq/2])."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    B = cfg.batch if batch is None else batch
+    L = cfg.kv_len if kv_len is None else kv_len
+    gen = torch.Generator().manual_seed(seed)
+    t = {
+        "q": _draw(gen, (B, cfg.q_heads, cfg.head_dim), cfg.input_scale, cfg.dtype),
+        "k_cache": _draw(gen, (B, L, cfg.kv_heads, cfg.head_dim), cfg.input_scale, cfg.dtype),
+        "v_cache": _draw(gen, (B, L, cfg.kv_heads, cfg.head_dim), cfg.input_scale, cfg.dtype),
+    }
+    lam_shape = (cfg.q_heads // 2,) if cfg.lam_shape == "per_head" else (B, cfg.q_heads // 2)
+    t["lam"] = torch.randn(lam_shape, generator=gen, dtype=torch.float32)
+    t["cfg"] = cfg
+    return t
+
+
+def worked_example_inputs(n: int = 6, d: int = 8, seed: int = 0):
+    """The glossary page's worked example draw: seed 0, one randn(4, n, d) call
+    split into q1, k1, q2, k2, then randn(n, 2d) for v (float32)."""
+    gen = torch.Generator().manual_seed(seed)
+    q1, k1, q2, k2 = torch.randn(4, n, d, generator=gen)
+    v = torch.randn(n, 2 * d, generator=gen)
+    return q1, k1, q2, k2, v

@@ -1,0 +1,16 @@
+"""Slow, plain float64 CPU oracle for multi-head differential attention.
+
+Test infrastructure only.  The test suite, the smoke check and the CPU-baseline
+leg of the benchmark may call it; the product path (the HIP library and its
+Python binding) never imports it, and it imports nothing from the product.
+"""
+from .diffattn_oracle import (  # noqa: F401
+    lambda_init,
+    lambda_value,
+    diff_weights,
+    diff_attn_fwd,
+    diff_attn_bwd,
+    v2_decode,
+    sigmoid,
+)
+from .brute import brute_diff_attn_fwd, brute_v2_decode  # noqa: F401

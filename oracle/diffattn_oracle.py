@@ -1,0 +1,288 @@
+"""float64 numpy oracle for multi-head differential attention (DIFF V1) and the
+DIFF V2 decode combine.
+
+Test infrastructure only: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.  Shares no code with
+the HIP library or its binding.  Every function is the plain definition written
+out with numpy matrix products; there is no tiling, fusion or online softmax.
+
+Sources (the pages describing the method):
+  [G]  Ultralytics glossary, "Differential Transformer" (Korean and Russian
+       editions), section "How differential attention works": two softmax maps
+       with scale 1/sqrt(d), combined as (map1 - lambda*map2) @ V, V twice as
+       wide as the query/key width; lambda_init schedule; per-head
+       normalisation ("GroupNorm") scaled by (1 - lambda_init); halved head
+       count with doubled value width.
+  [V2] neuralnode.tistory.com, "Differential Transformer V2 (DIFF V2) technical
+       innovations": section "DIFF V1 limits" (lambda re-parameterisation),
+       section "DIFF V2 innovations" items 1, 2 and 5 (2h query heads over h KV
+       heads, even/odd head split, sigmoid(lambda) combine), section "GQA
+       compatibility" (pairs must share a KV head).
+  [N]  esgcw.com.cn news write-up of the paper, sections on the differential
+       attention operator and on multi-head differential attention (lambda
+       shared by all heads of a layer, per-head RMSNorm, fixed multiplier
+       (1 - lambda_init)).
+
+Readings where the pages are silent (each listed in the design notes):
+  * per-head RMSNorm has no learnable gain; eps sits inside the root and is an
+    explicit argument;
+  * causal means query i sees keys j <= i (equal query and key lengths);
+  * layout is [batch, seq, head, channel];
+  * the V2 decode uses scale 1/sqrt(D) and, for an empty sequence (length 0),
+    returns zeros;
+  * the backward is the chain rule of the forward below (the pages print no
+    gradient formulas).
+
+Parity pins live in tests/test_oracle_*.py; none of them re-types these formulas.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "lambda_init",
+    "lambda_value",
+    "sigmoid",
+    "diff_weights",
+    "diff_attn_fwd",
+    "diff_attn_bwd",
+    "v2_decode",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def lambda_init(layer: int) -> float:
+    """Depth schedule of lambda's starting value for layer l >= 1 ([G]; [V2]
+    "DIFF V1 limits"; [N] differential attention section):
+    0.8 - 0.6 * exp(-0.3 * (l - 1))."""
+    if layer < 1:
+        raise ValueError("layer index starts at 1")
+    return 0.8 - 0.6 * math.exp(-0.3 * (layer - 1))
+
+
+def lambda_value(lq1, lk1, lq2, lk2, lam_init: float) -> float:
+    """Re-parameterised lambda from the four learnable vectors ([V2] "DIFF V1
+    limits"; [N] differential attention section):
+    exp(<lq1, lk1>) - exp(<lq2, lk2>) + lambda_init, the sums taken over the
+    vector dimension.  One scalar per layer, shared by all heads ([N])."""
+    a = float(np.dot(_f64(lq1), _f64(lk1)))
+    b = float(np.dot(_f64(lq2), _f64(lk2)))
+    return math.exp(a) - math.exp(b) + float(lam_init)
+
+
+def sigmoid(x):
+    """Logistic function used by the V2 combine ([V2] item 5)."""
+    x = _f64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax of a score matrix whose masked entries are -inf."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
+            rows: np.ndarray) -> np.ndarray:
+    """scale * q[rows] @ k^T with keys j > i set to -inf when causal."""
+    s = (q[rows] @ k.T) * scale
+    if causal:
+        cols = np.arange(k.shape[0])
+        s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def diff_weights(q1, k1, q2, k2, lam: float, scale: float | None = None,
+                 causal: bool = False) -> np.ndarray:
+    """The combined attention map softmax(q1 k1^T s) - lam * softmax(q2 k2^T s)
+    for one head ([G]), q*, k*: [n, d].  Rows sum to 1 - lam; entries may be
+    negative."""
+    q1, k1, q2, k2 = map(_f64, (q1, k1, q2, k2))
+    d = q1.shape[-1]
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rows = np.arange(q1.shape[0])
+    p1 = _softmax_rows(_scores(q1, k1, s, causal, rows))
+    p2 = _softmax_rows(_scores(q2, k2, s, causal, rows))
+    return p1 - lam * p2
+
+
+def diff_attn_fwd(q1, k1, q2, k2, v, lam: float, lam_init: float, *,
+                  causal: bool = True, norm: bool = True, eps: float = 1e-5,
+                  scale: float | None = None, rows=None,
+                  return_aux: bool = False):
+    """Multi-head differential attention forward.
+
+    q1, k1, q2, k2: [B, S, H, d]; v: [B, S, H, dv] (dv = 2d in the pages' model,
+    any dv accepted here).  lam is the layer's scalar lambda, lam_init the
+    constant of the (1 - lambda_init) multiplier.
+
+    Per batch b and head h ([G]; [N] multi-head section):
+      P_m = softmax(scale * Q_m K_m^T)  (scale 1/sqrt(d), d = query/key width)
+      O   = (P_1 - lam * P_2) @ V
+      Y   = O / sqrt(mean_c O^2 + eps) * (1 - lam_init)   if norm, else O.
+
+    rows: optional 1-D array of query positions to evaluate (all keys each row
+    may see are still used); default all positions.
+    Returns Y [B, R, H, dv]; with return_aux also a dict holding O, A1 = P_1 V,
+    A2 = P_2 V, lse1, lse2 (natural-log partition functions of the scaled
+    scores, [B, H, R]) and rstd ([B, H, R], ones when norm is off).
+    """
+    q1, k1, q2, k2, v = map(_f64, (q1, k1, q2, k2, v))
+    B, S, H, d = q1.shape
+    dv = v.shape[-1]
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    Y = np.empty((B, R, H, dv))
+    aux = {key: np.empty((B, R, H, dv)) for key in ("O", "A1", "A2")}
+    for key in ("lse1", "lse2", "rstd"):
+        aux[key] = np.empty((B, H, R))
+    for b in range(B):
+        for h in range(H):
+            s1 = _scores(q1[b, :, h], k1[b, :, h], s, causal, rows)
+            s2 = _scores(q2[b, :, h], k2[b, :, h], s, causal, rows)
+            p1 = _softmax_rows(s1)
+            p2 = _softmax_rows(s2)
+            vv = v[b, :, h]
+            a1 = p1 @ vv
+            a2 = p2 @ vv
+            o = (p1 - lam * p2) @ vv
+            if norm:
+                r = 1.0 / np.sqrt(np.mean(o * o, axis=-1) + eps)
+                y = o * r[:, None] * (1.0 - lam_init)
+            else:
+                r = np.ones(R)
+                y = o
+            Y[b, :, h] = y
+            if return_aux:
+                aux["O"][b, :, h] = o
+                aux["A1"][b, :, h] = a1
+                aux["A2"][b, :, h] = a2
+                m1 = np.max(s1, axis=-1)
+                m2 = np.max(s2, axis=-1)
+                aux["lse1"][b, h] = m1 + np.log(np.sum(np.exp(s1 - m1[:, None]), axis=-1))
+                aux["lse2"][b, h] = m2 + np.log(np.sum(np.exp(s2 - m2[:, None]), axis=-1))
+                aux["rstd"][b, h] = r
+    if return_aux:
+        return Y, aux
+    return Y
+
+
+def diff_attn_bwd(q1, k1, q2, k2, v, dy, *, lam_init: float,
+                  lam_vectors=None, lam_fixed: float | None = None,
+                  causal: bool = True, norm: bool = True, eps: float = 1e-5,
+                  scale: float | None = None) -> dict:
+    """Gradients of L = <dy, Y> for the forward above, by the chain rule.
+
+    lambda comes either from lam_vectors = (lq1, lk1, lq2, lk2) (then the four
+    vector gradients are returned) or from lam_fixed (then d lambda itself is
+    returned).  No gradient flows into lambda_init or the (1 - lambda_init)
+    multiplier, which the pages call a fixed multiplier ([N]).
+
+    Steps, per (b, h), with a = 1 - lam_init:
+      Y = a r O,  r = (mean_c O^2 + eps)^-1/2
+      g = dL/dO = a r dy - a r^3 O (sum_c dy O) / dv        (g = dy if no norm)
+      O = A1 - lam A2, A_m = P_m V:  dA1 = g, dA2 = -lam g,
+                                      dlam += -sum(g * A2)
+      dV  = P1^T dA1 + P2^T dA2,  dP_m = dA_m V^T
+      dS_m = P_m * (dP_m - rowsum(P_m * dP_m))
+      dQ_m = scale dS_m K_m,  dK_m = scale dS_m^T Q_m
+      lam = e^al - e^be + lam_init, al = <lq1,lk1>, be = <lq2,lk2>:
+      dlq1 = dlam e^al lk1, dlk1 = dlam e^al lq1,
+      dlq2 = -dlam e^be lk2, dlk2 = -dlam e^be lq2.
+    """
+    q1, k1, q2, k2, v, dy = map(_f64, (q1, k1, q2, k2, v, dy))
+    B, S, H, d = q1.shape
+    dv_w = v.shape[-1]
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if lam_vectors is not None:
+        lq1, lk1, lq2, lk2 = map(_f64, lam_vectors)
+        lam = lambda_value(lq1, lk1, lq2, lk2, lam_init)
+    else:
+        if lam_fixed is None:
+            raise ValueError("need lam_vectors or lam_fixed")
+        lam = float(lam_fixed)
+    rows = np.arange(S)
+    out = {key: np.zeros_like(x) for key, x in
+           (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
+    dlam = 0.0
+    a = 1.0 - lam_init
+    for b in range(B):
+        for h in range(H):
+            Q1, K1, Q2, K2, V = (t[b, :, h] for t in (q1, k1, q2, k2, v))
+            dY = dy[b, :, h]
+            P1 = _softmax_rows(_scores(Q1, K1, s, causal, rows))
+            P2 = _softmax_rows(_scores(Q2, K2, s, causal, rows))
+            A1 = P1 @ V
+            A2 = P2 @ V
+            O = A1 - lam * A2
+            if norm:
+                r = 1.0 / np.sqrt(np.mean(O * O, axis=-1) + eps)
+                dot = np.sum(dY * O, axis=-1)
+                g = a * r[:, None] * dY - a * (r ** 3 * dot)[:, None] * O / dv_w
+            else:
+                g = dY
+            dA1 = g
+            dA2 = -lam * g
+            dlam += -float(np.sum(g * A2))
+            out["dv"][b, :, h] = P1.T @ dA1 + P2.T @ dA2
+            for P, dA, Q, K, kq, kk in ((P1, dA1, Q1, K1, "dq1", "dk1"),
+                                        (P2, dA2, Q2, K2, "dq2", "dk2")):
+                dP = dA @ V.T
+                dS = P * (dP - np.sum(P * dP, axis=-1, keepdims=True))
+                out[kq][b, :, h] = s * (dS @ K)
+                out[kk][b, :, h] = s * (dS.T @ Q)
+    if lam_vectors is not None:
+        ea = math.exp(float(np.dot(lq1, lk1)))
+        eb = math.exp(float(np.dot(lq2, lk2)))
+        out["dlq1"] = dlam * ea * lk1
+        out["dlk1"] = dlam * ea * lq1
+        out["dlq2"] = -dlam * eb * lk2
+        out["dlk2"] = -dlam * eb * lq2
+    out["dlambda"] = dlam
+    out["lambda"] = lam
+    return out
+
+
+def v2_decode(q, k_cache, v_cache, lam, seqlens=None, scale: float | None = None):
+    """DIFF V2 decode step with grouped-query attention ([V2] items 1, 2, 5 and
+    "GQA compatibility").
+
+    q: [B, Hq, D] (one new token per sequence); k_cache, v_cache:
+    [B, S_kv, Hkv, D]; query head t reads KV head t // (Hq / Hkv), the usual
+    grouped-query assignment.  Every query head runs ordinary softmax
+    attention over the first seqlens[b] cached keys (all S_kv by default);
+    then heads are split into even and odd along the head axis and combined
+    as attn[even] - sigmoid(lam) * attn[odd].  lam: [Hq/2] shared by the batch,
+    or [B, Hq/2].  Returns [B, Hq/2, D].  A sequence of length 0 yields zeros.
+    """
+    q, k_cache, v_cache = map(_f64, (q, k_cache, v_cache))
+    B, Hq, D = q.shape
+    S_kv, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if Hq % Hkv or (Hq // Hkv) % 2:
+        raise ValueError("each even/odd query-head pair must share a KV head")
+    group = Hq // Hkv
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lam = _f64(lam)
+    if lam.ndim == 1:
+        lam = np.broadcast_to(lam, (B, Hq // 2))
+    lens = np.full(B, S_kv) if seqlens is None else np.asarray(seqlens)
+    attn = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(lens[b])
+        for t in range(Hq):
+            if n == 0:
+                continue
+            j = t // group
+            K = k_cache[b, :n, j]
+            V = v_cache[b, :n, j]
+            sc = (K @ q[b, t]) * s
+            p = np.exp(sc - np.max(sc))
+            attn[b, t] = (p / np.sum(p)) @ V
+    return attn[:, 0::2] - sigmoid(lam)[:, :, None] * attn[:, 1::2]
