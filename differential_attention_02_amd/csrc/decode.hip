@@ -1,0 +1,280 @@
+// DIFF V2 decode step: one new query token per sequence, 2h query heads over h
+// KV heads, even/odd heads of one grouped-query group combined as
+// attn_even - sigmoid(lambda) attn_odd (neuralnode.tistory.com "DIFF V2
+// technical innovations", section "DIFF V2 innovations" items 1, 2 and 5;
+// section "GQA compatibility").
+//
+// Decode is bound by HBM bandwidth (that page, item 1): the kernel's job is to
+// stream the K and V cache exactly once at full rate.  Split-K layout:
+//   decode_split: one workgroup per (key chunk, KV head (or part of its query
+//     group), batch).  Every query head of the group is served by the same
+//     workgroup, so each K/V byte is read once for all of them.  Phase 1
+//     streams K (D / 8 lanes per key row, 16-byte loads, whole rows per load
+//     instruction) and writes log2-domain scores to LDS; phase 2 takes each
+//     head's max and sum over the chunk; phase 3 streams V and accumulates the
+//     probability-weighted rows.  Arithmetic is float32.  The chunk's
+//     (max, sum, un-normalised output) go to the workspace.
+//   decode_combine: per (batch, pair) merges the chunks by log-sum-exp
+//     rescaling, normalises, and applies the even/odd sigmoid(lambda) combine.
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int NT = 256;
+constexpr int MAX_CHUNK = 2048;  // keys per split (LDS holds the chunk's scores)
+
+template <typename T>
+__device__ __forceinline__ void to_f32x8(const u32x4 &raw, float *f);
+
+template <>
+__device__ __forceinline__ void to_f32x8<bf16>(const u32x4 &raw, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(raw[i] << 16);
+    f[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+  }
+}
+
+// float32 caches: the "8 values" of a lane are two 16-byte loads.
+struct Raw8 {
+  u32x4 a, b;
+};
+
+template <typename T>
+struct RowLoad;
+
+template <>
+struct RowLoad<bf16> {
+  typedef u32x4 raw_t;
+  static __device__ __forceinline__ raw_t load(const bf16 *p) { return *(const u32x4 *)p; }
+  static __device__ __forceinline__ raw_t zero() { return u32x4{0, 0, 0, 0}; }
+  static __device__ __forceinline__ void cvt(const raw_t &r, float *f) { to_f32x8<bf16>(r, f); }
+};
+
+template <>
+struct RowLoad<float> {
+  typedef Raw8 raw_t;
+  static __device__ __forceinline__ raw_t load(const float *p) {
+    return Raw8{*(const u32x4 *)p, *(const u32x4 *)(p + 4)};
+  }
+  static __device__ __forceinline__ raw_t zero() { return Raw8{{0, 0, 0, 0}, {0, 0, 0, 0}}; }
+  static __device__ __forceinline__ void cvt(const raw_t &r, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(r.a[i]);
+      f[4 + i] = __uint_as_float(r.b[i]);
+    }
+  }
+};
+
+template <typename T, int D, int NH>
+__global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
+  constexpr int LPK = D / 8;      // lanes per key row (8 channels each)
+  constexpr int KPW = 64 / LPK;   // keys per wave per load step
+  constexpr int U = 4;            // load steps in flight per lane
+  constexpr int STEP = 4 * KPW * U;
+  typedef RowLoad<T> RL;
+  typedef typename RL::raw_t raw_t;
+
+  __shared__ float s_lds[NH][MAX_CHUNK];
+  __shared__ float red[4][NH][D];
+  __shared__ float stat[4][NH];
+
+  const int split = blockIdx.x, grp = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = lane % LPK, kl = lane / LPK;
+  const int G = p.Hq / p.Hkv, per = G / NH;
+  const int j = grp / per, t0 = j * G + (grp % per) * NH;
+  int len = p.L;
+  if (p.seqlens) len = min(max(p.seqlens[b], 0), p.L);
+  const int kb = split * p.chunk;
+  const int n = max(0, min(len, kb + p.chunk) - kb);
+
+  const float c = p.scale * kLog2e;
+  float q[NH][8];
+#pragma unroll
+  for (int u = 0; u < NH; ++u) {
+    const T *qp = (const T *)p.q + b * p.qs_b + (t0 + u) * p.qs_h + part * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[u][e] = (float)qp[e] * c;
+  }
+  const T *kbase = (const T *)p.k + b * p.kvs_b + j * p.kvs_h + (int64_t)kb * p.kvs_s + part * 8;
+  const T *vbase = (const T *)p.v + b * p.kvs_b + j * p.kvs_h + (int64_t)kb * p.kvs_s + part * 8;
+
+  // Phase 1: scores (log2 domain) of every key of the chunk.
+  for (int base = wave * KPW * U; base < n; base += STEP) {
+    raw_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPW + kl;
+      r[u] = key < n ? RL::load(kbase + (int64_t)key * p.kvs_s) : RL::zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+      RL::cvt(r[u], kf);
+      const int key = base + u * KPW + kl;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(q[hh][e], kf[e], s);
+#pragma unroll
+        for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o);
+        if (part == 0 && key < n) s_lds[hh][key] = s;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: per-head max and sum over the chunk; scores become 2^(s - m).
+  float m[NH], l[NH];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float mx = kNegInf;
+    for (int i = tid; i < n; i += NT) mx = fmaxf(mx, s_lds[hh][i]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) stat[wave][hh] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+    m[hh] = fmaxf(fmaxf(stat[0][hh], stat[1][hh]), fmaxf(stat[2][hh], stat[3][hh]));
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    float sm = 0.f;
+    for (int i = tid; i < n; i += NT) {
+      const float e = fast_exp2(s_lds[hh][i] - m[hh]);
+      s_lds[hh][i] = e;
+      sm += e;
+    }
+    sm = wave_sum(sm);
+    if (lane == 0) stat[wave][hh] = sm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) l[hh] = (stat[0][hh] + stat[1][hh]) + (stat[2][hh] + stat[3][hh]);
+
+  // Phase 3: un-normalised P V over the chunk.
+  float acc[NH][8];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  for (int base = wave * KPW * U; base < n; base += STEP) {
+    raw_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPW + kl;
+      r[u] = key < n ? RL::load(vbase + (int64_t)key * p.kvs_s) : RL::zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPW + kl;
+      if (key < n) {
+        float vf[8];
+        RL::cvt(r[u], vf);
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          const float pr = s_lds[hh][key];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+        }
+      }
+    }
+  }
+  // Reduce over the KPW key slots of the wave, then over the 4 waves.
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[hh][e];
+      for (int o = LPK; o < 64; o <<= 1) x += __shfl_xor(x, o);
+      acc[hh][e] = x;
+    }
+  if (kl == 0) {
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][hh][part * 8 + e] = acc[hh][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < NH * D; i += NT) {
+    const int hh = i / D, ch = i % D;
+    const float x = (red[0][hh][ch] + red[1][hh][ch]) + (red[2][hh][ch] + red[3][hh][ch]);
+    const int64_t slot = ((int64_t)b * p.Hq + t0 + hh) * p.splits + split;
+    p.part_o[slot * D + ch] = x;
+    if (ch == 0) {
+      p.part_ml[slot * 2] = n > 0 ? m[hh] : kNegInf;
+      p.part_ml[slot * 2 + 1] = n > 0 ? l[hh] : 0.f;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
+  const int pr = blockIdx.x, b = blockIdx.y, ch = threadIdx.x;
+  float a[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t slot0 = ((int64_t)b * p.Hq + 2 * pr + u) * p.splits;
+    float M = kNegInf;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[(slot0 + s) * 2]);
+    float L = 0.f, acc = 0.f;
+    if (M != kNegInf) {
+      for (int s = 0; s < p.splits; ++s) {
+        const float w = fast_exp2(p.part_ml[(slot0 + s) * 2] - M);
+        L = fmaf(p.part_ml[(slot0 + s) * 2 + 1], w, L);
+        acc = fmaf(p.part_o[(slot0 + s) * D + ch], w, acc);
+      }
+    }
+    a[u] = L > 0.f ? acc / L : 0.f;
+  }
+  const float lam = p.lam[b * p.lam_stride_b + pr];
+  const float sg = 1.f / (1.f + expf(-lam));
+  T *out = (T *)p.out + b * p.os_b + pr * p.os_h;
+  out[ch] = (T)(a[0] - sg * a[1]);
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const DecodeParams &p, hipStream_t st) {
+  const int G = p.Hq / p.Hkv;
+  const int nh = (G % 4 == 0) ? 4 : 2;
+  dim3 grid(p.splits, p.Hkv * (G / nh), p.B);
+  if (nh == 4)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, 2>), grid, dim3(NT), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq / 2, p.B), dim3(D), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int splits) {
+  return (size_t)B * Hq * splits * (D + 2) * sizeof(float);
+}
+
+int decode_auto_splits(int B, int Hkv, int L) {
+  const int min_splits = (L + MAX_CHUNK - 1) / MAX_CHUNK;
+  const int units = max(B * Hkv, 1);
+  // Aim for about 4096 workgroups in flight over the 256 CUs.
+  int s = (4096 + units - 1) / units;
+  s = max(s, min_splits);
+  s = min(s, max(1, (L + 255) / 256));  // at least ~256 keys per split
+  return max(max(s, min_splits), 1);
+}
+
+int decode_max_chunk() { return MAX_CHUNK; }
+
+hipError_t launch_decode(const DecodeParams &p, int dtype, hipStream_t st) {
+  if (dtype == 0) return p.D == 64 ? launch_typed<float, 64>(p, st) : launch_typed<float, 128>(p, st);
+  return p.D == 64 ? launch_typed<bf16, 64>(p, st) : launch_typed<bf16, 128>(p, st);
+}
+
+}  // namespace diffattn

@@ -1,0 +1,368 @@
+// Fused causal/non-causal forward of multi-head differential attention on
+// gfx950 matrix cores: bf16 storage, d = 64 (query/key width), dv = 128.
+//
+// The operator (glossary page "Differential Transformer", section "How
+// differential attention works"; news write-up, multi-head section):
+//   Y = RMSNorm_head((softmax(s Q1 K1^T) - lambda softmax(s Q2 K2^T)) V) (1 - lambda_init)
+//
+// Work split.  One workgroup of 4 waves owns 128 query rows of one (batch,
+// head); wave w owns rows 32w .. 32w+31.  Causal tiles are issued longest
+// first, and consecutive workgroup ids walk the (batch, head) index so every
+// query tile of one head lands on the same XCD (workgroups are dealt to the 8
+// XCDs round-robin), sharing that XCD's L2 for the head's K and V.
+//
+// Two passes over 64-key tiles staged through LDS:
+//   pass 1 streams K1, K2 and computes, per map and query row, the log2
+//          partition function L_m (online max and sum of 2^(s c));
+//   pass 2 streams K1, K2, V, recomputes the scores and forms the combined,
+//          already normalised weight W = 2^(s1 c - L1) - lambda 2^(s2 c - L2)
+//          in float32, rounds W once to fp16 and accumulates O = W V.
+// Rounding the combined weight once (rather than each map's probabilities
+// separately) keeps the error proportional to |map1 - lambda map2|: when
+// lambda is near 1 the two maps cancel and per-map rounding error would be
+// amplified by 1 / (1 - lambda).  W and V enter the PV product as fp16 (V is
+// converted exactly from bf16 on its way into LDS), because bf16's 8-bit
+// significand alone would spend most of the error budget.  Each row's W is
+// scaled by a power of two 2^sigma chosen from pass 1 (the largest weight is
+// at most 2^(M1 - L1) + |lambda| 2^(M2 - L2), M the row's top score), so it
+// sits just under 2^15 and even 64K-key rows of ~1/65536 weights stay in
+// fp16's normal range; sigma folds into L for free and the epilogue removes
+// it exactly.  Matrix-core work per (query, key) pair is 4 QK^T products of
+// width 64 plus one PV product of width 128: 768 flop, the same as a one-pass
+// form with two PV products.
+//
+// Scores are computed transposed, S^T = K Q^T (keys on rows), so that each lane
+// owns one query column: row max, row sum and the online-softmax state are
+// per-lane scalars, and the score registers are already in the B-operand
+// layout of the PV product O^T = V^T W^T.  K rows are loaded in a permuted
+// order inside each 16-row block so that a lane's 16 score registers are keys
+// 8 h + 0..7 and 16 + 8 h + 0..7 (h = lane / 32), exactly the k-slots of two
+// 32x32x16 PV steps.  V^T operands come from the row-major V tile through LDS
+// transpose reads.  The epilogue (RMSNorm over the head's 128 channels) reduces
+// inside the lane and across the two half-waves.  V entries beyond the fp16
+// range (|v| > 65504) saturate.
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int D = 64, DV = 128, BM = 128, BN = 64, NT = 256;
+constexpr int KST = D + 8;   // LDS row stride of a K tile, bf16 elements (144 B)
+constexpr int VST = DV + 32; // LDS row stride of the V tile (320 B)
+
+struct Smem {
+  bf16 k1[BN * KST];
+  bf16 k2[BN * KST];
+  f16 v[BN * VST];  // V tile converted to fp16
+};
+
+struct TileRegs {
+  u32x4 k1[2], k2[2], v[4];
+};
+
+// Row of the K tile that lane row index i (0..31) reads: bits 2 and 3 of the
+// position inside each 16-row block are swapped.
+__device__ __forceinline__ int k_row_perm(int i) {
+  return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Key (relative to its 32-key sub-tile) held by score register r of a lane in
+// half h.
+__device__ __forceinline__ int key_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
+
+__device__ __forceinline__ void load_tile(const bf16 *k1, const bf16 *k2, const bf16 *v, int64_t ks,
+                                          int64_t vs, int kbase, int S, int tid, bool with_v,
+                                          TileRegs &r) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8, key = kbase + row;
+    if (key < S) {
+      r.k1[i] = *(const u32x4 *)(k1 + key * ks + col);
+      r.k2[i] = *(const u32x4 *)(k2 + key * ks + col);
+    } else {
+      r.k1[i] = u32x4{0, 0, 0, 0};
+      r.k2[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  if (with_v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + NT * i, row = c >> 4, col = (c & 15) * 8, key = kbase + row;
+      r.v[i] = key < S ? *(const u32x4 *)(v + key * vs + col) : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile(Smem &sm, const TileRegs &r, int tid, bool with_v) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
+    *(u32x4 *)(sm.k1 + row * KST + col) = r.k1[i];
+    *(u32x4 *)(sm.k2 + row * KST + col) = r.k2[i];
+  }
+  if (with_v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + NT * i, row = c >> 4, col = (c & 15) * 8;
+      const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]),
+                       bf16x2_to_f16x2(r.v[i][2]), bf16x2_to_f16x2(r.v[i][3])};
+      *(u32x4 *)(sm.v + row * VST + col) = h;
+    }
+  }
+}
+
+// S^T sub-tile (32 keys x 32 queries) of both maps.
+__device__ __forceinline__ void scores(const Smem &sm, int sub, int krow, int h, const bf16x8 *qf1,
+                                       const bf16x8 *qf2, f32x16 &s1, f32x16 &s2) {
+  const bf16 *a1 = sm.k1 + (sub * 32 + krow) * KST + 8 * h;
+  const bf16 *a2 = sm.k2 + (sub * 32 + krow) * KST + 8 * h;
+  s1 = f32x16{};
+  s2 = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    s1 = mfma32(*(const bf16x8 *)(a1 + kc * 16), qf1[kc], s1);
+    s2 = mfma32(*(const bf16x8 *)(a2 + kc * 16), qf2[kc], s2);
+  }
+}
+
+// Online log2-domain max/sum update of one lane's share of a map's row.
+__device__ __forceinline__ void lse_update(const f32x16 &s, float c, float &m, float &l) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  const float mn = fmaxf(m, mx * c);
+  const float ms = mn == kNegInf ? 0.f : mn;
+  float acc = l * fast_exp2(m - ms);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], c, -ms));
+  l = acc;
+  m = mn;
+}
+
+// Full-row top score M and log2 partition function L from the two
+// half-waves' (m, l).
+__device__ __forceinline__ void lse_finish(float m, float l, float &M, float &L) {
+  const float mo = other_half(m), lo = other_half(l);
+  M = fmaxf(m, mo);
+  const float Ms = M == kNegInf ? 0.f : M;
+  L = Ms + log2f(l * fast_exp2(m - Ms) + lo * fast_exp2(mo - Ms));
+}
+
+// Exponent sigma that brings a row whose largest |weight| is wmax just under
+// 2^15.
+__device__ __forceinline__ float row_scale_log2(float wmax) {
+  return fminf(fmaxf(floorf(15.f - log2f(wmax)), -100.f), 100.f);
+}
+
+__device__ __forceinline__ f16x8 pack8(const float *w) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 x = {w[i], w[i + 1]};
+    const f16x2 y = __builtin_convertvector(x, f16x2);
+    r[i] = y[0];
+    r[i + 1] = y[1];
+  }
+  return r;
+}
+
+// O^T[ct] += V^T (channels ct*32.., keys of sub-tile chunk kc2) * W^T.
+__device__ __forceinline__ void pv_step(const Smem &sm, int sub, int lane, const f16x8 *wb,
+                                        f32x16 *o) {
+  const int h = lane >> 5, j = lane & 15, half16 = (lane >> 4) & 1;
+#pragma unroll
+  for (int kc2 = 0; kc2 < 2; ++kc2) {
+    const int key0 = sub * 32 + kc2 * 16 + 8 * h + (j >> 2);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f16 *p = sm.v + key0 * VST + ct * 32 + 16 * half16 + 4 * (j & 3);
+      const f16x4 lo = lds_read_tr16(p);
+      const f16x4 hi = lds_read_tr16(p + 4 * VST);
+      const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[ct] = mfma32(a, wb[kc2], o[ct]);
+    }
+  }
+}
+
+template <bool SAVE>
+__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdParams p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, h = lane >> 5;
+  const int BH = p.B * p.H;
+  const int n_qt = (p.S + BM - 1) / BM;
+  const int bh = blockIdx.x % BH;
+  const int qt_i = blockIdx.x / BH;
+  const int qt = p.causal ? n_qt - 1 - qt_i : qt_i;
+  const int b = bh / p.H, hd = bh % p.H;
+  const int q0 = qt * BM, qw = q0 + wave * 32, my_q = qw + ln;
+  const int S = p.S;
+
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  if (blockIdx.x == 0 && tid == 0 && p.lambda_out) *p.lambda_out = lam;
+  const float c = p.scale * kLog2e;
+
+  const bf16 *k1 = (const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h;
+  const bf16 *k2 = (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h;
+  const bf16 *v = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
+
+  bf16x8 qf1[4], qf2[4];
+  {
+    const bf16 *q1 = (const bf16 *)p.q1 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
+    const bf16 *q2 = (const bf16 *)p.q2 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      qf1[kc] = my_q < S ? *(const bf16x8 *)(q1 + kc * 16) : bf16x8{};
+      qf2[kc] = my_q < S ? *(const bf16x8 *)(q2 + kc * 16) : bf16x8{};
+    }
+  }
+
+  const int kend = p.causal ? min(S, q0 + BM) : S;
+  const int n_kt = (kend + BN - 1) / BN;
+  const int krow = k_row_perm(ln);
+  const int q_last = qw + 31;
+
+  // ---------------- pass 1: per-map log2 partition functions ----------------
+  float m1 = kNegInf, l1 = 0.f, m2 = kNegInf, l2 = 0.f;
+  TileRegs nxt;
+  load_tile(k1, k2, v, p.ks_s, p.vs_s, 0, S, tid, false, nxt);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    store_tile(sm, nxt, tid, false);
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(k1, k2, v, p.ks_s, p.vs_s, (kt + 1) * BN, S, tid, false, nxt);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kt * BN + sub * 32;
+      if (sb >= S || (p.causal && sb > q_last)) continue;
+      f32x16 s1, s2;
+      scores(sm, sub, krow, h, qf1, qf2, s1, s2);
+      if ((p.causal && sb + 31 > qw) || sb + 32 > S) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = sb + key_of_reg(r, h);
+          if (key >= S || (p.causal && key > my_q)) {
+            s1[r] = kNegInf;
+            s2[r] = kNegInf;
+          }
+        }
+      }
+      lse_update(s1, c, m1, l1);
+      lse_update(s2, c, m2, l2);
+    }
+  }
+  float M1, L1, M2, L2;
+  lse_finish(m1, l1, M1, L1);
+  lse_finish(m2, l2, M2, L2);
+  // Row scale 2^sg for the fp16 weights (and 2^sg2 for the saved second map).
+  const float sg = row_scale_log2(fast_exp2(M1 - L1) + fabsf(lam) * fast_exp2(M2 - L2));
+  const float L1s = L1 - sg, L2s = L2 - sg;
+  const float sg2 = SAVE ? row_scale_log2(fast_exp2(M2 - L2)) : 0.f;
+  const float L2s2 = L2 - sg2;
+
+  // ---------------- pass 2: O = (P1 / l1 - lambda P2 / l2) V ----------------
+  f32x16 o[4], o2[SAVE ? 4 : 1];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
+  if constexpr (SAVE) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) o2[ct] = f32x16{};
+  }
+  load_tile(k1, k2, v, p.ks_s, p.vs_s, 0, S, tid, true, nxt);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    store_tile(sm, nxt, tid, true);
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(k1, k2, v, p.ks_s, p.vs_s, (kt + 1) * BN, S, tid, true, nxt);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kt * BN + sub * 32;
+      if (sb >= S || (p.causal && sb > q_last)) continue;
+      f32x16 s1, s2;
+      scores(sm, sub, krow, h, qf1, qf2, s1, s2);
+      if ((p.causal && sb + 31 > qw) || sb + 32 > S) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = sb + key_of_reg(r, h);
+          if (key >= S || (p.causal && key > my_q)) {
+            s1[r] = kNegInf;
+            s2[r] = kNegInf;
+          }
+        }
+      }
+      float w[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        w[r] = fast_exp2(fmaf(s1[r], c, -L1s)) - lam * fast_exp2(fmaf(s2[r], c, -L2s));
+      const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
+      pv_step(sm, sub, lane, wb, o);
+      if constexpr (SAVE) {
+        float w2[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w2[r] = fast_exp2(fmaf(s2[r], c, -L2s2));
+        const f16x8 wb2[2] = {pack8(w2), pack8(w2 + 8)};
+        pv_step(sm, sub, lane, wb2, o2);
+      }
+    }
+  }
+
+  // ---------------- epilogue: per-head RMSNorm x (1 - lambda_init) ----------------
+  // o holds 2^sg O; unscale exactly by powers of two.
+  const float unscale = fast_exp2(-sg);
+  float ss = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss = fmaf(o[ct][r], o[ct][r], ss);
+  ss += other_half(ss);
+  ss *= unscale * unscale;
+  const float rstd = p.norm ? 1.f / sqrtf(ss * (1.f / DV) + p.eps) : 1.f;
+  const float f = (p.norm ? rstd * (1.f - p.lambda_init) : 1.f) * unscale;
+  if (my_q < S) {
+    bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + hd * p.os_h;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = ct * 32 + 8 * g + 4 * h;
+        bf16x4 y = {f2bf(o[ct][4 * g] * f), f2bf(o[ct][4 * g + 1] * f), f2bf(o[ct][4 * g + 2] * f),
+                    f2bf(o[ct][4 * g + 3] * f)};
+        *(bf16x4 *)(out + ch) = y;
+      }
+    if constexpr (SAVE) {
+      const int64_t row = ((int64_t)b * S + my_q) * p.H + hd;
+      float *op = p.o_pre + row * DV;
+      float *ap = p.a2 + row * DV;
+      const float un2 = fast_exp2(-sg2);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = ct * 32 + 8 * g + 4 * h;
+          *(f32x4 *)(op + ch) = f32x4{o[ct][4 * g], o[ct][4 * g + 1], o[ct][4 * g + 2], o[ct][4 * g + 3]} * unscale;
+          *(f32x4 *)(ap + ch) = f32x4{o2[ct][4 * g], o2[ct][4 * g + 1], o2[ct][4 * g + 2], o2[ct][4 * g + 3]} * un2;
+        }
+      if (h == 0) {
+        const int64_t si = ((int64_t)b * p.H + hd) * S + my_q;
+        p.lse1[si] = L1 * kLn2;
+        p.lse2[si] = L2 * kLn2;
+        p.rstd[si] = rstd;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st) {
+  const int n_qt = (p.S + BM - 1) / BM;
+  dim3 grid(n_qt * p.B * p.H), block(NT);
+  if (p.lse1)
+    hipLaunchKernelGGL(fwd_mfma_kernel<true>, grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL(fwd_mfma_kernel<false>, grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -1,0 +1,70 @@
+// Host-side launchers of the libdiffattn kernels (internal to the library).
+// Arguments reaching these have been validated by the C ABI layer (api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+// Everything the forward kernels read.  Strides in elements.
+struct FwdParams {
+  const void *q1, *k1, *q2, *k2, *v;
+  int64_t qs_b, qs_s, qs_h, ks_b, ks_s, ks_h, vs_b, vs_s, vs_h, os_b, os_s, os_h;
+  void *out;
+  int B, S, H;
+  int causal, norm;
+  const float *lq1, *lk1, *lq2, *lk2;
+  int lambda_dim;
+  float lambda_fixed, lambda_init;
+  float scale;  // softmax scale (> 0)
+  float eps;
+  float *lambda_out;
+  float *lse1, *lse2, *rstd, *o_pre, *a2;  // training saves (all or none)
+};
+
+struct BwdParams {
+  const void *q1, *k1, *q2, *k2, *v, *dout;
+  int64_t qs_b, qs_s, qs_h, ks_b, ks_s, ks_h, vs_b, vs_s, vs_h, ds_b, ds_s, ds_h;
+  int B, S, H;
+  int causal, norm;
+  const float *lq1, *lk1, *lq2, *lk2;
+  int lambda_dim;
+  float lambda_fixed, lambda_init;
+  float scale;
+  const float *lse1, *lse2, *rstd, *o_pre, *a2;
+  void *dq1, *dk1, *dq2, *dk2, *dv;
+  int64_t dqs_b, dqs_s, dqs_h, dks_b, dks_s, dks_h, dvs_b, dvs_s, dvs_h;
+  float *dlq1, *dlk1, *dlq2, *dlk2, *dlambda;
+  void *workspace;
+};
+
+struct DecodeParams {
+  const void *q, *k, *v;
+  int64_t qs_b, qs_h, kvs_b, kvs_s, kvs_h, os_b, os_h;
+  const int32_t *seqlens;
+  const float *lam;
+  int64_t lam_stride_b;
+  void *out;
+  int B, Hq, Hkv, D, L;
+  int splits, chunk;  // keys per split
+  float scale;
+  float *part_o;   // [B, Hq, splits, D]
+  float *part_ml;  // [B, Hq, splits, 2]
+};
+
+// Reference vector-ALU forward: any supported (d, dv), f32 or bf16.
+hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipStream_t st);
+// Fused bf16 matrix-core forward, d = 64, dv = 128.
+hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st);
+
+size_t bwd_workspace_bytes(int B, int S, int H, int d, int dv);
+hipError_t launch_bwd(const BwdParams &p, hipStream_t st);
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int splits);
+int decode_max_chunk();
+int decode_auto_splits(int B, int Hkv, int L);
+hipError_t launch_decode(const DecodeParams &p, int dtype, hipStream_t st);
+
+}  // namespace diffattn

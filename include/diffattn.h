@@ -1,0 +1,194 @@
+/*
+ * diffattn.h - C ABI of libdiffattn.so: multi-head differential attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations (citations name the pages that define them):
+ *   - DIFF V1 forward: per head, two softmax maps softmax(s Q1 K1^T) and
+ *     softmax(s Q2 K2^T), s = 1/sqrt(d), over one value tensor twice as wide as
+ *     the query/key width, combined as (map1 - lambda * map2) V; then per-head
+ *     RMSNorm scaled by the fixed multiplier (1 - lambda_init)
+ *     [Ultralytics glossary "Differential Transformer", section "How
+ *     differential attention works"; esgcw.com.cn write-up, sections on the
+ *     differential attention operator and multi-head differential attention].
+ *     lambda = exp(<lq1,lk1>) - exp(<lq2,lk2>) + lambda_init, one scalar per
+ *     layer shared by all heads; lambda_init = 0.8 - 0.6 exp(-0.3 (l - 1))
+ *     [neuralnode.tistory.com "DIFF V2 technical innovations", section "DIFF V1
+ *     limits"; esgcw.com.cn write-up, differential attention section].
+ *   - DIFF V1 backward: gradients of the forward by the chain rule (the pages
+ *     print none; the forward above defines them).
+ *   - DIFF V2 decode: 2h query heads over h KV heads; each query head runs
+ *     ordinary softmax attention over the KV cache, then heads split into even
+ *     and odd along the head axis are combined as attn_even - sigmoid(lam) *
+ *     attn_odd; pairs sit inside one grouped-query group so the KV cache is read
+ *     once [neuralnode.tistory.com, section "DIFF V2 innovations" items 1, 2, 5;
+ *     section "GQA compatibility"].
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a device pointer owned by the caller (for example
+ *     torch tensor storage).  The library allocates no device memory and keeps
+ *     no state beyond a per-thread copy of the last error message.
+ *   - Tensors are [batch, seq, head, channel] with the channel dimension
+ *     contiguous; the other three strides are passed in elements (int64).
+ *   - Calls are asynchronous on the HIP stream passed as `stream`
+ *     (hipStream_t; NULL = the default stream) and never synchronise.
+ *   - Arguments are validated on the host before any launch; on an error the
+ *     function returns a negative status, launches nothing and writes nothing.
+ *     diffattn_last_error() then describes the failure.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define DIFFATTN_OK 0
+#define DIFFATTN_ERR_INVALID_ARGUMENT (-1) /* null pointer, bad size or stride      */
+#define DIFFATTN_ERR_UNSUPPORTED (-2)      /* dtype / head-size combination absent  */
+#define DIFFATTN_ERR_WORKSPACE (-3)        /* workspace missing or too small        */
+#define DIFFATTN_ERR_HIP (-4)              /* HIP runtime or launch failure         */
+
+/* Element types of the activation tensors. */
+#define DIFFATTN_F32 0
+#define DIFFATTN_BF16 1
+
+/*
+ * Forward arguments.
+ *   Shapes: q1, k1, q2, k2 [B, S, H, d]; v and out [B, S, H, dv].  Query and
+ *   key lengths are equal (S).  Supported: bf16 with d = 64, dv = 128 (the
+ *   fused matrix-core kernel); f32 or bf16 with (d, dv) in {(8,16), (16,32),
+ *   (32,64), (64,128), (128,256)} through the reference vector kernel.
+ *   causal: query i sees keys j <= i.  norm: 1 applies the per-head RMSNorm
+ *   times (1 - lambda_init); 0 returns the raw combine (map1 - lambda map2) V.
+ *   lambda: from the four device vectors lq1, lk1, lq2, lk2 (float32,
+ *   lambda_dim each) when all four are non-NULL, else lambda_fixed.
+ *   softmax_scale <= 0 selects 1/sqrt(d).  eps sits inside the RMS root.
+ *   lambda_out (optional, device float32[1]) receives the lambda used.
+ *   Training saves (all five non-NULL, or all NULL; bf16 fused path only):
+ *     lse1, lse2, rstd: float32 [B, H, S] contiguous - natural-log partition
+ *       function of each map's scaled scores, and the RMSNorm reciprocal
+ *       root (1 when norm = 0);
+ *     o_pre, a2: float32 [B, S, H, dv] contiguous - the un-normalised combine
+ *       O = A1 - lambda A2 and the second map's output A2 = map2 V.
+ */
+typedef struct diffattn_fwd_args {
+  int32_t batch, seqlen, heads, head_dim, v_dim;
+  int32_t dtype, causal, norm;
+  const void *q1, *k1, *q2, *k2, *v;
+  int64_t q_stride[3]; /* batch, seq, head strides of q1 and q2 */
+  int64_t k_stride[3]; /* of k1 and k2 */
+  int64_t v_stride[3];
+  int64_t o_stride[3]; /* of out */
+  const float *lq1, *lk1, *lq2, *lk2;
+  int32_t lambda_dim;
+  float lambda_fixed;
+  float lambda_init;
+  float softmax_scale;
+  float eps;
+  void *out;
+  float *lambda_out;
+  float *lse1, *lse2, *rstd;
+  float *o_pre, *a2;
+} diffattn_fwd_args;
+
+/*
+ * Backward arguments: gradients of L = <dout, out> for a forward with the same
+ * inputs and flags (bf16, d = 64, dv = 128, causal or not).
+ *   Needs the five training saves of that forward (lse1, lse2, rstd, o_pre,
+ *   a2).  dout has strides do_stride; outputs dq1, dq2 (strides dq_stride),
+ *   dk1, dk2 (dk_stride), dv (dv_stride) in the activation dtype.
+ *   With the four lambda vectors given, dlq1, dlk1, dlq2, dlk2 (device
+ *   float32[lambda_dim], all four required) receive their gradients; dlambda
+ *   (optional, device float32[1]) receives dL/dlambda in either mode.
+ *   workspace: device memory of at least diffattn_bwd_workspace_size() bytes,
+ *   256-byte aligned; its contents on entry do not matter.
+ */
+typedef struct diffattn_bwd_args {
+  int32_t batch, seqlen, heads, head_dim, v_dim;
+  int32_t dtype, causal, norm;
+  const void *q1, *k1, *q2, *k2, *v;
+  int64_t q_stride[3], k_stride[3], v_stride[3];
+  const void *dout;
+  int64_t do_stride[3];
+  const float *lq1, *lk1, *lq2, *lk2;
+  int32_t lambda_dim;
+  float lambda_fixed;
+  float lambda_init;
+  float softmax_scale;
+  const float *lse1, *lse2, *rstd, *o_pre, *a2;
+  void *dq1, *dk1, *dq2, *dk2, *dv;
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  float *dlq1, *dlk1, *dlq2, *dlk2;
+  float *dlambda;
+  void *workspace;
+  size_t workspace_bytes;
+} diffattn_bwd_args;
+
+/*
+ * DIFF V2 decode arguments (one new query token per sequence).
+ *   q [B, Hq, D] (strides q_stride: batch, head); k_cache, v_cache
+ *   [B, S_kv, Hkv, D] sharing kv_stride (batch, seq, head).  Query head t
+ *   reads KV head t / (Hq / Hkv); Hq / Hkv must be even so that each even/odd
+ *   pair shares its KV head.  Supported: bf16 or f32, D in {64, 128}.
+ *   seqlens: device int32[B] (NULL = every sequence has kv_len keys); values
+ *   are clamped to [0, kv_len]; a length of 0 yields a zero output row.
+ *   lam: device float32, element (b, p) at lam[b * lam_stride_b + p] for
+ *   p < Hq/2 (lam_stride_b = 0 shares one [Hq/2] vector across the batch).
+ *   out [B, Hq/2, D] (strides o_stride: batch, head), in the cache dtype:
+ *   out[b, p] = attn[b, 2p] - sigmoid(lam[b, p]) * attn[b, 2p + 1].
+ *   softmax_scale <= 0 selects 1/sqrt(D).  num_splits: number of key chunks
+ *   each (batch, KV head) is split into (0 = chosen by the library).
+ *   workspace: at least diffattn_v2_decode_workspace_size() bytes.
+ */
+typedef struct diffattn_v2_decode_args {
+  int32_t batch, q_heads, kv_heads, head_dim, kv_len;
+  int32_t dtype;
+  const void *q;
+  int64_t q_stride[2];
+  const void *k_cache, *v_cache;
+  int64_t kv_stride[3];
+  const int32_t *seqlens;
+  const float *lam;
+  int64_t lam_stride_b;
+  float softmax_scale;
+  void *out;
+  int64_t o_stride[2];
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+} diffattn_v2_decode_args;
+
+/* Forward pass. Returns DIFFATTN_OK or a negative status. */
+int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
+
+/* Backward pass. Returns DIFFATTN_OK or a negative status. */
+int diffattn_bwd(const diffattn_bwd_args *args, void *stream);
+
+/* Workspace bytes diffattn_bwd needs for these arguments (0 if invalid). */
+size_t diffattn_bwd_workspace_size(const diffattn_bwd_args *args);
+
+/* DIFF V2 decode step. Returns DIFFATTN_OK or a negative status. */
+int diffattn_v2_decode(const diffattn_v2_decode_args *args, void *stream);
+
+/* Workspace bytes diffattn_v2_decode needs for these arguments (0 if invalid). */
+size_t diffattn_v2_decode_workspace_size(const diffattn_v2_decode_args *args);
+
+/* lambda_init for layer index l >= 1: 0.8 - 0.6 exp(-0.3 (l - 1)); NaN for l < 1. */
+float diffattn_lambda_init(int layer);
+
+/* Static name of a status code. */
+const char *diffattn_status_str(int status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *diffattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

@@ -1,0 +1,92 @@
+"""GPU parity of diffattn_v2_decode (through the C ABI) against the float64
+oracle: small ragged cases in float32 and bf16, split invariance, wider query
+groups, per-batch lambda, and the full 64 x 8192-token workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differential_attention_02_amd import binding as B
+from differential_attention_02_amd import workloads
+from tests.parity import as_f64, assert_bf16_rows, assert_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _case(seed, Bn, Hq, Hkv, D, L, dtype, scale=None, per_batch_lam=False):
+    cfg = workloads.DecodeConfig("t", Bn, Hq, Hkv, D, L, dtype, scale or D ** -0.5,
+                                 lam_shape="per_batch_head" if per_batch_lam else "per_head")
+    return workloads.make_decode_inputs(cfg, seed=seed)
+
+
+def _run(inp, seqlens=None, num_splits=0):
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k_cache", "v_cache", "lam"))
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    out = B.v2_decode(q, k, v, lam, seqlens=sl, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(inp, seqlens=None):
+    return oracle.v2_decode(as_f64(inp["q"]), as_f64(inp["k_cache"]), as_f64(inp["v_cache"]),
+                            as_f64(inp["lam"]), seqlens)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_small_f32(D):
+    _note(f"decode f32 D={D}")
+    inp = _case(0, 3, 8, 4, D, 1000, torch.float32)
+    lens = [1000, 513, 0]
+    out = _run(inp, lens)
+    assert_f32(out, _ref(inp, lens), f"decode f32 D={D}")
+    assert np.all(out[2].cpu().numpy() == 0.0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_small_bf16(D):
+    _note(f"decode bf16 D={D}")
+    inp = _case(1, 4, 8, 4, D, 777, torch.bfloat16)
+    lens = [777, 1, 300, 64]
+    assert_bf16_rows(_run(inp, lens), _ref(inp, lens), f"decode bf16 D={D}")
+
+
+def test_split_invariance():
+    """The answer does not depend on how many key chunks the cache is split
+    into (float32, up to accumulation order)."""
+    inp = _case(2, 2, 4, 2, 128, 3000, torch.float32)
+    outs = [as_f64(_run(inp, num_splits=s)) for s in (2, 3, 7, 0)]
+    for o in outs[1:]:
+        np.testing.assert_allclose(o, outs[0], rtol=1e-5, atol=1e-7)
+    assert_f32(outs[0], _ref(inp), "decode splits")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (12, 2), (4, 2)])
+def test_query_groups(Hq, Hkv):
+    """Groups of 4 and 6 query heads per KV head: even/odd pairs stay inside
+    their group."""
+    inp = _case(3, 2, Hq, Hkv, 64, 400, torch.float32)
+    assert_f32(_run(inp), _ref(inp), f"decode Hq={Hq} Hkv={Hkv}")
+
+
+def test_per_batch_lambda():
+    inp = _case(4, 3, 8, 4, 128, 256, torch.float32, per_batch_lam=True)
+    assert_f32(_run(inp), _ref(inp), "decode per-batch lambda")
+
+
+def test_v2_decode_full():
+    """DIFF V2 decode workload: batch 64, 8192 cached tokens, 32 query heads
+    over 16 KV heads, head dim 128, bf16; every output row checked."""
+    _note("v2_decode full")
+    inp = workloads.make_decode_inputs("v2_decode")
+    out = _run(inp).float().cpu().numpy()
+    lam = as_f64(inp["lam"])
+    worst = (0.0, 0.0)
+    for b in range(0, 64, 8):
+        sl = slice(b, b + 8)
+        ref = oracle.v2_decode(as_f64(inp["q"][sl]), as_f64(inp["k_cache"][sl]), as_f64(inp["v_cache"][sl]), lam)
+        assert_bf16_rows(out[sl], ref, f"v2_decode batches {b}..{b + 7}")
+    assert np.isfinite(out).all()
