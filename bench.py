@@ -1,0 +1,286 @@
+"""Benchmark of the differential-attention hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+
+Headline step: one forward pass (diffattn_fwd) over the 3B-class 4K workload
+(batch 4, 4096 causal tokens, 12 heads, d 64, dv 128, bf16) with inputs
+resident in HBM.  value = algorithmic TFLOP/s: 768 flop per unmasked
+(query, key, head) pair (two QK^T products of width 64 and two PV products of
+width 128, counted once however the kernel schedules them).
+Also reported under "extra": the 64K-token forward, the 8K training step
+(forward + backward) when the backward is built, and the DIFF V2 decode step
+(GB/s of K/V cache + query + output bytes).
+Each timing: W untimed launches, then exactly K launches between two
+synchronisations; HIP events on the launch stream give the average launch
+duration used for the roofline.  "cpu_baseline" times the float64 oracle on a
+bounded sample of the same workload on the host cores.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "diff-attn fwd TFLOP/s (bf16 causal, 4K seq) + V2 decode HBM GB/s, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FLOP_PER_PAIR_FWD = 768
+FLOP_PER_PAIR_BWD = 1280
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _kernel_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(name, files):
+    """HBM bytes per launch recorded by a committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic_json: (\{.*\})$", open(path).read(), flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_digest") != _kernel_digest(files):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+FWD_SOURCES = ["differential_attention_02_amd/csrc/fwd_mfma.hip", "differential_attention_02_amd/csrc/common.h"]
+DEC_SOURCES = ["differential_attention_02_amd/csrc/decode.hip", "differential_attention_02_amd/csrc/common.h"]
+
+
+def _time_launches(launch, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / 1e3 / steps   # seconds total, seconds per launch (events)
+
+
+def _gpu_attn(name, steps, warmup):
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS[name]
+    inp = workloads.make_attn_inputs(cfg)
+    x = [inp[k].cuda() for k in ("q1", "k1", "q2", "k2", "v")]
+    vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    out = torch.empty_like(x[4])
+    args = B.fwd_args(*x, out, lambda_init=B.lambda_init(cfg.layer), lambda_vecs=vecs,
+                      causal=cfg.causal, norm=True, eps=cfg.eps)
+    wall, per = _time_launches(lambda: B.fwd_launch(args), steps, warmup)
+    flops = cfg.batch * cfg.heads * cfg.pairs * FLOP_PER_PAIR_FWD
+    return {"cfg": cfg, "wall_s": wall, "event_s_per_launch": per, "flop_per_step": flops,
+            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12, "inputs": inp}
+
+
+def _gpu_train(steps, warmup):
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["train_8k"]
+    inp = workloads.make_attn_inputs(cfg)
+    x = [inp[k].cuda() for k in ("q1", "k1", "q2", "k2", "v")]
+    vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    dy = inp["dy"].cuda()
+    li = B.lambda_init(cfg.layer)
+
+    def step():
+        _, saves = B.fwd(*x, lambda_init=li, lambda_vecs=vecs, causal=True, eps=cfg.eps, save=True)
+        B.bwd(*x, dy, saves, lambda_init=li, lambda_vecs=vecs, causal=True)
+
+    try:
+        step()
+        torch.cuda.synchronize()
+    except RuntimeError as e:
+        return {"skipped": str(e)}
+    wall, per = _time_launches(step, steps, warmup)
+    pairs = cfg.batch * cfg.heads * cfg.pairs
+    flops = pairs * (FLOP_PER_PAIR_FWD + FLOP_PER_PAIR_BWD)
+    return {"tflops": flops * steps / wall / 1e12, "ms_per_step": wall / steps * 1e3,
+            "flop_per_step": flops}
+
+
+def _gpu_decode(steps, warmup):
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["v2_decode"]
+    inp = workloads.make_decode_inputs(cfg)
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k_cache", "v_cache", "lam"))
+    sample = {n: inp[n][:16].clone() for n in ("q", "k_cache", "v_cache")}
+    sample["lam"] = inp["lam"]
+    del inp
+    out = torch.empty((cfg.batch, cfg.q_heads // 2, cfg.head_dim), dtype=q.dtype, device="cuda")
+    args = B.decode_args(q, k, v, lam, out)
+    nbytes = B.decode_workspace_size(args)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), nbytes
+    wall, per = _time_launches(lambda: B.decode_launch(args), steps, warmup)
+    esz = 2
+    moved = (2 * cfg.batch * cfg.kv_len * cfg.kv_heads * cfg.head_dim + cfg.batch * cfg.q_heads * cfg.head_dim
+             + cfg.batch * cfg.q_heads // 2 * cfg.head_dim) * esz
+    return {"cfg": cfg, "bytes_per_step": moved, "gbs": moved * steps / wall / 1e9,
+            "event_gbs": moved / per / 1e9, "event_s_per_launch": per, "splits": args.num_splits,
+            "sample": sample}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _cpu_baseline_fwd(inp, budget_s=12.0):
+    """The float64 oracle on whole heads of the 4K workload (all 4096 causal
+    rows each, same inputs as the GPU run), one head at a time until about
+    budget_s seconds have passed or all 48 heads are done."""
+    import oracle
+    cfg = inp["cfg"]
+    li = oracle.lambda_init(cfg.layer)
+    lam = oracle.lambda_value(*[t.double().numpy() for t in inp["lambda_vecs"]], li)
+    done, dt = 0, 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            x = [inp[k][b:b + 1, :, h:h + 1].double().numpy() for k in ("q1", "k1", "q2", "k2", "v")]
+            t0 = time.perf_counter()
+            oracle.diff_attn_fwd(*x, lam, li, causal=True, norm=True, eps=cfg.eps)
+            dt += time.perf_counter() - t0
+            done += 1
+            if dt >= budget_s:
+                break
+        if dt >= budget_s:
+            break
+    flops = done * cfg.pairs * FLOP_PER_PAIR_FWD
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"prefill_4k: {done} of 48 (batch, head) slices, all 4096 causal rows each; "
+                      f"{dt:.1f} s of oracle time"}
+
+
+def _cpu_baseline_decode(sample, cfg):
+    """The float64 oracle on the first 16 of the 64 sequences of the decode
+    workload (same inputs as the GPU run)."""
+    import oracle
+    nb = sample["q"].shape[0]
+    t0 = time.perf_counter()
+    for b in range(0, nb, 4):   # 4 sequences at a time bounds the float64 copies
+        a = [sample[k][b:b + 4].double().numpy() for k in ("q", "k_cache", "v_cache")]
+        oracle.v2_decode(*a, sample["lam"].double().numpy())
+    dt = time.perf_counter() - t0
+    moved = (2 * nb * cfg.kv_len * cfg.kv_heads * cfg.head_dim + nb * cfg.q_heads * cfg.head_dim * 1.5) * 2
+    return {"value": moved / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"v2_decode sequences 0-{nb - 1} of 64, bf16 byte count, including float64 "
+                      f"up-conversion; {dt:.2f} s wall"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode"], default=None,
+                    help="time one workload only (for profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        return 2
+    from differential_attention_02_amd import binding
+    binding.lib()   # fails loudly if the HIP library is missing
+
+    if args.only is not None:
+        if args.only in ("prefill_4k", "prefill_64k"):
+            r = _gpu_attn(args.only, args.steps, args.warmup)
+            print(json.dumps({"workload": args.only, "tflops": r["tflops"], "event_tflops": r["event_tflops"]}))
+        elif args.only == "train_8k":
+            print(json.dumps({"workload": "train_8k", **_gpu_train(args.steps, args.warmup)}))
+        else:
+            r = _gpu_decode(args.steps, args.warmup)
+            print(json.dumps({"workload": "v2_decode", "gbs": r["gbs"], "event_gbs": r["event_gbs"]}))
+        return 0
+
+    main_r = _gpu_attn("prefill_4k", args.steps, args.warmup)
+    cfg = main_r["cfg"]
+    achieved = main_r["flop_per_step"] / main_r["event_s_per_launch"] / 1e12
+    traffic = _traffic_from_profile("fwd_mfma_prefill_4k_pmc.md", FWD_SOURCES)
+    extra = {}
+    r64 = _gpu_attn("prefill_64k", max(3, args.steps // 10), 1)
+    extra["prefill_64k"] = {"metric": "fwd TFLOP/s", "value": r64["tflops"],
+                            "frac_of_bf16_peak": r64["event_tflops"] / PEAK_BF16_TFLOPS,
+                            "ms_per_step": r64["wall_s"] / max(3, args.steps // 10) * 1e3}
+    tr = _gpu_train(max(3, args.steps // 10), 1)
+    extra["train_8k"] = tr if "skipped" in tr else {"metric": "fwd+bwd TFLOP/s", "value": tr["tflops"],
+                                                   "ms_per_step": tr["ms_per_step"]}
+    dec = _gpu_decode(args.steps, args.warmup)
+    dec_traffic = _traffic_from_profile("decode_split_v2_decode_pmc.md", DEC_SOURCES)
+    extra["v2_decode"] = {
+        "metric": "V2 decode HBM GB/s", "value": dec["gbs"], "unit": "GB/s",
+        "ms_per_step": dec["event_s_per_launch"] * 1e3,
+        "config": {"workload": "v2_decode: B64, 32 query heads over 16 KV heads, D 128, KV 8192, bf16",
+                   "num_splits": "auto"},
+        "roofline": {"bound": "hbm", "achieved": dec["event_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": dec["event_gbs"] / PEAK_HBM_GBS, "traffic": dec_traffic},
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline_fwd(main_r["inputs"])
+        extra["v2_decode"]["cpu_baseline"] = _cpu_baseline_decode(dec["sample"], dec["cfg"])
+    line = {
+        "metric": METRIC,
+        "value": main_r["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["wall_s"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_4k: batch 4, seq 4096 causal, 12 heads, d 64, dv 128, bf16, "
+                               "lambda from 64-dim vectors, lambda_init at layer 12, per-head RMSNorm",
+                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
