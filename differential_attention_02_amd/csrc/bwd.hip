@@ -1,12 +1,603 @@
-// Backward of multi-head differential attention (placeholder until the fused
-// kernels land): reports that the configuration is not available.
+// Backward of multi-head differential attention on gfx950 (bf16 storage,
+// d = 64, dv = 128).  The pages print no gradient formulas; these are the
+// chain rule of the forward (glossary page "Differential Transformer",
+// section "How differential attention works"; news write-up, multi-head
+// section):
+//   Y = a r O,  a = 1 - lambda_init,  r = (mean_c O^2 + eps)^-1/2
+//   g = dL/dO = a r dY - a r^3 O (sum_c dY O) / dv        (g = dY without norm)
+//   O = A1 - lambda A2,  A_m = P_m V
+//   E_m = g . A_m = sum_j P_m dP  (per query row)
+//   dL/dlambda = -sum_rows g . A2
+//   dV = (P1 - lambda P2)^T g                     (one product for both maps)
+//   dP = g V^T                                    (shared: dP2 = -lambda dP1)
+//   dS1 = P1 (dP - E1),  dS2 = -lambda P2 (dP - E2)
+//   dQ_m = s dS_m K_m,  dK_m = s dS_m^T Q_m,  s = softmax scale
+//   lambda = e^al - e^be + lambda_init:  dlq1 = dlam e^al lk1, dlk1 = dlam e^al lq1,
+//   dlq2 = -dlam e^be lk2, dlk2 = -dlam e^be lq2.
+//
+// Kernels, in launch order:
+//   bwd_pre    one wave per query row: g (float32), |g|, |V_row| and the row's
+//              share -g.A2 of dL/dlambda from the forward's float32 A2
+//              (the sum over rows cancels by orders of magnitude, so it takes
+//              float32 g rather than the fp16 copy the matrix products use);
+//   bwd_scales one workgroup per (batch, head): power-of-two scales that keep
+//              the fp16 operands below 2^13 (g by its largest row norm; dS by
+//              the bound |dS| <= max(1,|lambda|) (|g| |V| + |E|) <= 2 max(1,|lambda|)
+//              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|);
+//   bwd_gconv  g scaled and rounded to fp16;
+//   bwd_dq     query-outer (the forward's layout): each workgroup owns 128
+//              queries and streams 64-key tiles twice: first E_m = sum_j P_m dP
+//              (from the very dP the second pass uses, so dS = P (dP - E) stays
+//              self-consistent where one key dominates a row and dP - E
+//              cancels), then dS and dQ1, dQ2 accumulated in registers;
+//   bwd_dkdv   KV-outer: each workgroup owns 128 keys (4 waves x 32) and
+//              streams 64-query chunks: recomputes P1, P2 and dP, accumulates
+//              dV, dK1, dK2 in registers.  Recomputing rather than
+//              accumulating dQ with atomics keeps every result deterministic;
+//   bwd_lambda one workgroup: dL/dlambda = sum of the row shares in a fixed
+//              order, then the chain rule into the four lambda vectors.
+// Matrix-core operands are fp16 (bf16 inputs convert exactly) with float32
+// accumulation: bf16 rounding of g, W and dS alone would spend most of the
+// bf16 error budget.
 #include "common.h"
 #include "kernels.h"
 
 namespace diffattn {
+namespace {
 
-size_t bwd_workspace_bytes(int, int, int, int, int) { return 0; }
+constexpr int D = 64, DV = 128, NT = 256;
+constexpr int QST = D + 8;    // LDS row stride (fp16) of Q / K tiles
+constexpr int GST = DV + 32;  // LDS row stride (fp16) of g / V tiles (tr16-friendly)
 
-hipError_t launch_bwd(const BwdParams &, hipStream_t) { return hipErrorNotSupported; }
+struct Ws {
+  float *g;        // [B, H, S, DV] float32
+  f16 *gh;         // [B, H, S, DV] fp16, g * 2^sg
+  float *e1, *e2;  // [B, H, S]  E_m = sum_j P_m dP (unscaled)
+  float *gnorm, *vnorm, *dlam_row;  // [B, H, S]
+  float *scales;   // [B*H][4]: sg, kappa, omega, unused (exponents of 2)
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
+  char *p = static_cast<char *>(base);
+  const size_t rows = (size_t)B * H * S;
+  Ws w;
+  w.g = (float *)p; p += align256(rows * DV * 4);
+  w.gh = (f16 *)p; p += align256(rows * DV * 2);
+  w.e1 = (float *)p; p += align256(rows * 4);
+  w.e2 = (float *)p; p += align256(rows * 4);
+  w.gnorm = (float *)p; p += align256(rows * 4);
+  w.vnorm = (float *)p; p += align256(rows * 4);
+  w.dlam_row = (float *)p; p += align256(rows * 4);
+  w.scales = (float *)p; p += align256((size_t)B * H * 16);
+  return w;
+}
+
+__host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
+  const size_t rows = (size_t)B * H * S;
+  return align256(rows * DV * 4) + align256(rows * DV * 2) + 5 * align256(rows * 4) +
+         align256((size_t)B * H * 16);
+}
+
+__device__ __forceinline__ float exp2i(float e) { return fast_exp2(e); }  // e integral: exact power of 2
+
+// ---------------------------------------------------------------------------
+// bwd_pre: one wave per (b, h, s) row; lane holds channels 2 lane, 2 lane + 1.
+__global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over [B, H, S]
+  const int64_t nrows = (int64_t)p.B * p.H * p.S;
+  if (row >= nrows) return;
+  const int s = row % p.S;
+  const int bh = row / p.S;
+  const int b = bh / p.H, h = bh % p.H;
+  const int c = 2 * lane;
+  const bf16 *dyp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + h * p.ds_h + c;
+  const bf16 *vp = (const bf16 *)p.v + b * p.vs_b + (int64_t)s * p.vs_s + h * p.vs_h + c;
+  const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
+  const float2 o = *(const float2 *)(p.o_pre + srow * DV + c);
+  const float2 a2 = *(const float2 *)(p.a2 + srow * DV + c);
+  const float dy0 = bf2f(dyp[0]), dy1 = bf2f(dyp[1]);
+  const float v0 = bf2f(vp[0]), v1 = bf2f(vp[1]);
+  float g0 = dy0, g1 = dy1;
+  if (p.norm) {
+    const float r = p.rstd[((int64_t)b * p.H + h) * p.S + s];
+    const float a = 1.f - p.lambda_init;
+    const float t = wave_sum(dy0 * o.x + dy1 * o.y);
+    const float k = a * r * r * r * t * (1.f / DV);
+    g0 = a * r * dy0 - k * o.x;
+    g1 = a * r * dy1 - k * o.y;
+  }
+  const float gn = wave_sum(g0 * g0 + g1 * g1);
+  const float vn = wave_sum(v0 * v0 + v1 * v1);
+  const float ga = wave_sum(g0 * a2.x + g1 * a2.y);
+  *(float2 *)(w.g + row * DV + c) = make_float2(g0, g1);
+  if (lane == 0) {
+    w.gnorm[row] = sqrtf(gn);
+    w.vnorm[row] = sqrtf(vn);
+    w.dlam_row[row] = -ga;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_scales: one workgroup per (b, h).
+__global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
+  __shared__ float red[2][NT / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  const int64_t base = (int64_t)bh * p.S;
+  float gm = 0.f, vm = 0.f;
+  for (int s = tid; s < p.S; s += NT) {
+    gm = fmaxf(gm, w.gnorm[base + s]);
+    vm = fmaxf(vm, w.vnorm[base + s]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    gm = fmaxf(gm, __shfl_xor(gm, o));
+    vm = fmaxf(vm, __shfl_xor(vm, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = gm;
+    red[1][wave] = vm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    vm = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const float al = fmaxf(1.f, fabsf(lam));
+    const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
+    const float x = 2.f * al * gm * vm;  // bound on |dS| before scaling by 2^sg
+    const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) : 0.f;
+    const float om = floorf(13.f - log2f(1.f + fabsf(lam)));
+    w.scales[bh * 4 + 0] = sg;
+    w.scales[bh * 4 + 1] = kap;
+    w.scales[bh * 4 + 2] = om;
+    w.scales[bh * 4 + 3] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_gconv: g' = fp16(g 2^sg), 8 channels per thread.
+__global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8
+  const int64_t n = (int64_t)p.B * p.H * p.S * (DV / 8);
+  if (i >= n) return;
+  const int bh = (i / (DV / 8)) / p.S;
+  const float f = exp2i(w.scales[bh * 4 + 0]);
+  const f32x4 a = *(const f32x4 *)(w.g + i * 8);
+  const f32x4 b = *(const f32x4 *)(w.g + i * 8 + 4);
+  f16x8 h;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h[k] = (f16)(a[k] * f);
+    h[4 + k] = (f16)(b[k] * f);
+  }
+  *(f16x8 *)(w.gh + i * 8) = h;
+}
+
+// Permutation of rows 0..31 used for the A operand of score-like products so
+// that a lane's 16 result registers are rows 8 h + 0..7 and 16 + 8 h + 0..7.
+__device__ __forceinline__ int row_perm(int i) { return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1); }
+__device__ __forceinline__ int row_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
+
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4 &raw) {
+  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
+                   bf16x2_to_f16x2(raw[3])};
+  return __builtin_bit_cast(f16x8, h);
+}
+
+__device__ __forceinline__ f16x8 pack8h(const float *w) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 x = {w[i], w[i + 1]};
+    const f16x2 y = __builtin_convertvector(x, f16x2);
+    r[i] = y[0];
+    r[i + 1] = y[1];
+  }
+  return r;
+}
+
+// A operand (rows = the 32 matrix columns c0..c0+31 of a row-major fp16 tile,
+// k = 16 consecutive tile rows starting at r0) through transpose reads:
+// lane l receives column c0 + l % 32 of rows r0 + 8 (l / 32) + 0..7.
+__device__ __forceinline__ f16x8 tr_operand(const f16 *tile, int stride, int r0, int c0, int lane) {
+  const int h = lane >> 5, j = lane & 15, half16 = (lane >> 4) & 1;
+  const f16 *ptr = tile + (r0 + 8 * h + (j >> 2)) * stride + c0 + 16 * half16 + 4 * (j & 3);
+  const f16x4 lo = lds_read_tr16(ptr);
+  const f16x4 hi = lds_read_tr16(ptr + 4 * stride);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dkdv: KV-outer.  Workgroup = 128 keys of one (b, h); wave w owns keys
+// kb + 32 w + 0..31 (lane l % 32).  Streams 64-query chunks through LDS.
+constexpr int KVB = 128, QCH = 64;
+
+struct SmemA {
+  f16 q1[QCH * QST];
+  f16 q2[QCH * QST];
+  f16 g[QCH * GST];
+  float lse1[QCH], lse2[QCH], e1[QCH], e2[QCH];
+};
+
+__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
+  __shared__ SmemA sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 31, h = lane >> 5;
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  const int bh = blockIdx.y, b = bh / p.H, hd = bh % p.H;
+  const int S = p.S;
+  const int kb = blockIdx.x * KVB, kw = kb + wave * 32, my_key = kw + ln;
+  const float sg = w.scales[bh * 4 + 0], kap = w.scales[bh * 4 + 1], om = w.scales[bh * 4 + 2];
+  const float c = p.scale * kLog2e;
+  const float fdS = exp2i(kap), fW = exp2i(om), fE = exp2i(sg);
+
+  // K1, K2 (B operand of S = Q K^T) and V (B operand of dP = g V^T) for my key, fp16.
+  f16x8 kf1[4], kf2[4], vf[8];
+  {
+    const bool ok = my_key < S;
+    const bf16 *k1 = (const bf16 *)p.k1 + b * p.ks_b + (int64_t)my_key * p.ks_s + hd * p.ks_h + 8 * h;
+    const bf16 *k2 = (const bf16 *)p.k2 + b * p.ks_b + (int64_t)my_key * p.ks_s + hd * p.ks_h + 8 * h;
+    const bf16 *vv = (const bf16 *)p.v + b * p.vs_b + (int64_t)my_key * p.vs_s + hd * p.vs_h + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      kf1[kc] = ok ? bf16x8_to_f16x8(*(const u32x4 *)(k1 + kc * 16)) : f16x8{};
+      kf2[kc] = ok ? bf16x8_to_f16x8(*(const u32x4 *)(k2 + kc * 16)) : f16x8{};
+    }
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) vf[kc] = ok ? bf16x8_to_f16x8(*(const u32x4 *)(vv + kc * 16)) : f16x8{};
+  }
+
+  f32x16 dv[4], dk1[2], dk2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dv[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dk1[i] = dk2[i] = f32x16{};
+
+  const int q_begin = p.causal ? (kb / QCH) * QCH : 0;
+  const int prow = row_perm(ln);
+  const int64_t statb = (int64_t)bh * S;
+  for (int q0 = q_begin; q0 < S; q0 += QCH) {
+    __syncthreads();
+    // Stage Q1, Q2 (bf16 -> fp16), g' (fp16) and the row statistics.
+    for (int i = tid; i < QCH * 8; i += NT) {
+      const int r = i >> 3, col = (i & 7) * 8, q = q0 + r;
+      u32x4 a = {0, 0, 0, 0}, bq = {0, 0, 0, 0};
+      if (q < S) {
+        a = *(const u32x4 *)((const bf16 *)p.q1 + b * p.qs_b + (int64_t)q * p.qs_s + hd * p.qs_h + col);
+        bq = *(const u32x4 *)((const bf16 *)p.q2 + b * p.qs_b + (int64_t)q * p.qs_s + hd * p.qs_h + col);
+      }
+      *(f16x8 *)(sm.q1 + r * QST + col) = bf16x8_to_f16x8(a);
+      *(f16x8 *)(sm.q2 + r * QST + col) = bf16x8_to_f16x8(bq);
+    }
+    for (int i = tid; i < QCH * 16; i += NT) {
+      const int r = i >> 4, col = (i & 15) * 8, q = q0 + r;
+      u32x4 gv = {0, 0, 0, 0};
+      if (q < S) gv = *(const u32x4 *)(w.gh + (statb + q) * DV + col);
+      *(u32x4 *)(sm.g + r * GST + col) = gv;
+    }
+    if (tid < QCH) {
+      const int q = q0 + tid;
+      const bool ok = q < S;
+      sm.lse1[tid] = ok ? p.lse1[statb + q] * kLog2e : __builtin_inff();
+      sm.lse2[tid] = ok ? p.lse2[statb + q] * kLog2e : __builtin_inff();
+      sm.e1[tid] = ok ? w.e1[statb + q] * fE : 0.f;
+      sm.e2[tid] = ok ? w.e2[statb + q] * fE : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qs = q0 + sub * 32;
+      if (qs >= S) continue;
+      if (p.causal && qs + 31 < kw) continue;  // every query of this sub-chunk precedes my keys
+      // S1, S2 = Q K^T and dP' = g' V^T; lane = key, registers = queries.
+      f32x16 s1 = {}, s2 = {}, dp = {};
+      const f16 *qa1 = sm.q1 + (sub * 32 + prow) * QST + 8 * h;
+      const f16 *qa2 = sm.q2 + (sub * 32 + prow) * QST + 8 * h;
+      const f16 *ga = sm.g + (sub * 32 + prow) * GST + 8 * h;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        s1 = mfma32(*(const f16x8 *)(qa1 + kc * 16), kf1[kc], s1);
+        s2 = mfma32(*(const f16x8 *)(qa2 + kc * 16), kf2[kc], s2);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
+      const bool need_mask = (p.causal && qs < kw + 31) || kw + 32 > S || qs + 32 > S;
+      float wv[16], ds1[16], ds2[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = sub * 32 + row_of_reg(r, h);
+        float p1 = fast_exp2(fmaf(s1[r], c, -sm.lse1[qi]));
+        float p2 = fast_exp2(fmaf(s2[r], c, -sm.lse2[qi]));
+        if (need_mask) {
+          const int q = q0 + qi;
+          if (my_key >= S || q >= S || (p.causal && my_key > q)) p1 = p2 = 0.f;
+        }
+        wv[r] = (p1 - lam * p2) * fW;
+        ds1[r] = p1 * (dp[r] - sm.e1[qi]) * fdS;
+        ds2[r] = -lam * p2 * (dp[r] - sm.e2[qi]) * fdS;
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const f16x8 wb = pack8h(wv + 8 * kc2), b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
+        const int r0 = sub * 32 + kc2 * 16;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) dv[ct] = mfma32(tr_operand(sm.g, GST, r0, ct * 32, lane), wb, dv[ct]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          dk1[dt] = mfma32(tr_operand(sm.q1, QST, r0, dt * 32, lane), b1, dk1[dt]);
+          dk2[dt] = mfma32(tr_operand(sm.q2, QST, r0, dt * 32, lane), b2, dk2[dt]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
+  if (my_key < S) {
+    const float fv = exp2i(-(om + sg));
+    const float fk = p.scale * exp2i(-(kap + sg));
+    bf16 *dvp = (bf16 *)p.dv + b * p.dvs_b + (int64_t)my_key * p.dvs_s + hd * p.dvs_h;
+    bf16 *dk1p = (bf16 *)p.dk1 + b * p.dks_b + (int64_t)my_key * p.dks_s + hd * p.dks_h;
+    bf16 *dk2p = (bf16 *)p.dk2 + b * p.dks_b + (int64_t)my_key * p.dks_s + hd * p.dks_h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int ch = ct * 32 + 8 * g + 4 * h;
+        *(bf16x4 *)(dvp + ch) = bf16x4{f2bf(dv[ct][4 * g] * fv), f2bf(dv[ct][4 * g + 1] * fv),
+                                       f2bf(dv[ct][4 * g + 2] * fv), f2bf(dv[ct][4 * g + 3] * fv)};
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int ch = dt * 32 + 8 * g + 4 * h;
+        *(bf16x4 *)(dk1p + ch) = bf16x4{f2bf(dk1[dt][4 * g] * fk), f2bf(dk1[dt][4 * g + 1] * fk),
+                                        f2bf(dk1[dt][4 * g + 2] * fk), f2bf(dk1[dt][4 * g + 3] * fk)};
+        *(bf16x4 *)(dk2p + ch) = bf16x4{f2bf(dk2[dt][4 * g] * fk), f2bf(dk2[dt][4 * g + 1] * fk),
+                                        f2bf(dk2[dt][4 * g + 2] * fk), f2bf(dk2[dt][4 * g + 3] * fk)};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq: query-outer.  Workgroup = 128 queries of one (b, h); wave w owns
+// queries q0 + 32 w + 0..31 (lane l % 32).  Streams 64-key tiles of K1, K2, V
+// twice: pass 1 accumulates E_m = sum_j P_m dP, pass 2 forms dS and dQ.
+constexpr int QB = 128, KT = 64;
+
+struct SmemB {
+  f16 k1[KT * QST];
+  f16 k2[KT * QST];
+  f16 v[KT * GST];
+};
+
+__device__ __forceinline__ void stage_kv(SmemB &sm, const bf16 *k1g, const bf16 *k2g, const bf16 *vg,
+                                         int64_t ks, int64_t vs, int kbase, int S, int tid) {
+  for (int i = tid; i < KT * 8; i += NT) {
+    const int r = i >> 3, col = (i & 7) * 8, key = kbase + r;
+    u32x4 a = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
+    if (key < S) {
+      a = *(const u32x4 *)(k1g + (int64_t)key * ks + col);
+      bb = *(const u32x4 *)(k2g + (int64_t)key * ks + col);
+    }
+    *(f16x8 *)(sm.k1 + r * QST + col) = bf16x8_to_f16x8(a);
+    *(f16x8 *)(sm.k2 + r * QST + col) = bf16x8_to_f16x8(bb);
+  }
+  for (int i = tid; i < KT * 16; i += NT) {
+    const int r = i >> 4, col = (i & 15) * 8, key = kbase + r;
+    u32x4 a = {0, 0, 0, 0};
+    if (key < S) a = *(const u32x4 *)(vg + (int64_t)key * vs + col);
+    *(f16x8 *)(sm.v + r * GST + col) = bf16x8_to_f16x8(a);
+  }
+}
+
+// S1^T, S2^T and dP'^T of one 32-key sub-tile (lane = query, registers = keys).
+__device__ __forceinline__ void dq_products(const SmemB &sm, int sub, int krow, int h, const f16x8 *qf1,
+                                            const f16x8 *qf2, const f16x8 *gf, f32x16 &s1, f32x16 &s2,
+                                            f32x16 &dp) {
+  s1 = f32x16{};
+  s2 = f32x16{};
+  dp = f32x16{};
+  const f16 *ka1 = sm.k1 + (sub * 32 + krow) * QST + 8 * h;
+  const f16 *ka2 = sm.k2 + (sub * 32 + krow) * QST + 8 * h;
+  const f16 *va = sm.v + (sub * 32 + krow) * GST + 8 * h;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    s1 = mfma32(*(const f16x8 *)(ka1 + kc * 16), qf1[kc], s1);
+    s2 = mfma32(*(const f16x8 *)(ka2 + kc * 16), qf2[kc], s2);
+  }
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(va + kc * 16), gf[kc], dp);
+}
+
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
+  __shared__ SmemB sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 31, h = lane >> 5;
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  const int BH = p.B * p.H;
+  const int n_qt = (p.S + QB - 1) / QB;
+  const int bh = blockIdx.x % BH;
+  const int qt = p.causal ? n_qt - 1 - blockIdx.x / BH : blockIdx.x / BH;
+  const int b = bh / p.H, hd = bh % p.H;
+  const int S = p.S;
+  const int q0 = qt * QB, qw = q0 + wave * 32, my_q = qw + ln;
+  const float sg = w.scales[bh * 4 + 0], kap = w.scales[bh * 4 + 1];
+  const float c = p.scale * kLog2e;
+  const float fdS = exp2i(kap);
+  const int64_t statb = (int64_t)bh * S;
+  const bool qok = my_q < S;
+
+  // B operands: Q1, Q2 (for S^T = K Q^T) and g' (for dP'^T = V g'^T), fp16.
+  f16x8 qf1[4], qf2[4], gf[8];
+  {
+    const bf16 *q1 = (const bf16 *)p.q1 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
+    const bf16 *q2 = (const bf16 *)p.q2 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      qf1[kc] = qok ? bf16x8_to_f16x8(*(const u32x4 *)(q1 + kc * 16)) : f16x8{};
+      qf2[kc] = qok ? bf16x8_to_f16x8(*(const u32x4 *)(q2 + kc * 16)) : f16x8{};
+    }
+    const f16 *gp = w.gh + (statb + my_q) * DV + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) gf[kc] = qok ? *(const f16x8 *)(gp + kc * 16) : f16x8{};
+  }
+  const float L1 = qok ? p.lse1[statb + my_q] * kLog2e : __builtin_inff();
+  const float L2 = qok ? p.lse2[statb + my_q] * kLog2e : __builtin_inff();
+
+  const int kend = p.causal ? min(S, q0 + QB) : S;
+  const int n_kt = (kend + KT - 1) / KT;
+  const int krow = row_perm(ln);
+  const int q_last = qw + 31;
+  const bf16 *k1g = (const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h;
+  const bf16 *k2g = (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h;
+  const bf16 *vg = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
+
+  // ---- pass 1: E_m' = sum_j P_m dP' (this lane's half of the keys, then both halves)
+  float e1 = 0.f, e2 = 0.f;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    stage_kv(sm, k1g, k2g, vg, p.ks_s, p.vs_s, kt * KT, S, tid);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kt * KT + sub * 32;
+      if (sb >= S || (p.causal && sb > q_last)) continue;
+      f32x16 s1, s2, dp;
+      dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
+      const bool need_mask = (p.causal && sb + 31 > qw) || sb + 32 > S;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p1 = fast_exp2(fmaf(s1[r], c, -L1));
+        float p2 = fast_exp2(fmaf(s2[r], c, -L2));
+        if (need_mask) {
+          const int key = sb + row_of_reg(r, h);
+          if (key >= S || (p.causal && key > my_q)) p1 = p2 = 0.f;
+        }
+        e1 = fmaf(p1, dp[r], e1);
+        e2 = fmaf(p2, dp[r], e2);
+      }
+    }
+  }
+  e1 += other_half(e1);
+  e2 += other_half(e2);
+  if (qok && h == 0) {   // unscaled E for the KV-outer kernel and the lambda gradient
+    const float un = exp2i(-sg);
+    w.e1[statb + my_q] = e1 * un;
+    w.e2[statb + my_q] = e2 * un;
+  }
+
+  // ---- pass 2: dS and dQ
+  f32x16 dq1[2], dq2[2];
+  dq1[0] = dq1[1] = dq2[0] = dq2[1] = f32x16{};
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    stage_kv(sm, k1g, k2g, vg, p.ks_s, p.vs_s, kt * KT, S, tid);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kt * KT + sub * 32;
+      if (sb >= S || (p.causal && sb > q_last)) continue;
+      f32x16 s1, s2, dp;
+      dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
+      const bool need_mask = (p.causal && sb + 31 > qw) || sb + 32 > S;
+      float ds1[16], ds2[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p1 = fast_exp2(fmaf(s1[r], c, -L1));
+        float p2 = fast_exp2(fmaf(s2[r], c, -L2));
+        if (need_mask) {
+          const int key = sb + row_of_reg(r, h);
+          if (key >= S || (p.causal && key > my_q)) p1 = p2 = 0.f;
+        }
+        ds1[r] = p1 * (dp[r] - e1) * fdS;
+        ds2[r] = -lam * p2 * (dp[r] - e2) * fdS;
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const f16x8 b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
+        const int r0 = sub * 32 + kc2 * 16;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          dq1[dt] = mfma32(tr_operand(sm.k1, QST, r0, dt * 32, lane), b1, dq1[dt]);
+          dq2[dt] = mfma32(tr_operand(sm.k2, QST, r0, dt * 32, lane), b2, dq2[dt]);
+        }
+      }
+    }
+  }
+  if (qok) {
+    const float fq = p.scale * exp2i(-(kap + sg));
+    bf16 *d1 = (bf16 *)p.dq1 + b * p.dqs_b + (int64_t)my_q * p.dqs_s + hd * p.dqs_h;
+    bf16 *d2 = (bf16 *)p.dq2 + b * p.dqs_b + (int64_t)my_q * p.dqs_s + hd * p.dqs_h;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = dt * 32 + 8 * g + 4 * h;
+        *(bf16x4 *)(d1 + ch) = bf16x4{f2bf(dq1[dt][4 * g] * fq), f2bf(dq1[dt][4 * g + 1] * fq),
+                                      f2bf(dq1[dt][4 * g + 2] * fq), f2bf(dq1[dt][4 * g + 3] * fq)};
+        *(bf16x4 *)(d2 + ch) = bf16x4{f2bf(dq2[dt][4 * g] * fq), f2bf(dq2[dt][4 * g + 1] * fq),
+                                      f2bf(dq2[dt][4 * g + 2] * fq), f2bf(dq2[dt][4 * g + 3] * fq)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_lambda: one workgroup; dL/dlambda = sum of the rows' shares, in a fixed
+// order (per-thread strided partial sums, then a fixed reduction tree), then
+// the chain rule into the four lambda vectors.
+__global__ __launch_bounds__(NT) void bwd_lambda_kernel(BwdParams p, Ws w) {
+  __shared__ float red[NT / 64];
+  __shared__ float dl_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rows = (int64_t)p.B * p.H * p.S;
+  float s = 0.f;
+  for (int64_t i = tid; i < rows; i += NT) s += w.dlam_row[i];
+  s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    dl_sh = (red[0] + red[1]) + (red[2] + red[3]);
+    if (p.dlambda) *p.dlambda = dl_sh;
+  }
+  __syncthreads();
+  if (p.lq1 == nullptr || wave != 0) return;
+  const float dl = dl_sh;
+  float al = 0.f, be = 0.f;
+  for (int i = lane; i < p.lambda_dim; i += 64) {
+    al = fmaf(p.lq1[i], p.lk1[i], al);
+    be = fmaf(p.lq2[i], p.lk2[i], be);
+  }
+  al = wave_sum(al);
+  be = wave_sum(be);
+  const float ca = dl * expf(al), cb = -dl * expf(be);
+  for (int i = lane; i < p.lambda_dim; i += 64) {
+    p.dlq1[i] = ca * p.lk1[i];
+    p.dlk1[i] = ca * p.lq1[i];
+    p.dlq2[i] = cb * p.lk2[i];
+    p.dlk2[i] = cb * p.lq2[i];
+  }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int S, int H, int d, int dv) {
+  (void)d;
+  (void)dv;
+  return ws_bytes(B, S, H);
+}
+
+hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
+  Ws w = carve(p.workspace, p.B, p.S, p.H);
+  const int64_t rows = (int64_t)p.B * p.H * p.S;
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.B * p.H), dim3(NT), 0, st, p, w);
+  const int64_t chunks = rows * (DV / 8);
+  hipLaunchKernelGGL(bwd_gconv_kernel, dim3((chunks + NT - 1) / NT), dim3(NT), 0, st, p, w);
+  const int n_qt = (p.S + QB - 1) / QB;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.S + KVB - 1) / KVB, p.B * p.H), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_lambda_kernel, dim3(1), dim3(NT), 0, st, p, w);
+  return hipGetLastError();
+}
 
 }  // namespace diffattn

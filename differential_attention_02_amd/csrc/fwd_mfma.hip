@@ -155,6 +155,22 @@ __device__ __forceinline__ float row_scale_log2(float wmax) {
   return fminf(fmaxf(floorf(15.f - log2f(wmax)), -100.f), 100.f);
 }
 
+// w = hi + lo with both halves in fp16: lo carries the rounding residual of
+// hi, so hi V + lo V is accurate to about 2^-22 of |w| |V|.
+__device__ __forceinline__ void pack8_hilo(const float *w, f16x8 &hi, f16x8 &lo) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 x = {w[i], w[i + 1]};
+    const f16x2 y = __builtin_convertvector(x, f16x2);
+    const f32x2 back = __builtin_convertvector(y, f32x2);
+    const f16x2 z = __builtin_convertvector(x - back, f16x2);
+    hi[i] = y[0];
+    hi[i + 1] = y[1];
+    lo[i] = z[0];
+    lo[i + 1] = z[1];
+  }
+}
+
 __device__ __forceinline__ f16x8 pack8(const float *w) {
   f16x8 r;
 #pragma unroll
@@ -186,7 +202,7 @@ __device__ __forceinline__ void pv_step(const Smem &sm, int sub, int lane, const
 }
 
 template <bool SAVE>
-__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdParams p) {
+__global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, h = lane >> 5;
@@ -295,14 +311,25 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         w[r] = fast_exp2(fmaf(s1[r], c, -L1s)) - lam * fast_exp2(fmaf(s2[r], c, -L2s));
-      const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
-      pv_step(sm, sub, lane, wb, o);
-      if constexpr (SAVE) {
+      if constexpr (!SAVE) {
+        const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
+        pv_step(sm, sub, lane, wb, o);
+      } else {
+        // Training saves feed the backward, whose lambda gradient sums
+        // g . A2 over every row with heavy cancellation: O and A2 are
+        // accumulated from fp16 hi + lo weight pairs (two PV products each).
+        f16x8 hi[2], lo[2];
+        pack8_hilo(w, hi[0], lo[0]);
+        pack8_hilo(w + 8, hi[1], lo[1]);
+        pv_step(sm, sub, lane, hi, o);
+        pv_step(sm, sub, lane, lo, o);
         float w2[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) w2[r] = fast_exp2(fmaf(s2[r], c, -L2s2));
-        const f16x8 wb2[2] = {pack8(w2), pack8(w2 + 8)};
-        pv_step(sm, sub, lane, wb2, o2);
+        pack8_hilo(w2, hi[0], lo[0]);
+        pack8_hilo(w2 + 8, hi[1], lo[1]);
+        pv_step(sm, sub, lane, hi, o2);
+        pv_step(sm, sub, lane, lo, o2);
       }
     }
   }

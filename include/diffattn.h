@@ -74,7 +74,8 @@ extern "C" {
  *       function of each map's scaled scores, and the RMSNorm reciprocal
  *       root (1 when norm = 0);
  *     o_pre, a2: float32 [B, S, H, dv] contiguous - the un-normalised combine
- *       O = A1 - lambda A2 and the second map's output A2 = map2 V.
+ *       O = (map1 - lambda map2) V and the second map's output A2 = map2 V.
+ *   batch = 0 or seqlen = 0 is an empty problem: DIFFATTN_OK, nothing read.
  */
 typedef struct diffattn_fwd_args {
   int32_t batch, seqlen, heads, head_dim, v_dim;
@@ -100,8 +101,9 @@ typedef struct diffattn_fwd_args {
  * Backward arguments: gradients of L = <dout, out> for a forward with the same
  * inputs and flags (bf16, d = 64, dv = 128, causal or not).
  *   Needs the five training saves of that forward (lse1, lse2, rstd, o_pre,
- *   a2).  dout has strides do_stride; outputs dq1, dq2 (strides dq_stride),
- *   dk1, dk2 (dk_stride), dv (dv_stride) in the activation dtype.
+ *   a2).
+ *   dout has strides do_stride; outputs dq1, dq2 (strides dq_stride), dk1,
+ *   dk2 (dk_stride), dv (dv_stride) in the activation dtype.
  *   With the four lambda vectors given, dlq1, dlk1, dlq2, dlk2 (device
  *   float32[lambda_dim], all four required) receive their gradients; dlambda
  *   (optional, device float32[1]) receives dL/dlambda in either mode.

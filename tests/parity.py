@@ -51,6 +51,26 @@ def assert_bf16_tensor(got, ref, what=""):
     assert mx <= BF16_MAX and mean <= BF16_MEAN, (what, mx, mean)
 
 
+def grad_normalised(got, ref, floor_frac=5e-2):
+    """(max, mean) of per-row errors divided by max(row RMS, floor_frac x
+    tensor RMS).  Gradient rows can be exactly zero (the first query's dq sees
+    one key) or tiny (late keys in causal attention receive few queries whose
+    contributions cancel), so each row is measured against its own size but
+    never against less than 5% of the tensor's: a small row's error is
+    magnified at most 20x relative to the tensor scale."""
+    got, ref = as_f64(got), as_f64(ref)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    floor = floor_frac * np.sqrt(np.mean(ref * ref))
+    err = np.abs(got - ref) / np.maximum(rms, floor)
+    return float(err.max()), float(err.mean())
+
+
+def assert_bf16_grad(got, ref, what=""):
+    mx, mean = grad_normalised(got, ref)
+    print(f"[parity] {what}: grad row-normalised max {mx:.3e} mean {mean:.3e}", flush=True)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN, (what, mx, mean)
+
+
 def assert_f32(got, ref, what=""):
     err = float(np.abs(as_f64(got) - as_f64(ref)).max())
     print(f"[parity] {what}: max-abs {err:.3e}", flush=True)

@@ -1,0 +1,108 @@
+"""GPU parity of diffattn_bwd (through the C ABI) against the float64 oracle's
+backward, itself pinned by finite differences.  Gradients: per-row errors over
+max(row RMS, 1% of tensor RMS), max <= 2e-2 and mean <= 2e-3; the lambda
+gradient (scalar and the four vectors) as one row each."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differential_attention_02_amd import binding as B
+from differential_attention_02_amd import workloads
+from tests.parity import as_f64, assert_bf16_grad, assert_bf16_rows
+
+pytestmark = pytest.mark.gpu
+
+X = ("q1", "k1", "q2", "k2", "v")
+
+
+def _note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _run(inp, *, layer, causal, norm, eps, use_vecs=True, lambda_fixed=0.8, heads=None):
+    x = {k: inp[k].cuda() for k in X}
+    vecs = [t.cuda() for t in inp["lambda_vecs"]] if use_vecs else None
+    dy = inp["dy"].cuda()
+    li = B.lambda_init(layer)
+    y, saves = B.fwd(*(x[k] for k in X), lambda_init=li, lambda_vecs=vecs, lambda_fixed=lambda_fixed,
+                     causal=causal, norm=norm, eps=eps, save=True)
+    g = B.bwd(*(x[k] for k in X), dy, saves, lambda_init=li, lambda_vecs=vecs, lambda_fixed=lambda_fixed,
+              causal=causal, norm=norm)
+    torch.cuda.synchronize()
+    return g
+
+
+def _ref(inp, *, layer, causal, norm, eps, use_vecs=True, lambda_fixed=0.8, bh=None):
+    x = [as_f64(inp[k]) for k in X]
+    dy = as_f64(inp["dy"])
+    if bh is not None:
+        b, h = bh
+        x = [t[b:b + 1, :, h:h + 1] for t in x]
+        dy = dy[b:b + 1, :, h:h + 1]
+    li = oracle.lambda_init(layer)
+    kw = dict(lam_init=li, causal=causal, norm=norm, eps=eps)
+    if use_vecs:
+        kw["lam_vectors"] = [as_f64(t) for t in inp["lambda_vecs"]]
+    else:
+        kw["lam_fixed"] = lambda_fixed
+    return oracle.diff_attn_bwd(*x, dy, **kw)
+
+
+def _compare(g, ref, what, bh=None, with_lambda=True):
+    for k in ("dq1", "dk1", "dq2", "dk2", "dv"):
+        got = g[k].float().cpu().numpy()
+        if bh is not None:
+            got = got[bh[0]:bh[0] + 1, :, bh[1]:bh[1] + 1]
+        assert np.isfinite(got).all(), k
+        assert_bf16_grad(got, ref[k], f"{what} {k}")
+    if with_lambda:
+        assert_bf16_rows(g["dlambda"].cpu().numpy()[None, :], np.array([[ref["dlambda"]]]), f"{what} dlambda")
+        if "dlq1" in g:
+            for k in ("dlq1", "dlk1", "dlq2", "dlk2"):
+                assert_bf16_rows(g[k].cpu().numpy()[None, :], ref[k][None, :], f"{what} {k}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 32, 2), (2, 300, 3), (1, 129, 1), (1, 1000, 2)], ids=lambda s: "B%dS%dH%d" % s)
+def test_bwd_small(shape, causal):
+    Bn, S, H = shape
+    _note(f"bwd {shape} causal={causal}")
+    inp = workloads.make_attn_inputs("train_8k", seed=21, batch=Bn, seqlen=S, heads=H)
+    g = _run(inp, layer=12, causal=causal, norm=True, eps=1e-5)
+    _compare(g, _ref(inp, layer=12, causal=causal, norm=True, eps=1e-5), f"bwd {shape} causal={causal}")
+
+
+def test_bwd_no_norm_fixed_lambda():
+    inp = workloads.make_attn_inputs("train_8k", seed=22, batch=2, seqlen=256, heads=2)
+    kw = dict(layer=3, causal=True, norm=False, eps=0.0, use_vecs=False, lambda_fixed=0.9)
+    g = _run(inp, **kw)
+    _compare(g, _ref(inp, **kw), "bwd no-norm fixed lambda")
+
+
+def test_bwd_large_logits():
+    inp = workloads.make_attn_inputs("train_8k", seed=23, batch=1, seqlen=400, heads=2)
+    for k in ("q1", "k1", "q2", "k2"):
+        inp[k] = (inp[k].float() * 16.0).to(torch.bfloat16)
+    g = _run(inp, layer=12, causal=True, norm=True, eps=1e-5)
+    _compare(g, _ref(inp, layer=12, causal=True, norm=True, eps=1e-5), "bwd large logits")
+
+
+def test_bwd_medium_lambda_grads():
+    """Every head contributes to dL/dlambda: a medium case checked in full."""
+    inp = workloads.make_attn_inputs("train_8k", seed=24, batch=2, seqlen=1024, heads=4)
+    g = _run(inp, layer=12, causal=True, norm=True, eps=1e-5)
+    _compare(g, _ref(inp, layer=12, causal=True, norm=True, eps=1e-5), "bwd medium")
+
+
+def test_train_8k_full():
+    """Training workload at full size (batch 2, 8192 causal, 16 heads): the
+    kernels run on everything; the oracle checks two whole (batch, head)
+    slices of every gradient."""
+    _note("train_8k full")
+    inp = workloads.make_attn_inputs("train_8k")
+    g = _run(inp, layer=12, causal=True, norm=True, eps=1e-5)
+    for bh in ((0, 0), (1, 15)):
+        ref = _ref(inp, layer=12, causal=True, norm=True, eps=1e-5, bh=bh)
+        _compare(g, ref, f"train_8k b{bh[0]} h{bh[1]}", bh=bh, with_lambda=False)
+    assert np.isfinite(g["dlambda"].cpu().numpy()).all()
