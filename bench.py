@@ -208,6 +208,8 @@ def main(argv=None) -> int:
     ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first copy a device buffer of this many MiB (reference kernel for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -219,6 +221,14 @@ def main(argv=None) -> int:
         return 2
     from differential_attention_02_amd import binding
     binding.lib()   # fails loudly if the HIP library is missing
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)   # reads and writes calib_copy_mib MiB each
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.only is not None:
         if args.only in ("prefill_4k", "prefill_64k"):

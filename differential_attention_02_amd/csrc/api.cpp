@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/diffattn.h"
+#include "diffattn.h"
 #include "kernels.h"
 
 namespace {
@@ -125,6 +125,10 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
     const int64_t *str[] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
     if (!fused_layout_ok(ptrs, 6, str, 4))
       return fail(DIFFATTN_ERR_UNSUPPORTED, "bf16 fused path needs 16-byte aligned pointers and strides that are multiples of 8");
+    // Key tiles are addressed with 32-bit byte offsets inside one (batch, head) slice.
+    const int64_t span = (int64_t)a->seqlen * (a->k_stride[1] > a->v_stride[1] ? a->k_stride[1] : a->v_stride[1]) * 2;
+    if (span >= ((int64_t)1 << 31))
+      return fail(DIFFATTN_ERR_UNSUPPORTED, "bf16 fused path needs seqlen x key-row stride below 2^30 elements");
   }
 
   diffattn::FwdParams p{};

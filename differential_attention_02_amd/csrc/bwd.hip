@@ -23,7 +23,8 @@
 //   bwd_scales one workgroup per (batch, head): power-of-two scales that keep
 //              the fp16 operands below 2^13 (g by its largest row norm; dS by
 //              the bound |dS| <= max(1,|lambda|) (|g| |V| + |E|) <= 2 max(1,|lambda|)
-//              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|);
+//              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|), and the
+//              (batch, head) sum of the rows' dL/dlambda shares (fixed order);
 //   bwd_gconv  g scaled and rounded to fp16;
 //   bwd_dq     query-outer (the forward's layout): each workgroup owns 128
 //              queries and streams 64-key tiles twice: first E_m = sum_j P_m dP
@@ -55,6 +56,7 @@ struct Ws {
   float *e1, *e2;  // [B, H, S]  E_m = sum_j P_m dP (unscaled)
   float *gnorm, *vnorm, *dlam_row;  // [B, H, S]
   float *scales;   // [B*H][4]: sg, kappa, omega, unused (exponents of 2)
+  float *dlam_bh;  // [B*H] per-(batch, head) sums of dlam_row
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -71,13 +73,14 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
   w.vnorm = (float *)p; p += align256(rows * 4);
   w.dlam_row = (float *)p; p += align256(rows * 4);
   w.scales = (float *)p; p += align256((size_t)B * H * 16);
+  w.dlam_bh = (float *)p; p += align256((size_t)B * H * 4);
   return w;
 }
 
 __host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
   const size_t rows = (size_t)B * H * S;
   return align256(rows * DV * 4) + align256(rows * DV * 2) + 5 * align256(rows * 4) +
-         align256((size_t)B * H * 16);
+         align256((size_t)B * H * 16) + align256((size_t)B * H * 4);
 }
 
 __device__ __forceinline__ float exp2i(float e) { return fast_exp2(e); }  // e integral: exact power of 2
@@ -123,27 +126,31 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
 // ---------------------------------------------------------------------------
 // bwd_scales: one workgroup per (b, h).
 __global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
-  __shared__ float red[2][NT / 64];
+  __shared__ float red[3][NT / 64];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int64_t base = (int64_t)bh * p.S;
-  float gm = 0.f, vm = 0.f;
+  float gm = 0.f, vm = 0.f, dl = 0.f;
   for (int s = tid; s < p.S; s += NT) {
     gm = fmaxf(gm, w.gnorm[base + s]);
     vm = fmaxf(vm, w.vnorm[base + s]);
+    dl += w.dlam_row[base + s];
   }
   for (int o = 32; o > 0; o >>= 1) {
     gm = fmaxf(gm, __shfl_xor(gm, o));
     vm = fmaxf(vm, __shfl_xor(vm, o));
+    dl += __shfl_xor(dl, o);
   }
   if (lane == 0) {
     red[0][wave] = gm;
     red[1][wave] = vm;
+    red[2][wave] = dl;
   }
   __syncthreads();
   if (tid == 0) {
     gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     vm = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    w.dlam_bh[bh] = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
     const float al = fmaxf(1.f, fabsf(lam));
     const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
     const float x = 2.f * al * gm * vm;  // bound on |dS| before scaling by 2^sg
@@ -542,16 +549,15 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_lambda: one workgroup; dL/dlambda = sum of the rows' shares, in a fixed
-// order (per-thread strided partial sums, then a fixed reduction tree), then
-// the chain rule into the four lambda vectors.
+// bwd_lambda: one workgroup; dL/dlambda = sum of the (batch, head) sums that
+// bwd_scales formed, in a fixed order, then the chain rule into the four
+// lambda vectors.
 __global__ __launch_bounds__(NT) void bwd_lambda_kernel(BwdParams p, Ws w) {
   __shared__ float red[NT / 64];
   __shared__ float dl_sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
   float s = 0.f;
-  for (int64_t i = tid; i < rows; i += NT) s += w.dlam_row[i];
+  for (int i = tid; i < p.B * p.H; i += NT) s += w.dlam_bh[i];
   s = wave_sum(s);
   if (lane == 0) red[wave] = s;
   __syncthreads();

@@ -71,28 +71,47 @@ __device__ __forceinline__ int k_row_perm(int i) {
 // half h.
 __device__ __forceinline__ int key_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
 
-__device__ __forceinline__ void load_tile(const bf16 *k1, const bf16 *k2, const bf16 *v, int64_t ks,
-                                          int64_t vs, int kbase, int S, int tid, bool with_v,
-                                          TileRegs &r) {
+// Global -> register staging of one key tile through raw buffer loads: each
+// (batch, head) slice of K1, K2 and V gets a buffer resource whose range ends
+// at the slice's last key row, so rows past the sequence end read as zeros
+// without a branch.  Each thread owns fixed rows and columns of the tile; its
+// byte offsets are computed once and the tile base is added per load.
+struct TileLoader {
+  __amdgpu_buffer_rsrc_t rk1, rk2, rv;
+  uint32_t ko[2], vo[4];   // this thread's byte offsets inside a tile
+  uint32_t kstep, vstep;   // bytes per key row
+
+  __device__ __forceinline__ void init(const bf16 *k1, const bf16 *k2, const bf16 *v, int64_t ks, int64_t vs,
+                                       int S, int tid) {
+    const uint32_t kbytes = (uint32_t)((int64_t)(S - 1) * ks * 2 + D * 2);
+    const uint32_t vbytes = (uint32_t)((int64_t)(S - 1) * vs * 2 + DV * 2);
+    rk1 = __builtin_amdgcn_make_buffer_rsrc((void *)k1, 0, kbytes, 0x00020000);
+    rk2 = __builtin_amdgcn_make_buffer_rsrc((void *)k2, 0, kbytes, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, 0, vbytes, 0x00020000);
+    kstep = (uint32_t)(ks * 2);
+    vstep = (uint32_t)(vs * 2);
+    const int kr = tid >> 3, vr = tid >> 4;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8, key = kbase + row;
-    if (key < S) {
-      r.k1[i] = *(const u32x4 *)(k1 + key * ks + col);
-      r.k2[i] = *(const u32x4 *)(k2 + key * ks + col);
-    } else {
-      r.k1[i] = u32x4{0, 0, 0, 0};
-      r.k2[i] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < 2; ++i) ko[i] = (uint32_t)(kr + 32 * i) * kstep + (tid & 7) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vo[i] = (uint32_t)(vr + 16 * i) * vstep + (tid & 15) * 16;
+  }
+
+  __device__ __forceinline__ void load(int kbase, bool with_v, TileRegs &r) const {
+    const uint32_t kb = (uint32_t)kbase * kstep;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      r.k1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, (int)(ko[i] + kb), 0, 0));
+      r.k2[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk2, (int)(ko[i] + kb), 0, 0));
+    }
+    if (with_v) {
+      const uint32_t vb = (uint32_t)kbase * vstep;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(vo[i] + vb), 0, 0));
     }
   }
-  if (with_v) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NT * i, row = c >> 4, col = (c & 15) * 8, key = kbase + row;
-      r.v[i] = key < S ? *(const u32x4 *)(v + key * vs + col) : u32x4{0, 0, 0, 0};
-    }
-  }
-}
+};
 
 __device__ __forceinline__ void store_tile(Smem &sm, const TileRegs &r, int tid, bool with_v) {
 #pragma unroll
@@ -133,10 +152,10 @@ __device__ __forceinline__ void lse_update(const f32x16 &s, float c, float &m, f
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
   const float mn = fmaxf(m, mx * c);
   const float ms = mn == kNegInf ? 0.f : mn;
-  float acc = l * fast_exp2(m - ms);
+  float a[4] = {l * fast_exp2(m - ms), 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc += fast_exp2(fmaf(s[r], c, -ms));
-  l = acc;
+  for (int r = 0; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -ms));
+  l = (a[0] + a[1]) + (a[2] + a[3]);
   m = mn;
 }
 
@@ -201,9 +220,109 @@ __device__ __forceinline__ void pv_step(const Smem &sm, int sub, int lane, const
   }
 }
 
+// Masks the scores of keys past the sequence end or (causal) past the query.
+__device__ __forceinline__ void mask_scores(f32x16 &s1, f32x16 &s2, int sb, int h, int S, bool causal, int my_q) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = sb + key_of_reg(r, h);
+    if (key >= S || (causal && key > my_q)) {
+      s1[r] = kNegInf;
+      s2[r] = kNegInf;
+    }
+  }
+}
+
+// Pass 1 over one staged 64-key tile.  MASKED = false: every key of the tile
+// is visible to every query of the workgroup; both sub-tiles' score products
+// are issued before any softmax arithmetic so the exponentials of the first
+// overlap the matrix work of the second.
+template <bool MASKED>
+__device__ __forceinline__ void pass1_tile(const Smem &sm, int kbase, int krow, int h, const bf16x8 *qf1,
+                                           const bf16x8 *qf2, float c, float &m1, float &l1, float &m2,
+                                           float &l2, int S, bool causal, int qw, int my_q) {
+  if constexpr (!MASKED) {
+    f32x16 s1a, s2a, s1b, s2b;
+    scores(sm, 0, krow, h, qf1, qf2, s1a, s2a);
+    scores(sm, 1, krow, h, qf1, qf2, s1b, s2b);
+    lse_update(s1a, c, m1, l1);
+    lse_update(s2a, c, m2, l2);
+    lse_update(s1b, c, m1, l1);
+    lse_update(s2b, c, m2, l2);
+  } else {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kbase + sub * 32;
+      if (sb >= S || (causal && sb > qw + 31)) continue;
+      f32x16 s1, s2;
+      scores(sm, sub, krow, h, qf1, qf2, s1, s2);
+      if ((causal && sb + 31 > qw) || sb + 32 > S) mask_scores(s1, s2, sb, h, S, causal, my_q);
+      lse_update(s1, c, m1, l1);
+      lse_update(s2, c, m2, l2);
+    }
+  }
+}
+
+// Combined weights of one sub-tile and their PV product.
+template <bool SAVE>
+__device__ __forceinline__ void pass2_sub(const Smem &sm, int sub, int lane, const f32x16 &s1, const f32x16 &s2,
+                                          float c, float lam, float L1s, float L2s, float L2s2, f32x16 *o,
+                                          f32x16 *o2) {
+  float w[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    w[r] = fast_exp2(fmaf(s1[r], c, -L1s)) - lam * fast_exp2(fmaf(s2[r], c, -L2s));
+  if constexpr (!SAVE) {
+    const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
+    pv_step(sm, sub, lane, wb, o);
+  } else {
+    // Training saves feed the backward, whose lambda gradient sums
+    // g . A2 over every row with heavy cancellation: O and A2 are
+    // accumulated from fp16 hi + lo weight pairs (two PV products each).
+    f16x8 hi[2], lo[2];
+    pack8_hilo(w, hi[0], lo[0]);
+    pack8_hilo(w + 8, hi[1], lo[1]);
+    pv_step(sm, sub, lane, hi, o);
+    pv_step(sm, sub, lane, lo, o);
+    float w2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w2[r] = fast_exp2(fmaf(s2[r], c, -L2s2));
+    pack8_hilo(w2, hi[0], lo[0]);
+    pack8_hilo(w2 + 8, hi[1], lo[1]);
+    pv_step(sm, sub, lane, hi, o2);
+    pv_step(sm, sub, lane, lo, o2);
+  }
+}
+
+// Pass 2 over one staged tile: combined weights, PV accumulation (interior
+// tiles issue both sub-tiles' score products first, as in pass 1).
+template <bool MASKED, bool SAVE>
+__device__ __forceinline__ void pass2_tile(const Smem &sm, int kbase, int krow, int lane, const bf16x8 *qf1,
+                                           const bf16x8 *qf2, float c, float lam, float L1s, float L2s,
+                                           float L2s2, f32x16 *o, f32x16 *o2, int S, bool causal, int qw,
+                                           int my_q) {
+  const int h = lane >> 5;
+  if constexpr (!MASKED) {
+    f32x16 s1a, s2a, s1b, s2b;
+    scores(sm, 0, krow, h, qf1, qf2, s1a, s2a);
+    scores(sm, 1, krow, h, qf1, qf2, s1b, s2b);
+    pass2_sub<SAVE>(sm, 0, lane, s1a, s2a, c, lam, L1s, L2s, L2s2, o, o2);
+    pass2_sub<SAVE>(sm, 1, lane, s1b, s2b, c, lam, L1s, L2s, L2s2, o, o2);
+  } else {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kbase + sub * 32;
+      if (sb >= S || (causal && sb > qw + 31)) continue;
+      f32x16 s1, s2;
+      scores(sm, sub, krow, h, qf1, qf2, s1, s2);
+      if ((causal && sb + 31 > qw) || sb + 32 > S) mask_scores(s1, s2, sb, h, S, causal, my_q);
+      pass2_sub<SAVE>(sm, sub, lane, s1, s2, c, lam, L1s, L2s, L2s2, o, o2);
+    }
+  }
+}
+
 template <bool SAVE>
 __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p) {
-  __shared__ Smem sm;
+  __shared__ Smem sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, h = lane >> 5;
   const int BH = p.B * p.H;
@@ -214,14 +333,15 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
   const int b = bh / p.H, hd = bh % p.H;
   const int q0 = qt * BM, qw = q0 + wave * 32, my_q = qw + ln;
   const int S = p.S;
+  const bool causal = p.causal != 0;
 
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   if (blockIdx.x == 0 && tid == 0 && p.lambda_out) *p.lambda_out = lam;
   const float c = p.scale * kLog2e;
 
-  const bf16 *k1 = (const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h;
-  const bf16 *k2 = (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h;
-  const bf16 *v = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
+  TileLoader ld;
+  ld.init((const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h, (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h,
+          (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h, p.ks_s, p.vs_s, S, tid);
 
   bf16x8 qf1[4], qf2[4];
   {
@@ -234,39 +354,33 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
     }
   }
 
-  const int kend = p.causal ? min(S, q0 + BM) : S;
+  const int kend = causal ? min(S, q0 + BM) : S;
   const int n_kt = (kend + BN - 1) / BN;
+  // Tiles every query of the workgroup sees in full (no mask, no tail).
+  const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
   const int krow = k_row_perm(ln);
-  const int q_last = qw + 31;
 
   // ---------------- pass 1: per-map log2 partition functions ----------------
+  // Double-buffered LDS: tile kt is computed from buffer kt % 2 while tile
+  // kt + 1 (loaded into registers one tile ahead) is stored to the other
+  // buffer; one barrier per tile.
   float m1 = kNegInf, l1 = 0.f, m2 = kNegInf, l2 = 0.f;
   TileRegs nxt;
-  load_tile(k1, k2, v, p.ks_s, p.vs_s, 0, S, tid, false, nxt);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  ld.load(0, false, nxt);
+  store_tile(sm[0], nxt, tid, false);
+  __syncthreads();
+  // Interior tiles first (straight-line, no masks), then the diagonal / tail.
+  for (int kt = 0; kt < n_full; ++kt) {
+    ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
+    pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
-    store_tile(sm, nxt, tid, false);
+  }
+  for (int kt = n_full; kt < n_kt; ++kt) {
+    ld.load((kt + 1) * BN, false, nxt);
+    pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(k1, k2, v, p.ks_s, p.vs_s, (kt + 1) * BN, S, tid, false, nxt);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int sb = kt * BN + sub * 32;
-      if (sb >= S || (p.causal && sb > q_last)) continue;
-      f32x16 s1, s2;
-      scores(sm, sub, krow, h, qf1, qf2, s1, s2);
-      if ((p.causal && sb + 31 > qw) || sb + 32 > S) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = sb + key_of_reg(r, h);
-          if (key >= S || (p.causal && key > my_q)) {
-            s1[r] = kNegInf;
-            s2[r] = kNegInf;
-          }
-        }
-      }
-      lse_update(s1, c, m1, l1);
-      lse_update(s2, c, m2, l2);
-    }
   }
   float M1, L1, M2, L2;
   lse_finish(m1, l1, M1, L1);
@@ -285,53 +399,22 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o2[ct] = f32x16{};
   }
-  load_tile(k1, k2, v, p.ks_s, p.vs_s, 0, S, tid, true, nxt);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  ld.load(0, true, nxt);
+  store_tile(sm[0], nxt, tid, true);
+  __syncthreads();
+  for (int kt = 0; kt < n_full; ++kt) {
+    ld.load((kt + 1) * BN, true, nxt);
+    pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c, lam, L1s, L2s, L2s2, o, o2, S, causal,
+                            qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
-    store_tile(sm, nxt, tid, true);
+  }
+  for (int kt = n_full; kt < n_kt; ++kt) {
+    ld.load((kt + 1) * BN, true, nxt);
+    pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c, lam, L1s, L2s, L2s2, o, o2, S, causal,
+                           qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(k1, k2, v, p.ks_s, p.vs_s, (kt + 1) * BN, S, tid, true, nxt);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int sb = kt * BN + sub * 32;
-      if (sb >= S || (p.causal && sb > q_last)) continue;
-      f32x16 s1, s2;
-      scores(sm, sub, krow, h, qf1, qf2, s1, s2);
-      if ((p.causal && sb + 31 > qw) || sb + 32 > S) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = sb + key_of_reg(r, h);
-          if (key >= S || (p.causal && key > my_q)) {
-            s1[r] = kNegInf;
-            s2[r] = kNegInf;
-          }
-        }
-      }
-      float w[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        w[r] = fast_exp2(fmaf(s1[r], c, -L1s)) - lam * fast_exp2(fmaf(s2[r], c, -L2s));
-      if constexpr (!SAVE) {
-        const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
-        pv_step(sm, sub, lane, wb, o);
-      } else {
-        // Training saves feed the backward, whose lambda gradient sums
-        // g . A2 over every row with heavy cancellation: O and A2 are
-        // accumulated from fp16 hi + lo weight pairs (two PV products each).
-        f16x8 hi[2], lo[2];
-        pack8_hilo(w, hi[0], lo[0]);
-        pack8_hilo(w + 8, hi[1], lo[1]);
-        pv_step(sm, sub, lane, hi, o);
-        pv_step(sm, sub, lane, lo, o);
-        float w2[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w2[r] = fast_exp2(fmaf(s2[r], c, -L2s2));
-        pack8_hilo(w2, hi[0], lo[0]);
-        pack8_hilo(w2 + 8, hi[1], lo[1]);
-        pv_step(sm, sub, lane, hi, o2);
-        pv_step(sm, sub, lane, lo, o2);
-      }
-    }
   }
 
   // ---------------- epilogue: per-head RMSNorm x (1 - lambda_init) ----------------
