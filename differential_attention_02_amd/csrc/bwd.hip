@@ -53,6 +53,7 @@ constexpr int GST = DV + 32;  // LDS row stride (fp16) of g / V tiles (tr16-frie
 struct Ws {
   float *g;        // [B, H, S, DV] float32
   f16 *gh;         // [B, H, S, DV] fp16, g * 2^sg
+  f16 *qh;         // [B, H, S, 2 D] fp16: Q1 (channels 0..63) and Q2 (64..127)
   float *e1, *e2;  // [B, H, S]  E_m = sum_j P_m dP (unscaled)
   float *gnorm, *vnorm, *dlam_row;  // [B, H, S]
   float *scales;   // [B*H][4]: sg, kappa, omega, unused (exponents of 2)
@@ -67,6 +68,7 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
   Ws w;
   w.g = (float *)p; p += align256(rows * DV * 4);
   w.gh = (f16 *)p; p += align256(rows * DV * 2);
+  w.qh = (f16 *)p; p += align256(rows * 2 * D * 2);
   w.e1 = (float *)p; p += align256(rows * 4);
   w.e2 = (float *)p; p += align256(rows * 4);
   w.gnorm = (float *)p; p += align256(rows * 4);
@@ -79,7 +81,7 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
 
 __host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
   const size_t rows = (size_t)B * H * S;
-  return align256(rows * DV * 4) + align256(rows * DV * 2) + 5 * align256(rows * 4) +
+  return align256(rows * DV * 4) + align256(rows * DV * 2) + align256(rows * 2 * D * 2) + 5 * align256(rows * 4) +
          align256((size_t)B * H * 16) + align256((size_t)B * H * 4);
 }
 
@@ -182,6 +184,24 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
   *(f16x8 *)(w.gh + i * 8) = h;
 }
 
+// ---------------------------------------------------------------------------
+// bwd_qconv: Q1 | Q2 rows to fp16 (bf16 converts exactly within fp16's range),
+// 8 channels per thread, into [B, H, S, 2 D] for the key-outer kernel's
+// staging.
+__global__ __launch_bounds__(NT) void bwd_qconv_kernel(BwdParams p, Ws w) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8
+  const int64_t n = (int64_t)p.B * p.H * p.S * (2 * D / 8);
+  if (i >= n) return;
+  const int64_t row = i / (2 * D / 8);
+  const int ch = (int)(i % (2 * D / 8)) * 8;
+  const int s = row % p.S, bh = row / p.S, b = bh / p.H, hd = bh % p.H;
+  const bf16 *q = (const bf16 *)(ch < D ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s + hd * p.qs_h + (ch & (D - 1));
+  const u32x4 raw = *(const u32x4 *)q;
+  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
+                   bf16x2_to_f16x2(raw[3])};
+  *(u32x4 *)(w.qh + i * 8) = h;
+}
+
 // Permutation of rows 0..31 used for the A operand of score-like products so
 // that a lane's 16 result registers are rows 8 h + 0..7 and 16 + 8 h + 0..7.
 __device__ __forceinline__ int row_perm(int i) { return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -228,9 +248,54 @@ struct SmemA {
   float lse1[QCH], lse2[QCH], e1[QCH], e2[QCH];
 };
 
+// One thread's share of a staged query chunk: four 16-byte chunks of the
+// fp16 Q1 | Q2 rows, four of g', and (threads 0..63) one row's statistics.
+struct ChunkRegs {
+  u32x4 q[4], g[4];
+  float lse1, lse2, e1, e2;
+};
+
+// Loads the chunk of QCH query rows starting at q0 (rows past the end read as
+// zeros, their statistics as masked values).
+__device__ __forceinline__ void load_chunk(const BwdParams &p, const Ws &w, int64_t statb, int q0, int S, int tid,
+                                           float fE, ChunkRegs &r) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
+    const bool ok = q < S;
+    r.q[k] = ok ? *(const u32x4 *)(w.qh + (statb + q) * (2 * D) + col) : u32x4{0, 0, 0, 0};
+    r.g[k] = ok ? *(const u32x4 *)(w.gh + (statb + q) * DV + col) : u32x4{0, 0, 0, 0};
+  }
+  if (tid < QCH) {
+    const int q = q0 + tid;
+    const bool ok = q < S;
+    r.lse1 = ok ? p.lse1[statb + q] * kLog2e : __builtin_inff();
+    r.lse2 = ok ? p.lse2[statb + q] * kLog2e : __builtin_inff();
+    r.e1 = ok ? w.e1[statb + q] * fE : 0.f;
+    r.e2 = ok ? w.e2[statb + q] * fE : 0.f;
+  }
+}
+
+__device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int tid) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8;
+    f16 *dq = col < D ? sm.q1 + row * QST + col : sm.q2 + row * QST + (col - D);
+    *(u32x4 *)dq = r.q[k];
+    *(u32x4 *)(sm.g + row * GST + col) = r.g[k];
+  }
+  if (tid < QCH) {
+    sm.lse1[tid] = r.lse1;
+    sm.lse2[tid] = r.lse2;
+    sm.e1[tid] = r.e1;
+    sm.e2[tid] = r.e2;
+  }
+}
+
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
-  __shared__ SmemA sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 31, h = lane >> 5;
+  __shared__ SmemA smb[2];
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int bh = blockIdx.y, b = bh / p.H, hd = bh % p.H;
   const int S = p.S;
@@ -264,34 +329,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   const int q_begin = p.causal ? (kb / QCH) * QCH : 0;
   const int prow = row_perm(ln);
   const int64_t statb = (int64_t)bh * S;
-  for (int q0 = q_begin; q0 < S; q0 += QCH) {
-    __syncthreads();
-    // Stage Q1, Q2 (bf16 -> fp16), g' (fp16) and the row statistics.
-    for (int i = tid; i < QCH * 8; i += NT) {
-      const int r = i >> 3, col = (i & 7) * 8, q = q0 + r;
-      u32x4 a = {0, 0, 0, 0}, bq = {0, 0, 0, 0};
-      if (q < S) {
-        a = *(const u32x4 *)((const bf16 *)p.q1 + b * p.qs_b + (int64_t)q * p.qs_s + hd * p.qs_h + col);
-        bq = *(const u32x4 *)((const bf16 *)p.q2 + b * p.qs_b + (int64_t)q * p.qs_s + hd * p.qs_h + col);
-      }
-      *(f16x8 *)(sm.q1 + r * QST + col) = bf16x8_to_f16x8(a);
-      *(f16x8 *)(sm.q2 + r * QST + col) = bf16x8_to_f16x8(bq);
-    }
-    for (int i = tid; i < QCH * 16; i += NT) {
-      const int r = i >> 4, col = (i & 15) * 8, q = q0 + r;
-      u32x4 gv = {0, 0, 0, 0};
-      if (q < S) gv = *(const u32x4 *)(w.gh + (statb + q) * DV + col);
-      *(u32x4 *)(sm.g + r * GST + col) = gv;
-    }
-    if (tid < QCH) {
-      const int q = q0 + tid;
-      const bool ok = q < S;
-      sm.lse1[tid] = ok ? p.lse1[statb + q] * kLog2e : __builtin_inff();
-      sm.lse2[tid] = ok ? p.lse2[statb + q] * kLog2e : __builtin_inff();
-      sm.e1[tid] = ok ? w.e1[statb + q] * fE : 0.f;
-      sm.e2[tid] = ok ? w.e2[statb + q] * fE : 0.f;
-    }
-    __syncthreads();
+  // Query chunks double-buffered in LDS: chunk n + 1 is loaded into
+  // registers while chunk n is computed, then stored to the other buffer; one
+  // barrier per chunk.
+  ChunkRegs nxt;
+  if (q_begin < S) {
+    load_chunk(p, w, statb, q_begin, S, tid, fE, nxt);
+    store_chunk(smb[0], nxt, tid);
+  }
+  __syncthreads();
+  for (int q0 = q_begin, it = 0; q0 < S; q0 += QCH, ++it) {
+    SmemA &sm = smb[it & 1];
+    const bool more = q0 + QCH < S;
+    if (more) load_chunk(p, w, statb, q0 + QCH, S, tid, fE, nxt);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int qs = q0 + sub * 32;
@@ -337,6 +387,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
         }
       }
     }
+    if (more) store_chunk(smb[(it + 1) & 1], nxt, tid);
+    __syncthreads();
   }
 
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
@@ -599,6 +651,7 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
   hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.B * p.H), dim3(NT), 0, st, p, w);
   const int64_t chunks = rows * (DV / 8);
   hipLaunchKernelGGL(bwd_gconv_kernel, dim3((chunks + NT - 1) / NT), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.S + KVB - 1) / KVB, p.B * p.H), dim3(NT), 0, st, p, w);
