@@ -297,9 +297,13 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
-  const int bh = blockIdx.y, b = bh / p.H, hd = bh % p.H;
+  // Workgroup id -> (key block, batch-head): key blocks with the most causal
+  // work are dispatched first across all heads, and consecutive ids walk the
+  // (batch, head) index so a head's key blocks share one XCD's L2.
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH, b = bh / p.H, hd = bh % p.H;
   const int S = p.S;
-  const int kb = blockIdx.x * KVB, kw = kb + wave * 32, my_key = kw + ln;
+  const int kb = (blockIdx.x / BH) * KVB, kw = kb + wave * 32, my_key = kw + ln;
   const float sg = w.scales[bh * 4 + 0], kap = w.scales[bh * 4 + 1], om = w.scales[bh * 4 + 2];
   const float c = p.scale * kLog2e;
   const float fdS = exp2i(kap), fW = exp2i(om), fE = exp2i(sg);
@@ -654,7 +658,7 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
   hipLaunchKernelGGL(bwd_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.S + KVB - 1) / KVB, p.B * p.H), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.S + KVB - 1) / KVB * p.B * p.H), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_lambda_kernel, dim3(1), dim3(NT), 0, st, p, w);
   return hipGetLastError();
 }
