@@ -25,12 +25,15 @@
 //              the bound |dS| <= max(1,|lambda|) (|g| |V| + |E|) <= 2 max(1,|lambda|)
 //              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|), and the
 //              (batch, head) sum of the rows' dL/dlambda shares (fixed order);
-//   bwd_gconv  g scaled and rounded to fp16;
+//   bwd_gconv  one wave per row: g' = fp16(g 2^sg) and E_m = g' . A_m (A2
+//              saved by the forward, A1 = O + lambda A2): from the same fp16
+//              g' the matrix products use, E equals sum_j P_m dP' up to
+//              float32 rounding, so dS = P (dP - E) stays self-consistent
+//              where one key dominates a row and dP - E cancels;
+//   bwd_qconv  Q1 | Q2 rows to fp16 for the key-outer kernel's staging;
 //   bwd_dq     query-outer (the forward's layout): each workgroup owns 128
-//              queries and streams 64-key tiles twice: first E_m = sum_j P_m dP
-//              (from the very dP the second pass uses, so dS = P (dP - E) stays
-//              self-consistent where one key dominates a row and dP - E
-//              cancels), then dS and dQ1, dQ2 accumulated in registers;
+//              queries and streams 64-key tiles: dS and dQ1, dQ2 accumulated
+//              in registers;
 //   bwd_dkdv   KV-outer: each workgroup owns 128 keys (4 waves x 32) and
 //              streams 64-query chunks: recomputes P1, P2 and dP, accumulates
 //              dV, dK1, dK2 in registers.  Recomputing rather than
@@ -166,22 +169,36 @@ __global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_gconv: g' = fp16(g 2^sg), 8 channels per thread.
+// bwd_gconv: one wave per (b, h, s) row: g' = fp16(g 2^sg) and the row terms
+// E_m = g' . A_m (A2 saved by the forward, A1 = O + lambda A2), stored
+// unscaled.  Taking E from the same fp16 g' the matrix products use makes it
+// equal to sum_j P_m dP' up to float32 rounding, so dS = P (dP - E) stays
+// self-consistent where one key dominates a row and dP - E cancels.
 __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8
-  const int64_t n = (int64_t)p.B * p.H * p.S * (DV / 8);
-  if (i >= n) return;
-  const int bh = (i / (DV / 8)) / p.S;
-  const float f = exp2i(w.scales[bh * 4 + 0]);
-  const f32x4 a = *(const f32x4 *)(w.g + i * 8);
-  const f32x4 b = *(const f32x4 *)(w.g + i * 8 + 4);
-  f16x8 h;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    h[k] = (f16)(a[k] * f);
-    h[4 + k] = (f16)(b[k] * f);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over [B, H, S]
+  const int64_t nrows = (int64_t)p.B * p.H * p.S;
+  if (row >= nrows) return;
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  const int s = row % p.S;
+  const int bh = row / p.S;
+  const int b = bh / p.H, h = bh % p.H;
+  const int c = 2 * lane;
+  const float sg = w.scales[bh * 4 + 0], f = exp2i(sg);
+  const float2 g = *(const float2 *)(w.g + row * DV + c);
+  const f16x2 gh = {(f16)(g.x * f), (f16)(g.y * f)};
+  *(f16x2 *)(w.gh + row * DV + c) = gh;
+  const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
+  const float2 o = *(const float2 *)(p.o_pre + srow * DV + c);
+  const float2 a2 = *(const float2 *)(p.a2 + srow * DV + c);
+  const float g0 = (float)gh[0], g1 = (float)gh[1];
+  const float e2 = wave_sum(g0 * a2.x + g1 * a2.y);
+  const float e1 = wave_sum(g0 * fmaf(lam, a2.x, o.x) + g1 * fmaf(lam, a2.y, o.y));
+  if (lane == 0) {
+    const float un = exp2i(-sg);
+    w.e1[row] = e1 * un;
+    w.e2[row] = e2 * un;
   }
-  *(f16x8 *)(w.gh + i * 8) = h;
 }
 
 // ---------------------------------------------------------------------------
@@ -515,41 +532,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const bf16 *k2g = (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h;
   const bf16 *vg = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
 
-  // ---- pass 1: E_m' = sum_j P_m dP' (this lane's half of the keys, then both halves)
-  float e1 = 0.f, e2 = 0.f;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    stage_kv(sm, k1g, k2g, vg, p.ks_s, p.vs_s, kt * KT, S, tid);
-    __syncthreads();
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int sb = kt * KT + sub * 32;
-      if (sb >= S || (p.causal && sb > q_last)) continue;
-      f32x16 s1, s2, dp;
-      dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
-      const bool need_mask = (p.causal && sb + 31 > qw) || sb + 32 > S;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p1 = fast_exp2(fmaf(s1[r], c, -L1));
-        float p2 = fast_exp2(fmaf(s2[r], c, -L2));
-        if (need_mask) {
-          const int key = sb + row_of_reg(r, h);
-          if (key >= S || (p.causal && key > my_q)) p1 = p2 = 0.f;
-        }
-        e1 = fmaf(p1, dp[r], e1);
-        e2 = fmaf(p2, dp[r], e2);
-      }
-    }
-  }
-  e1 += other_half(e1);
-  e2 += other_half(e2);
-  if (qok && h == 0) {   // unscaled E for the KV-outer kernel and the lambda gradient
-    const float un = exp2i(-sg);
-    w.e1[statb + my_q] = e1 * un;
-    w.e2[statb + my_q] = e2 * un;
-  }
+  // E_m' = g' . A_m for this query (scaled like dP').
+  const float fE = exp2i(sg);
+  const float e1 = qok ? w.e1[statb + my_q] * fE : 0.f;
+  const float e2 = qok ? w.e2[statb + my_q] * fE : 0.f;
 
-  // ---- pass 2: dS and dQ
+  // ---- dS and dQ
   f32x16 dq1[2], dq2[2];
   dq1[0] = dq1[1] = dq2[0] = dq2[1] = f32x16{};
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -653,8 +641,7 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
   const int64_t rows = (int64_t)p.B * p.H * p.S;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.B * p.H), dim3(NT), 0, st, p, w);
-  const int64_t chunks = rows * (DV / 8);
-  hipLaunchKernelGGL(bwd_gconv_kernel, dim3((chunks + NT - 1) / NT), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_gconv_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);

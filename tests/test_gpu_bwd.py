@@ -1,6 +1,6 @@
 """GPU parity of diffattn_bwd (through the C ABI) against the float64 oracle's
 backward, itself pinned by finite differences.  Gradients: per-row errors over
-max(row RMS, 1% of tensor RMS), max <= 2e-2 and mean <= 2e-3; the lambda
+max(row RMS, 5% of tensor RMS), max <= 2e-2 and mean <= 2e-3; the lambda
 gradient (scalar and the four vectors) as one row each."""
 import numpy as np
 import pytest
