@@ -23,6 +23,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -64,7 +65,12 @@ FWD_SOURCES = ["differential_attention_02_amd/csrc/fwd_mfma.hip", "differential_
 DEC_SOURCES = ["differential_attention_02_amd/csrc/decode.hip", "differential_attention_02_amd/csrc/common.h"]
 
 
-def _time_launches(launch, steps, warmup):
+def _time_launches(launch, steps, warmup, per_launch=None):
+    """W untimed launches, then exactly K timed launches between two
+    synchronisations.  Returns (wall seconds for the K launches, mean seconds per
+    launch from HIP events on the launch stream).  With per_launch (a list), a
+    second run of K launches records one event pair around each launch and
+    appends the per-launch seconds (for median and min)."""
     import torch
     for _ in range(warmup):
         launch()
@@ -78,7 +84,32 @@ def _time_launches(launch, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if per_launch is not None:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_launch.extend(a.elapsed_time(b) / 1e3 for a, b in ev)
     return wall, e0.elapsed_time(e1) / 1e3 / steps   # seconds total, seconds per launch (events)
+
+
+def _device_info():
+    """CU count and peak clock read on the box (hipDeviceAttributeClockRate is
+    5 in hip_runtime_api.h's enum)."""
+    import ctypes
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:
+            info["peak_clock_mhz"] = v.value / 1000.0
+    except OSError:
+        pass
+    return info
 
 
 def _gpu_attn(name, steps, warmup):
@@ -92,10 +123,12 @@ def _gpu_attn(name, steps, warmup):
     out = torch.empty_like(x[4])
     args = B.fwd_args(*x, out, lambda_init=B.lambda_init(cfg.layer), lambda_vecs=vecs,
                       causal=cfg.causal, norm=True, eps=cfg.eps)
-    wall, per = _time_launches(lambda: B.fwd_launch(args), steps, warmup)
+    each = []
+    wall, per = _time_launches(lambda: B.fwd_launch(args), steps, warmup, each)
     flops = cfg.batch * cfg.heads * cfg.pairs * FLOP_PER_PAIR_FWD
     return {"cfg": cfg, "wall_s": wall, "event_s_per_launch": per, "flop_per_step": flops,
-            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12, "inputs": inp}
+            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12, "inputs": inp,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
 def _gpu_train(steps, warmup):
@@ -122,7 +155,7 @@ def _gpu_train(steps, warmup):
     pairs = cfg.batch * cfg.heads * cfg.pairs
     flops = pairs * (FLOP_PER_PAIR_FWD + FLOP_PER_PAIR_BWD)
     return {"tflops": flops * steps / wall / 1e12, "ms_per_step": wall / steps * 1e3,
-            "flop_per_step": flops}
+            "flop_per_step": flops, "inputs": inp}
 
 
 def _gpu_decode(steps, warmup):
@@ -140,13 +173,14 @@ def _gpu_decode(steps, warmup):
     nbytes = B.decode_workspace_size(args)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     args.workspace, args.workspace_bytes = ws.data_ptr(), nbytes
-    wall, per = _time_launches(lambda: B.decode_launch(args), steps, warmup)
+    each = []
+    wall, per = _time_launches(lambda: B.decode_launch(args), steps, warmup, each)
     esz = 2
     moved = (2 * cfg.batch * cfg.kv_len * cfg.kv_heads * cfg.head_dim + cfg.batch * cfg.q_heads * cfg.head_dim
              + cfg.batch * cfg.q_heads // 2 * cfg.head_dim) * esz
     return {"cfg": cfg, "bytes_per_step": moved, "gbs": moved * steps / wall / 1e9,
             "event_gbs": moved / per / 1e9, "event_s_per_launch": per, "splits": args.num_splits,
-            "sample": sample}
+            "sample": sample, "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
 def _blas_threads():
@@ -184,6 +218,26 @@ def _cpu_baseline_fwd(inp, budget_s=12.0):
                       f"{dt:.1f} s of oracle time"}
 
 
+def _cpu_baseline_train(inp):
+    """The float64 oracle's forward and backward on one (batch, head) slice of
+    the 8K training workload (all 8192 causal rows), same inputs as the GPU."""
+    import oracle
+    cfg = inp["cfg"]
+    li = oracle.lambda_init(cfg.layer)
+    vecs = [t.double().numpy() for t in inp["lambda_vecs"]]
+    lam = oracle.lambda_value(*vecs, li)
+    x = [inp[k][0:1, :, 0:1].double().numpy() for k in ("q1", "k1", "q2", "k2", "v")]
+    dy = inp["dy"][0:1, :, 0:1].double().numpy()
+    t0 = time.perf_counter()
+    oracle.diff_attn_fwd(*x, lam, li, causal=True, norm=True, eps=cfg.eps)
+    oracle.diff_attn_bwd(*x, dy, lam_init=li, lam_vectors=vecs, causal=True, norm=True, eps=cfg.eps)
+    dt = time.perf_counter() - t0
+    flops = cfg.pairs * (FLOP_PER_PAIR_FWD + FLOP_PER_PAIR_BWD)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"train_8k: 1 of {cfg.batch * cfg.heads} (batch, head) slices, all {cfg.seqlen} causal "
+                      f"rows, forward and backward; {dt:.1f} s of oracle time"}
+
+
 def _cpu_baseline_decode(sample, cfg):
     """The float64 oracle on the first 16 of the 64 sequences of the decode
     workload (same inputs as the GPU run)."""
@@ -204,7 +258,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -252,7 +306,8 @@ def main(argv=None) -> int:
                             "ms_per_step": r64["wall_s"] / max(3, args.steps // 10) * 1e3}
     tr = _gpu_train(max(3, args.steps // 10), 1)
     extra["train_8k"] = tr if "skipped" in tr else {"metric": "fwd+bwd TFLOP/s", "value": tr["tflops"],
-                                                   "ms_per_step": tr["ms_per_step"]}
+                                                   "ms_per_step": tr["ms_per_step"],
+                                                   "frac_of_bf16_peak": tr["tflops"] / PEAK_BF16_TFLOPS}
     dec = _gpu_decode(args.steps, args.warmup)
     dec_traffic = _traffic_from_profile("decode_split_v2_decode_pmc.md", DEC_SOURCES)
     extra["v2_decode"] = {
@@ -264,9 +319,12 @@ def main(argv=None) -> int:
                      "frac": dec["event_gbs"] / PEAK_HBM_GBS, "traffic": dec_traffic},
     }
     cpu = None
+    extra["v2_decode"]["median_ms"], extra["v2_decode"]["min_ms"] = dec["median_ms"], dec["min_ms"]
     if not args.no_cpu_baseline:
         cpu = _cpu_baseline_fwd(main_r["inputs"])
         extra["v2_decode"]["cpu_baseline"] = _cpu_baseline_decode(dec["sample"], dec["cfg"])
+        if "inputs" in tr:
+            extra["train_8k"]["cpu_baseline"] = _cpu_baseline_train(tr["inputs"])
     line = {
         "metric": METRIC,
         "value": main_r["tflops"],
@@ -286,6 +344,9 @@ def main(argv=None) -> int:
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
         "cpu_baseline": cpu,
+        "timing": {"median_ms": main_r["median_ms"], "min_ms": main_r["min_ms"],
+                   "note": "per-launch HIP events, a second run of the same K launches"},
+        "device": _device_info(),
         "extra": extra,
     }
     print(json.dumps(line))
