@@ -76,3 +76,29 @@ def brute_v2_decode(q, k_cache, v_cache, lam, seqlens=None, scale=None):
             row.append([heads[2 * p][c] - sg * heads[2 * p + 1][c] for c in range(D)])
         out.append(row)
     return out
+
+
+def brute_v2_prefill_fwd(q, k, v, lam, causal=True, scale=None):
+    """q: [B][S][Hq][D]; k, v: [B][S][Hkv][D]; lam: [B][S][Hq/2].
+    Returns out[B][S][Hq/2][D]."""
+    B, S, Hq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv = len(k[0][0])
+    group = Hq // Hkv
+    s = 1.0 / math.sqrt(D) if scale is None else scale
+    out = []
+    for b in range(B):
+        seq = []
+        for i in range(S):
+            n = i + 1 if causal else S
+            heads = []
+            for t in range(Hq):
+                j = t // group
+                w = _softmax([s * _dot(q[b][i][t], k[b][x][j]) for x in range(n)])
+                heads.append([math.fsum(w[x] * float(v[b][x][j][c]) for x in range(n)) for c in range(D)])
+            row = []
+            for p in range(Hq // 2):
+                sg = 1.0 / (1.0 + math.exp(-float(lam[b][i][p])))
+                row.append([heads[2 * p][c] - sg * heads[2 * p + 1][c] for c in range(D)])
+            seq.append(row)
+        out.append(seq)
+    return out

@@ -1,5 +1,5 @@
 """float64 numpy oracle for multi-head differential attention (DIFF V1) and the
-DIFF V2 decode combine.
+DIFF V2 decode and prefill combines.
 
 Test infrastructure only: imported by the tests, by the smoke check and by the
 benchmark's CPU-baseline leg, never by the product path.  Shares no code with
@@ -286,3 +286,39 @@ def v2_decode(q, k_cache, v_cache, lam, seqlens=None, scale: float | None = None
             p = np.exp(sc - np.max(sc))
             attn[b, t] = (p / np.sum(p)) @ V
     return attn[:, 0::2] - sigmoid(lam)[:, :, None] * attn[:, 1::2]
+
+
+def v2_prefill_fwd(q, k, v, lam, *, causal: bool = True, scale: float | None = None, rows=None):
+    """DIFF V2 forward over a whole sequence with grouped-query attention
+    ([V2] section "DIFF V2 innovations" items 1, 2 and 5; section "GQA
+    compatibility").
+
+    q: [B, S, Hq, D]; k, v: [B, S, Hkv, D]; query head t reads KV head
+    t // (Hq / Hkv), so each even/odd pair (2p, 2p + 1) shares one KV head.
+    Every query head runs ordinary softmax attention (scale 1/sqrt(D), causal:
+    query i sees keys j <= i); then out[b, i, p] = attn[2p] - sigmoid(lam) *
+    attn[2p + 1] with lam per token and pair: lam is [B, S, Hq/2] or anything
+    numpy broadcasts to it ([Hq/2] shares one vector across batch and tokens).
+    No per-head normalisation (V2 drops it).  rows: optional query-row indices
+    to evaluate (the output then has len(rows) rows).  Returns
+    [B, S or len(rows), Hq/2, D].
+    """
+    q, k, v = map(_f64, (q, k, v))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv or (Hq // Hkv) % 2:
+        raise ValueError("each even/odd query-head pair must share a KV head")
+    group = Hq // Hkv
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lam = np.broadcast_to(_f64(lam), (B, S, Hq // 2))
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    attn = np.zeros((B, len(rows), Hq, D))
+    for b in range(B):
+        for t in range(Hq):
+            j = t // group
+            sc = (q[b, rows, t] @ k[b, :, j].T) * s
+            if causal:
+                sc = np.where(np.arange(S)[None, :] > rows[:, None], -np.inf, sc)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            attn[b, :, t] = (p / p.sum(axis=1, keepdims=True)) @ v[b, :, j]
+    return attn[:, :, 0::2] - sigmoid(lam[:, rows])[..., None] * attn[:, :, 1::2]
