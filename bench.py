@@ -9,7 +9,10 @@ resident in HBM.  value = algorithmic TFLOP/s: 768 flop per unmasked
 width 128, counted once however the kernel schedules them).
 Also reported under "extra": the 64K-token forward, the 8K training step
 (forward + backward) when the backward is built, and the DIFF V2 decode step
-(GB/s of K/V cache + query + output bytes).
+(GB/s of K/V cache + query + output bytes), and the DIFF V2 prefill forward
+(batch 4, 4096 causal tokens, 24 query heads over 12 KV heads, D 128: 1024
+flop per unmasked (query, key, pair of query heads), two QK^T and two PV
+products of width 128).
 Each timing: W untimed launches, then exactly K launches between two
 synchronisations; HIP events on the launch stream give the average launch
 duration used for the roofline.  "cpu_baseline" times the float64 oracle on a
@@ -36,6 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FLOP_PER_PAIR_FWD = 768
 FLOP_PER_PAIR_BWD = 1280
+FLOP_PER_PAIR_V2 = 8 * 128     # per (query, key, even/odd pair of query heads), D = 128
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -61,7 +65,10 @@ def _traffic_from_profile(name, files):
     return rec.get("hbm_bytes_per_launch")
 
 
-FWD_SOURCES = ["differential_attention_02_amd/csrc/fwd_mfma.hip", "differential_attention_02_amd/csrc/common.h"]
+FWD_SOURCES = ["differential_attention_02_amd/csrc/fwd_mfma.hip", "differential_attention_02_amd/csrc/attn_tile.h",
+               "differential_attention_02_amd/csrc/common.h"]
+V2P_SOURCES = ["differential_attention_02_amd/csrc/fwd_v2.hip", "differential_attention_02_amd/csrc/attn_tile.h",
+               "differential_attention_02_amd/csrc/common.h"]
 DEC_SOURCES = ["differential_attention_02_amd/csrc/decode.hip", "differential_attention_02_amd/csrc/common.h"]
 
 
@@ -183,6 +190,23 @@ def _gpu_decode(steps, warmup):
             "sample": sample, "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
+def _gpu_v2_prefill(steps, warmup):
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["v2_prefill_4k"]
+    inp = workloads.make_v2_prefill_inputs(cfg)
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    out = torch.empty((cfg.batch, cfg.seqlen, cfg.q_heads // 2, cfg.head_dim), dtype=q.dtype, device="cuda")
+    args = B.v2_fwd_args(q, k, v, lam, out, causal=cfg.causal)
+    each = []
+    wall, per = _time_launches(lambda: B.v2_fwd_launch(args), steps, warmup, each)
+    flops = cfg.batch * (cfg.q_heads // 2) * cfg.pairs * FLOP_PER_PAIR_V2
+    return {"cfg": cfg, "wall_s": wall, "event_s_per_launch": per, "flop_per_step": flops,
+            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12, "inputs": inp,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -259,7 +283,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode"], default=None,
+    ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k"],
+                    default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -290,6 +315,10 @@ def main(argv=None) -> int:
             print(json.dumps({"workload": args.only, "tflops": r["tflops"], "event_tflops": r["event_tflops"]}))
         elif args.only == "train_8k":
             print(json.dumps({"workload": "train_8k", **_gpu_train(args.steps, args.warmup)}))
+        elif args.only == "v2_prefill_4k":
+            r = _gpu_v2_prefill(args.steps, args.warmup)
+            print(json.dumps({"workload": "v2_prefill_4k", "tflops": r["tflops"], "event_tflops": r["event_tflops"],
+                              "median_ms": r["median_ms"], "min_ms": r["min_ms"]}))
         else:
             r = _gpu_decode(args.steps, args.warmup)
             print(json.dumps({"workload": "v2_decode", "gbs": r["gbs"], "event_gbs": r["event_gbs"]}))
@@ -317,6 +346,16 @@ def main(argv=None) -> int:
                    "num_splits": "auto"},
         "roofline": {"bound": "hbm", "achieved": dec["event_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": dec["event_gbs"] / PEAK_HBM_GBS, "traffic": dec_traffic},
+    }
+    v2p = _gpu_v2_prefill(args.steps, args.warmup)
+    extra["v2_prefill_4k"] = {
+        "metric": "V2 prefill fwd TFLOP/s", "value": v2p["tflops"], "unit": "TFLOP/s",
+        "ms_per_step": v2p["wall_s"] / args.steps * 1e3,
+        "config": {"workload": "v2_prefill_4k: batch 4, seq 4096 causal, 24 query heads over 12 KV heads, "
+                               "D 128, bf16, sigmoid input per token and pair"},
+        "roofline": {"bound": "mfma", "achieved": v2p["event_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": v2p["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None},
+        "median_ms": v2p["median_ms"], "min_ms": v2p["min_ms"],
     }
     cpu = None
     extra["v2_decode"]["median_ms"], extra["v2_decode"]["min_ms"] = dec["median_ms"], dec["min_ms"]

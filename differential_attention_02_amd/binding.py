@@ -69,6 +69,18 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class V2FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_i32), ("seqlen", c_i32), ("q_heads", c_i32), ("kv_heads", c_i32), ("head_dim", c_i32),
+        ("dtype", c_i32), ("causal", c_i32),
+        ("q", c_vp), ("k", c_vp), ("v", c_vp),
+        ("q_stride", c_i64 * 3), ("kv_stride", c_i64 * 3),
+        ("lam", c_fp), ("lam_stride", c_i64 * 3),
+        ("softmax_scale", c_f32),
+        ("out", c_vp), ("o_stride", c_i64 * 3),
+    ]
+
+
 # Every symbol include/diffattn.h declares, with its ctypes signature.
 SIGNATURES = {
     "diffattn_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs), c_vp]),
@@ -76,6 +88,7 @@ SIGNATURES = {
     "diffattn_bwd_workspace_size": (c_sz, [ctypes.POINTER(BwdArgs)]),
     "diffattn_v2_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v2_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeArgs)]),
+    "diffattn_v2_fwd": (ctypes.c_int, [ctypes.POINTER(V2FwdArgs), c_vp]),
     "diffattn_lambda_init": (c_f32, [ctypes.c_int]),
     "diffattn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "diffattn_last_error": (ctypes.c_char_p, []),
@@ -332,4 +345,44 @@ def v2_decode(q, k_cache, v_cache, lam, *, seqlens=None, softmax_scale: float = 
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     a.workspace, a.workspace_bytes = _ptr(ws), nbytes
     decode_launch(a)
+    return out
+
+
+def v2_fwd_args(q, k, v, lam, out, *, causal=True, softmax_scale=0.0):
+    """V2FwdArgs for q [B,S,Hq,D], k, v [B,S,Hkv,D], out [B,S,Hq/2,D] and lam
+    [Hq/2], [S, Hq/2] or [B, S, Hq/2] (float32; missing leading axes broadcast)."""
+    _require(q.dim() == 4 and k.dim() == 4, "q must be [B, S, Hq, D], k and v [B, S, Hkv, D]")
+    B, S, Hq, D = q.shape
+    _require(k.shape[0] == B and k.shape[1] == S and k.shape[3] == D, "k shape does not match q")
+    _require(tuple(v.shape) == tuple(k.shape), "k and v shapes differ")
+    _require(tuple(out.shape) == (B, S, Hq // 2, D), "out must be [B, S, Hq/2, D]")
+    _check_dev((("q", q), ("k", k), ("v", v), ("out", out)), dtype=q.dtype, device=q.device)
+    _require(lam.dtype == torch.float32 and lam.is_cuda and lam.device == q.device, "lam: float32 on q's GPU")
+    shapes = {1: (Hq // 2,), 2: (S, Hq // 2), 3: (B, S, Hq // 2)}
+    _require(lam.dim() in shapes and tuple(lam.shape) == shapes[lam.dim()],
+             "lam must be [Hq/2], [S, Hq/2] or [B, S, Hq/2]")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    ls = (0,) * (3 - lam.dim()) + tuple(lam.stride())
+    a = V2FwdArgs()
+    a.batch, a.seqlen, a.q_heads, a.kv_heads, a.head_dim = B, S, Hq, k.shape[2], D
+    a.dtype, a.causal = _dtype_code(q), int(bool(causal))
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.q_stride, a.kv_stride = _strides3(q), _strides3(k)
+    a.lam, a.lam_stride = _ptr(lam), (c_i64 * 3)(*ls)
+    a.softmax_scale = float(softmax_scale)
+    a.out, a.o_stride = _ptr(out), _strides3(out)
+    return a
+
+
+def v2_fwd_launch(args: V2FwdArgs) -> None:
+    _check(lib().diffattn_v2_fwd(ctypes.byref(args), _stream()), "diffattn_v2_fwd")
+
+
+def v2_fwd(q, k, v, lam, *, causal: bool = True, softmax_scale: float = 0.0, out=None):
+    """DIFF V2 prefill forward through diffattn_v2_fwd; returns out [B, S, Hq/2, D]."""
+    B, S, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, S, Hq // 2, D), dtype=q.dtype, device=q.device)
+    v2_fwd_launch(v2_fwd_args(q, k, v, lam, out, causal=causal, softmax_scale=softmax_scale))
     return out

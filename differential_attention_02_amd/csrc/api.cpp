@@ -220,6 +220,48 @@ int diffattn_bwd(const diffattn_bwd_args *a, void *stream) {
   return hip_status(diffattn::launch_bwd(p, static_cast<hipStream_t>(stream)), "backward launch");
 }
 
+int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0 || a->seqlen < 0 || a->q_heads < 2 || a->kv_heads < 1)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0, q_heads >= 2, kv_heads >= 1");
+  if (a->q_heads % a->kv_heads || (a->q_heads / a->kv_heads) % 2)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                "q_heads / kv_heads must be an even integer so each even/odd pair shares a KV head");
+  if (a->dtype != DIFFATTN_F32 && a->dtype != DIFFATTN_BF16) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", a->dtype);
+  if (a->batch == 0 || a->seqlen == 0) return DIFFATTN_OK;
+  if (!a->q || !a->k || !a->v || !a->lam || !a->out)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "q, k, v, lam and out must be non-NULL");
+  if (!strides_ok(a->q_stride, 3) || !strides_ok(a->kv_stride, 3) || !strides_ok(a->o_stride, 3))
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
+  if (a->lam_stride[0] < 0 || a->lam_stride[1] < 0 || a->lam_stride[2] < 0)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "lam strides must be >= 0");
+  if (!std::isfinite(a->softmax_scale)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (a->dtype != DIFFATTN_BF16 || a->head_dim != 128)
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill is built for bf16 with head_dim 128");
+  {
+    const void *ptrs[] = {a->q, a->k, a->v, a->out};
+    const int64_t *str[] = {a->q_stride, a->kv_stride, a->o_stride};
+    if (!fused_layout_ok(ptrs, 4, str, 3))
+      return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs 16-byte aligned pointers and strides that are multiples of 8");
+  }
+  // Key tiles are addressed with 32-bit byte offsets inside one (batch, KV head)
+  // slice, including the two tiles a workgroup may prefetch past the end.
+  if (((int64_t)a->seqlen + 128) * a->kv_stride[1] * 2 >= ((int64_t)1 << 31))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs (seqlen + 128) x key-row stride below 2^30 elements");
+  diffattn::V2FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
+  p.kvs_b = a->kv_stride[0]; p.kvs_s = a->kv_stride[1]; p.kvs_h = a->kv_stride[2];
+  p.os_b = a->o_stride[0]; p.os_s = a->o_stride[1]; p.os_h = a->o_stride[2];
+  p.lam = a->lam; p.ls_b = a->lam_stride[0]; p.ls_s = a->lam_stride[1]; p.ls_p = a->lam_stride[2];
+  p.out = a->out;
+  p.B = a->batch; p.S = a->seqlen; p.Hq = a->q_heads; p.Hkv = a->kv_heads;
+  p.causal = a->causal != 0;
+  p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
+  return hip_status(diffattn::launch_fwd_v2(p, static_cast<hipStream_t>(stream)), "V2 prefill launch");
+}
+
 static int check_decode(const diffattn_v2_decode_args *a, int *splits_out) {
   if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0 || a->q_heads < 2 || a->kv_heads < 1 || a->kv_len < 0)

@@ -1,0 +1,250 @@
+// DIFF V2 prefill forward on gfx950 matrix cores: bf16 storage, head width
+// D = 128 for queries, keys and values.
+//
+// The operator (tistory page on DIFF V2, section "DIFF V2 innovations" items
+// 1, 2 and 5; section "GQA compatibility"): 2h query heads over h KV heads with
+// grouped-query attention; every query head runs ordinary softmax attention
+// (scale 1/sqrt(D), causal: query i sees keys j <= i); heads are then split
+// into even and odd along the head axis and each pair (2p, 2p + 1), which
+// shares one KV head, is combined per token as
+//   out[i, p] = attn_2p[i] - sigmoid(lambda[i, p]) attn_2p+1[i],
+// with no per-head normalisation.
+//
+// Work split.  One workgroup of 4 waves owns 128 query rows of one (batch,
+// pair); wave w owns rows 32 w .. 32 w + 31 of both query heads of the pair,
+// whose two maps read the same K and V tiles (one staged tile serves both).
+// Causal tiles are issued longest first; consecutive workgroup ids walk the
+// (batch, pair) index.
+//
+// Two passes over 64-key tiles staged through LDS (double-buffered, raw buffer
+// loads, one barrier per tile), as in the V1 forward: pass 1 computes each
+// map's log2 partition function per row; pass 2 recomputes the scores, forms
+// the combined weight W = 2^(s_e c - L_e) - sigmoid(lambda) 2^(s_o c - L_o) in
+// float32, scales it by a power of two per row (largest weight just under
+// 2^15), rounds it once to fp16 and accumulates W V with fp16 V.  Rounding the
+// combined weight keeps the error proportional to the combined map when
+// sigmoid(lambda) is near 1 and the two heads nearly cancel.  Scores are
+// computed transposed (S^T = K Q^T, lane = query); K rows are read in the
+// permuted order of the shared tile helpers so a lane's score registers are
+// the k-slots of the PV step; V^T comes through LDS transpose reads.
+#include "attn_tile.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int D = 128, BM = 128, BN = 64, NT = 256;
+constexpr int KST = D + 8;   // LDS row stride of the K tile, bf16 elements (272 B)
+constexpr int VST = D + 32;  // LDS row stride of the V tile, fp16 elements (320 B)
+
+struct SmemV2 {
+  bf16 k[BN * KST];
+  f16 v[BN * VST];  // V tile converted to fp16
+};
+
+// One thread's share of a staged tile: four 16-byte chunks of K and four of V.
+struct TileRegsV2 {
+  u32x4 k[4], v[4];
+};
+
+// Global -> register staging through raw buffer loads whose range ends at the
+// (batch, KV head) slice's last key row (rows past the end read as zeros).
+struct LoaderV2 {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t off[4];  // this thread's byte offsets inside a tile (K and V alike)
+  uint32_t step;    // bytes per key row
+
+  __device__ __forceinline__ void init(const bf16 *k, const bf16 *v, int64_t kvs, int S, int tid) {
+    const uint32_t bytes = (uint32_t)((int64_t)(S - 1) * kvs * 2 + D * 2);
+    rk = __builtin_amdgcn_make_buffer_rsrc((void *)k, 0, bytes, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, 0, bytes, 0x00020000);
+    step = (uint32_t)(kvs * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) off[i] = (uint32_t)((tid >> 4) + 16 * i) * step + (tid & 15) * 16;
+  }
+
+  __device__ __forceinline__ void load(int kbase, bool with_v, TileRegsV2 &r) const {
+    const uint32_t b = (uint32_t)kbase * step;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(off[i] + b), 0, 0));
+      if (with_v)
+        r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(off[i] + b), 0, 0));
+    }
+  }
+};
+
+__device__ __forceinline__ void store_tile(SmemV2 &sm, const TileRegsV2 &r, int tid, bool with_v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i, col = (tid & 15) * 8;
+    *(u32x4 *)(sm.k + row * KST + col) = r.k[i];
+    if (with_v) {
+      const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]), bf16x2_to_f16x2(r.v[i][2]),
+                       bf16x2_to_f16x2(r.v[i][3])};
+      *(u32x4 *)(sm.v + row * VST + col) = h;
+    }
+  }
+}
+
+// S^T sub-tile (32 keys x 32 queries) of both heads of the pair: one K
+// operand per step serves the even and the odd head.
+__device__ __forceinline__ void scores2(const SmemV2 &sm, int sub, int krow, int h, const bf16x8 *qe,
+                                        const bf16x8 *qo, f32x16 &se, f32x16 &so) {
+  const bf16 *a = sm.k + (sub * 32 + krow) * KST + 8 * h;
+  se = f32x16{};
+  so = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    const bf16x8 ka = *(const bf16x8 *)(a + kc * 16);
+    se = mfma32(ka, qe[kc], se);
+    so = mfma32(ka, qo[kc], so);
+  }
+}
+
+template <bool MASKED>
+__device__ __forceinline__ void pass1_tile(const SmemV2 &sm, int kbase, int krow, int h, const bf16x8 *qe,
+                                           const bf16x8 *qo, float c, float &me, float &le, float &mo, float &lo,
+                                           int S, bool causal, int qw, int my_q) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int sb = kbase + sub * 32;
+    if (MASKED && (sb >= S || (causal && sb > qw + 31))) continue;
+    f32x16 se, so;
+    scores2(sm, sub, krow, h, qe, qo, se, so);
+    if (MASKED && ((causal && sb + 31 > qw) || sb + 32 > S)) mask_scores(se, so, sb, h, S, causal, my_q);
+    lse_update(se, c, me, le);
+    lse_update(so, c, mo, lo);
+  }
+}
+
+template <bool MASKED>
+__device__ __forceinline__ void pass2_tile(const SmemV2 &sm, int kbase, int krow, int lane, const bf16x8 *qe,
+                                           const bf16x8 *qo, float c, float sig, float Les, float Los, f32x16 *o,
+                                           int S, bool causal, int qw, int my_q) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int sb = kbase + sub * 32;
+    if (MASKED && (sb >= S || (causal && sb > qw + 31))) continue;
+    f32x16 se, so;
+    scores2(sm, sub, krow, h, qe, qo, se, so);
+    if (MASKED && ((causal && sb + 31 > qw) || sb + 32 > S)) mask_scores(se, so, sb, h, S, causal, my_q);
+    float w[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w[r] = fast_exp2(fmaf(se[r], c, -Les)) - sig * fast_exp2(fmaf(so[r], c, -Los));
+    const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
+    pv_step_tile<VST, D / 32>(sm.v, sub, lane, wb, o);
+  }
+}
+
+__global__ __launch_bounds__(NT, 1) void fwd_v2_kernel(V2FwdParams p) {
+  __shared__ SmemV2 sm[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
+  const int ln = lane & 31, h = lane >> 5;
+  const int npair = p.Hq / 2;
+  const int BP = p.B * npair;
+  const int n_qt = (p.S + BM - 1) / BM;
+  const int bp = blockIdx.x % BP;
+  const int qt_i = blockIdx.x / BP;
+  const int qt = p.causal ? n_qt - 1 - qt_i : qt_i;
+  const int b = bp / npair, pr = bp % npair;
+  const int te = 2 * pr, j = te / (p.Hq / p.Hkv);  // even head and the pair's KV head
+  const int q0 = qt * BM, qw = q0 + wave * 32, my_q = qw + ln;
+  const int S = p.S;
+  const bool causal = p.causal != 0;
+  const bool qok = my_q < S;
+  const float c = p.scale * kLog2e;
+  const float lam = qok ? p.lam[b * p.ls_b + (int64_t)my_q * p.ls_s + pr * p.ls_p] : 0.f;
+  const float sig = 1.f / (1.f + expf(-lam));
+
+  LoaderV2 ld;
+  ld.init((const bf16 *)p.k + b * p.kvs_b + j * p.kvs_h, (const bf16 *)p.v + b * p.kvs_b + j * p.kvs_h, p.kvs_s, S,
+          tid);
+
+  bf16x8 qe[D / 16], qo[D / 16];
+  {
+    const bf16 *q = (const bf16 *)p.q + b * p.qs_b + (int64_t)my_q * p.qs_s + 8 * h;
+    const bf16 *qev = q + te * p.qs_h, *qov = q + (te + 1) * p.qs_h;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qe[kc] = qok ? *(const bf16x8 *)(qev + kc * 16) : bf16x8{};
+      qo[kc] = qok ? *(const bf16x8 *)(qov + kc * 16) : bf16x8{};
+    }
+  }
+
+  const int kend = causal ? min(S, q0 + BM) : S;
+  const int n_kt = (kend + BN - 1) / BN;
+  const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
+  const int krow = k_row_perm(ln);
+
+  // ---------------- pass 1: per-head log2 partition functions ----------------
+  float me = kNegInf, le = 0.f, mo = kNegInf, lo = 0.f;
+  TileRegsV2 nxt;
+  ld.load(0, false, nxt);
+  store_tile(sm[0], nxt, tid, false);
+  __syncthreads();
+  for (int kt = 0; kt < n_full; ++kt) {
+    ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
+    pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    __syncthreads();
+  }
+  for (int kt = n_full; kt < n_kt; ++kt) {
+    ld.load((kt + 1) * BN, false, nxt);
+    pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    __syncthreads();
+  }
+  float Me, Le, Mo, Lo;
+  lse_finish(me, le, Me, Le);
+  lse_finish(mo, lo, Mo, Lo);
+  const float sg = row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo));
+  const float Les = Le - sg, Los = Lo - sg;
+
+  // ---------------- pass 2: O = (P_e - sigmoid(lambda) P_o) V ----------------
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) o[ct] = f32x16{};
+  ld.load(0, true, nxt);
+  store_tile(sm[0], nxt, tid, true);
+  __syncthreads();
+  for (int kt = 0; kt < n_full; ++kt) {
+    ld.load((kt + 1) * BN, true, nxt);
+    pass2_tile<false>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, o, S, causal, qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    __syncthreads();
+  }
+  for (int kt = n_full; kt < n_kt; ++kt) {
+    ld.load((kt + 1) * BN, true, nxt);
+    pass2_tile<true>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, o, S, causal, qw, my_q);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue: unscale, store bf16 ----------------
+  if (qok) {
+    const float f = fast_exp2(-sg);
+    bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + pr * p.os_h;
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = ct * 32 + 8 * g + 4 * h;
+        const bf16x4 y = {f2bf(o[ct][4 * g] * f), f2bf(o[ct][4 * g + 1] * f), f2bf(o[ct][4 * g + 2] * f),
+                          f2bf(o[ct][4 * g + 3] * f)};
+        *(bf16x4 *)(out + ch) = y;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st) {
+  const int n_qt = (p.S + BM - 1) / BM;
+  hipLaunchKernelGGL(fwd_v2_kernel, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

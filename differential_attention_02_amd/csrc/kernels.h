@@ -54,10 +54,24 @@ struct DecodeParams {
   float *part_ml;  // [B, Hq, splits, 2]
 };
 
+// DIFF V2 prefill forward: Hq query heads over Hkv KV heads, bf16, D = 128.
+struct V2FwdParams {
+  const void *q, *k, *v;
+  int64_t qs_b, qs_s, qs_h, kvs_b, kvs_s, kvs_h, os_b, os_s, os_h;
+  const float *lam;  // sigmoid input per (batch, token, pair)
+  int64_t ls_b, ls_s, ls_p;
+  void *out;
+  int B, S, Hq, Hkv;
+  int causal;
+  float scale;
+};
+
 // Reference vector-ALU forward: any supported (d, dv), f32 or bf16.
 hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipStream_t st);
 // Fused bf16 matrix-core forward, d = 64, dv = 128.
 hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st);
+
+hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st);
 
 size_t bwd_workspace_bytes(int B, int S, int H, int d, int dv);
 hipError_t launch_bwd(const BwdParams &p, hipStream_t st);

@@ -4,7 +4,8 @@ Both the HIP path and the float64 oracle receive tensors made here; this module
 computes no attention, lambda or normalisation.  All draws come from a CPU
 torch.Generator seeded per call, in a fixed order:
 q1, k1, q2, k2, v, then the four lambda vectors (lq1, lk1, lq2, lk2), then the
-upstream gradient dy; for the V2 decode: q, k_cache, v_cache, lam.
+upstream gradient dy; for the V2 decode: q, k_cache, v_cache, lam; for the V2
+prefill: q, k, v, lam (then dy when a gradient is asked for).
 Each tensor is drawn in float32 one batch entry at a time, multiplied by its
 scale, and (for bf16 workloads) rounded once to bfloat16 (round to nearest
 even).  The oracle upcasts those same rounded values exactly.
@@ -16,8 +17,8 @@ import math
 
 import torch
 
-__all__ = ["AttnConfig", "DecodeConfig", "CONFIGS", "make_attn_inputs",
-           "make_decode_inputs", "worked_example_inputs"]
+__all__ = ["AttnConfig", "DecodeConfig", "V2PrefillConfig", "CONFIGS", "make_attn_inputs",
+           "make_decode_inputs", "make_v2_prefill_inputs", "worked_example_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +61,28 @@ class DecodeConfig:
     lam_shape: str = "per_head"   # "per_head" ([Hq/2]) or "per_batch_head"
 
 
+@dataclasses.dataclass(frozen=True)
+class V2PrefillConfig:
+    """A DIFF V2 prefill workload: whole sequences, Hq query heads over Hkv KV
+    heads, a sigmoid input per (batch, token, pair)."""
+    name: str
+    batch: int
+    seqlen: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    dtype: torch.dtype
+    causal: bool
+    input_scale: float          # q/k/v ~ N(0, 1) * input_scale
+    lam_std: float = 1.0        # lam ~ N(0, lam_std^2), float32 [B, S, Hq/2]
+    with_dy: bool = False
+
+    @property
+    def pairs(self) -> int:
+        s = self.seqlen
+        return s * (s + 1) // 2 if self.causal else s * s
+
+
 CONFIGS = {
     # Tiny single-head check in float32 (lambda fixed at 0.8, layer 1).
     "tiny_f32": AttnConfig("tiny_f32", 1, 64, 1, 8, 16, torch.float32, True, 1, 1.0),
@@ -75,6 +98,10 @@ CONFIGS = {
     # DIFF V2 decode: 32 query heads over 16 KV heads, cache length 8192.
     "v2_decode": DecodeConfig("v2_decode", 64, 32, 16, 128, 8192, torch.bfloat16,
                               1.0 / math.sqrt(128)),
+    # DIFF V2 prefill at 4K: 24 query heads over 12 KV heads (one even/odd pair
+    # per KV head), head width 128, causal.
+    "v2_prefill_4k": V2PrefillConfig("v2_prefill_4k", 4, 4096, 24, 12, 128, torch.bfloat16, True,
+                                     1.0 / math.sqrt(128)),
 }
 
 
@@ -134,6 +161,30 @@ def make_decode_inputs(cfg: DecodeConfig | str = "v2_decode", seed: int = 0, *,
     }
     lam_shape = (cfg.q_heads // 2,) if cfg.lam_shape == "per_head" else (B, cfg.q_heads // 2)
     t["lam"] = torch.randn(lam_shape, generator=gen, dtype=torch.float32)
+    t["cfg"] = cfg
+    return t
+
+
+def make_v2_prefill_inputs(cfg: V2PrefillConfig | str = "v2_prefill_4k", seed: int = 0, *,
+                           batch: int | None = None, seqlen: int | None = None, q_heads: int | None = None,
+                           kv_heads: int | None = None, input_scale: float | None = None) -> dict:
+    """Inputs of a DIFF V2 prefill workload on the CPU: q [B,S,Hq,D], k, v
+    [B,S,Hkv,D], lam float32 [B,S,Hq/2], dy [B,S,Hq/2,D] or None."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    B = cfg.batch if batch is None else batch
+    S = cfg.seqlen if seqlen is None else seqlen
+    Hq = cfg.q_heads if q_heads is None else q_heads
+    Hkv = cfg.kv_heads if kv_heads is None else kv_heads
+    sc = cfg.input_scale if input_scale is None else input_scale
+    gen = torch.Generator().manual_seed(seed)
+    t = {
+        "q": _draw(gen, (B, S, Hq, cfg.head_dim), sc, cfg.dtype),
+        "k": _draw(gen, (B, S, Hkv, cfg.head_dim), sc, cfg.dtype),
+        "v": _draw(gen, (B, S, Hkv, cfg.head_dim), sc, cfg.dtype),
+    }
+    t["lam"] = torch.randn((B, S, Hq // 2), generator=gen, dtype=torch.float32) * cfg.lam_std
+    t["dy"] = _draw(gen, (B, S, Hq // 2, cfg.head_dim), 1.0, cfg.dtype) if cfg.with_dy else None
     t["cfg"] = cfg
     return t
 

@@ -22,6 +22,9 @@
  *     attn_odd; pairs sit inside one grouped-query group so the KV cache is read
  *     once [neuralnode.tistory.com, section "DIFF V2 innovations" items 1, 2, 5;
  *     section "GQA compatibility"].
+ *   - DIFF V2 prefill forward: the same operator over whole sequences (causal
+ *     or not), with a sigmoid input per token and pair [same sections; item 5
+ *     makes lambda per token and per head].
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a device pointer owned by the caller (for example
@@ -165,6 +168,35 @@ typedef struct diffattn_v2_decode_args {
   size_t workspace_bytes;
 } diffattn_v2_decode_args;
 
+/*
+ * DIFF V2 prefill forward arguments (whole sequences, training or prefill).
+ *   q [B, S, Hq, D] (strides q_stride: batch, seq, head); k, v [B, S, Hkv, D]
+ *   sharing kv_stride; out [B, S, Hq/2, D] (strides o_stride).  Query head t
+ *   reads KV head t / (Hq / Hkv); Hq / Hkv must be even so that each even/odd
+ *   pair (2p, 2p + 1) shares its KV head.  Supported: bf16 with D = 128,
+ *   16-byte aligned q, k, v, out and strides that are multiples of 8.
+ *   lam: device float32, element (b, i, p) at lam[b * lam_stride[0] +
+ *   i * lam_stride[1] + p * lam_stride[2]] (strides >= 0; a zero stride
+ *   broadcasts, e.g. one value per pair shared by all tokens).
+ *   out[b, i, p] = attn_2p[b, i] - sigmoid(lam[b, i, p]) * attn_2p+1[b, i],
+ *   where attn_t = softmax(s q_t K^T) V over keys j <= i (causal) or all keys,
+ *   in fp32 arithmetic with fp16/bf16 matrix-core operands, rounded to bf16.
+ *   softmax_scale <= 0 selects s = 1/sqrt(D).
+ *   batch = 0 or seqlen = 0 is an empty problem: DIFFATTN_OK, nothing read.
+ */
+typedef struct diffattn_v2_fwd_args {
+  int32_t batch, seqlen, q_heads, kv_heads, head_dim;
+  int32_t dtype, causal;
+  const void *q, *k, *v;
+  int64_t q_stride[3];  /* batch, seq, head */
+  int64_t kv_stride[3]; /* of k and v */
+  const float *lam;
+  int64_t lam_stride[3]; /* batch, token, pair */
+  float softmax_scale;
+  void *out;
+  int64_t o_stride[3];
+} diffattn_v2_fwd_args;
+
 /* Forward pass. Returns DIFFATTN_OK or a negative status. */
 int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
 
@@ -179,6 +211,9 @@ int diffattn_v2_decode(const diffattn_v2_decode_args *args, void *stream);
 
 /* Workspace bytes diffattn_v2_decode needs for these arguments (0 if invalid). */
 size_t diffattn_v2_decode_workspace_size(const diffattn_v2_decode_args *args);
+
+/* DIFF V2 prefill forward. Returns DIFFATTN_OK or a negative status. */
+int diffattn_v2_fwd(const diffattn_v2_fwd_args *args, void *stream);
 
 /* lambda_init for layer index l >= 1: 0.8 - 0.6 exp(-0.3 (l - 1)); NaN for l < 1. */
 float diffattn_lambda_init(int layer);

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -157,6 +157,48 @@ def test_decode_rejects(field, value, code):
     assert B.lib().diffattn_v2_decode_workspace_size(ctypes.byref(a)) == 0
 
 
+def _v2_args(**kw):
+    a = B.V2FwdArgs()
+    a.batch, a.seqlen, a.q_heads, a.kv_heads, a.head_dim = 1, 256, 4, 2, 128
+    a.dtype, a.causal = B.BF16, 1
+    a.q = a.k = a.v = a.out = a.lam = FAKE
+    a.q_stride = (ctypes.c_int64 * 3)(256 * 4 * 128, 4 * 128, 128)
+    a.kv_stride = (ctypes.c_int64 * 3)(256 * 2 * 128, 2 * 128, 128)
+    a.o_stride = (ctypes.c_int64 * 3)(256 * 2 * 128, 2 * 128, 128)
+    a.lam_stride = (ctypes.c_int64 * 3)(0, 0, 1)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_v2_fwd_empty_problem_is_ok():
+    a = B.V2FwdArgs()
+    a.batch, a.seqlen, a.q_heads, a.kv_heads, a.head_dim, a.dtype = 0, 64, 4, 2, 128, B.BF16
+    assert B.lib().diffattn_v2_fwd(ctypes.byref(a), None) == 0
+    a.batch, a.seqlen = 2, 0
+    assert B.lib().diffattn_v2_fwd(ctypes.byref(a), None) == 0
+    a.seqlen = -3
+    assert B.lib().diffattn_v2_fwd(ctypes.byref(a), None) == -1
+
+
+@host_only
+@pytest.mark.parametrize("field,value,code", [
+    ("q_heads", 3, -1),          # not a multiple of kv_heads
+    ("kv_heads", 4, -1),         # group of 1: a pair would straddle two KV heads
+    ("dtype", 5, -1), ("q", None, -1), ("lam", None, -1), ("out", None, -1),
+    ("softmax_scale", float("nan"), -1),
+    ("lam_stride", (ctypes.c_int64 * 3)(0, -1, 1), -1),
+    ("kv_stride", (ctypes.c_int64 * 3)(1, 0, 128), -1),
+    ("head_dim", 64, -2), ("dtype", B.F32, -2), ("k", FAKE + 4, -2),
+    ("q_stride", (ctypes.c_int64 * 3)(256 * 4 * 128, 4 * 128 + 2, 128), -2),
+    ("seqlen", 1 << 22, -2),     # 32-bit key-tile offsets would overflow
+])
+def test_v2_fwd_rejects(field, value, code):
+    a = _v2_args(**{field: value})
+    assert B.lib().diffattn_v2_fwd(ctypes.byref(a), None) == code
+    assert B.lib().diffattn_last_error() != b""
+
+
 def test_bwd_rejects_without_saves():
     a = B.BwdArgs()
     a.batch, a.seqlen, a.heads, a.head_dim, a.v_dim = 1, 128, 2, 64, 128
@@ -183,7 +225,7 @@ def test_ctypes_layout_matches_c_compiler(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     checks = {"diffattn_fwd_args": B.FwdArgs, "diffattn_bwd_args": B.BwdArgs,
-              "diffattn_v2_decode_args": B.DecodeArgs}
+              "diffattn_v2_decode_args": B.DecodeArgs, "diffattn_v2_fwd_args": B.V2FwdArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "diffattn.h"', "int main(void) {"]
     for cname, ct in checks.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
