@@ -138,7 +138,7 @@ __device__ __forceinline__ void pass2_tile(const SmemV2 &sm, int kbase, int krow
   }
 }
 
-__global__ __launch_bounds__(NT, 1) void fwd_v2_kernel(V2FwdParams p) {
+__global__ __launch_bounds__(NT, 2) void fwd_v2_kernel(V2FwdParams p) {
   __shared__ SmemV2 sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
