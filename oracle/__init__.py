@@ -12,6 +12,7 @@ from .diffattn_oracle import (  # noqa: F401
     diff_attn_bwd,
     v2_decode,
     v2_prefill_fwd,
+    v2_prefill_bwd,
     sigmoid,
 )
 from .brute import brute_diff_attn_fwd, brute_v2_decode, brute_v2_prefill_fwd  # noqa: F401

@@ -49,6 +49,8 @@ __all__ = [
     "diff_attn_fwd",
     "diff_attn_bwd",
     "v2_decode",
+    "v2_prefill_fwd",
+    "v2_prefill_bwd",
 ]
 
 
@@ -322,3 +324,48 @@ def v2_prefill_fwd(q, k, v, lam, *, causal: bool = True, scale: float | None = N
             p = np.exp(sc - sc.max(axis=1, keepdims=True))
             attn[b, :, t] = (p / p.sum(axis=1, keepdims=True)) @ v[b, :, j]
     return attn[:, :, 0::2] - sigmoid(lam[:, rows])[..., None] * attn[:, :, 1::2]
+
+
+def v2_prefill_bwd(q, k, v, lam, dout, *, causal: bool = True, scale: float | None = None) -> dict:
+    """Gradients of L = <dout, out> for v2_prefill_fwd, by the chain rule (the
+    pages print no gradient formulas; [V2] sections "DIFF V2 innovations"
+    items 1, 2, 5 and "GQA compatibility" define the forward).
+
+    Per batch entry and pair (even head e = 2p, odd head o = 2p + 1, both on KV
+    head j), with sigma = sigmoid(lam) per token:
+      out = A_e - sigma A_o,  A_t = P_t V,  P_t = softmax(s Q_t K^T)
+      dA_e = dout,  dA_o = -sigma dout,  dlam = -sigma (1 - sigma) <dout, A_o>
+      per head t:  dP_t = dA_t V^T,  dS_t = P_t * (dP_t - rowsum(P_t * dP_t))
+                   dQ_t = s dS_t K,  dK += s dS_t^T Q_t,  dV += P_t^T dA_t
+    (dK and dV sum over every query head that reads the KV head).  Returns
+    dq [B, S, Hq, D], dk and dv [B, S, Hkv, D] and dlam [B, S, Hq/2] (the
+    gradient for a separate lam value per (batch, token, pair); a broadcast
+    lam's gradient is its sum over the broadcast axes).
+    """
+    q, k, v, dout = map(_f64, (q, k, v, dout))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv or (Hq // Hkv) % 2:
+        raise ValueError("each even/odd query-head pair must share a KV head")
+    group = Hq // Hkv
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    sig = sigmoid(np.broadcast_to(_f64(lam), (B, S, Hq // 2)))
+    rows = np.arange(S)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dlam = np.zeros((B, S, Hq // 2))
+    for b in range(B):
+        for p in range(Hq // 2):
+            j = (2 * p) // group
+            K, V = k[b, :, j], v[b, :, j]
+            g = dout[b, :, p]
+            sg = sig[b, :, p][:, None]
+            for t, dA in ((2 * p, g), (2 * p + 1, -sg * g)):
+                P = _softmax_rows(_scores(q[b, :, t], K, s, causal, rows))
+                if t % 2:
+                    dlam[b, :, p] = -(sg[:, 0] * (1.0 - sg[:, 0])) * np.sum(g * (P @ V), axis=-1)
+                dP = dA @ V.T
+                dS = P * (dP - np.sum(P * dP, axis=-1, keepdims=True))
+                dq[b, :, t] = s * (dS @ K)
+                dk[b, :, j] += s * (dS.T @ q[b, :, t])
+                dv[b, :, j] += P.T @ dA
+    return {"dq": dq, "dk": dk, "dv": dv, "dlam": dlam}
