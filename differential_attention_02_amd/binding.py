@@ -78,6 +78,24 @@ class V2FwdArgs(ctypes.Structure):
         ("lam", c_fp), ("lam_stride", c_i64 * 3),
         ("softmax_scale", c_f32),
         ("out", c_vp), ("o_stride", c_i64 * 3),
+        ("lse", c_fp), ("a_even", c_fp), ("a_odd", c_fp),
+    ]
+
+
+class V2BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_i32), ("seqlen", c_i32), ("q_heads", c_i32), ("kv_heads", c_i32), ("head_dim", c_i32),
+        ("dtype", c_i32), ("causal", c_i32),
+        ("q", c_vp), ("k", c_vp), ("v", c_vp),
+        ("q_stride", c_i64 * 3), ("kv_stride", c_i64 * 3),
+        ("lam", c_fp), ("lam_stride", c_i64 * 3),
+        ("softmax_scale", c_f32),
+        ("dout", c_vp), ("do_stride", c_i64 * 3),
+        ("lse", c_fp), ("a_even", c_fp), ("a_odd", c_fp),
+        ("dq", c_vp), ("dq_stride", c_i64 * 3),
+        ("dk", c_vp), ("dv", c_vp), ("dkv_stride", c_i64 * 3),
+        ("dlam", c_fp),
+        ("workspace", c_vp), ("workspace_bytes", c_sz),
     ]
 
 
@@ -89,6 +107,8 @@ SIGNATURES = {
     "diffattn_v2_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v2_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeArgs)]),
     "diffattn_v2_fwd": (ctypes.c_int, [ctypes.POINTER(V2FwdArgs), c_vp]),
+    "diffattn_v2_bwd": (ctypes.c_int, [ctypes.POINTER(V2BwdArgs), c_vp]),
+    "diffattn_v2_bwd_workspace_size": (c_sz, [ctypes.POINTER(V2BwdArgs)]),
     "diffattn_lambda_init": (c_f32, [ctypes.c_int]),
     "diffattn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "diffattn_last_error": (ctypes.c_char_p, []),
@@ -348,9 +368,18 @@ def v2_decode(q, k_cache, v_cache, lam, *, seqlens=None, softmax_scale: float = 
     return out
 
 
-def v2_fwd_args(q, k, v, lam, out, *, causal=True, softmax_scale=0.0):
+def _lam_strides(lam, B, S, P):
+    shapes = {1: (P,), 2: (S, P), 3: (B, S, P)}
+    _require(lam.dim() in shapes and tuple(lam.shape) == shapes[lam.dim()],
+             "lam must be [Hq/2], [S, Hq/2] or [B, S, Hq/2]")
+    return (c_i64 * 3)(*((0,) * (3 - lam.dim()) + tuple(lam.stride())))
+
+
+def v2_fwd_args(q, k, v, lam, out, *, causal=True, softmax_scale=0.0, saves=None):
     """V2FwdArgs for q [B,S,Hq,D], k, v [B,S,Hkv,D], out [B,S,Hq/2,D] and lam
-    [Hq/2], [S, Hq/2] or [B, S, Hq/2] (float32; missing leading axes broadcast)."""
+    [Hq/2], [S, Hq/2] or [B, S, Hq/2] (float32; missing leading axes
+    broadcast).  saves: optional dict of float32 training-save tensors lse
+    [B,Hq,S], a_even and a_odd [B,S,Hq/2,D] (contiguous)."""
     _require(q.dim() == 4 and k.dim() == 4, "q must be [B, S, Hq, D], k and v [B, S, Hkv, D]")
     B, S, Hq, D = q.shape
     _require(k.shape[0] == B and k.shape[1] == S and k.shape[3] == D, "k shape does not match q")
@@ -358,20 +387,22 @@ def v2_fwd_args(q, k, v, lam, out, *, causal=True, softmax_scale=0.0):
     _require(tuple(out.shape) == (B, S, Hq // 2, D), "out must be [B, S, Hq/2, D]")
     _check_dev((("q", q), ("k", k), ("v", v), ("out", out)), dtype=q.dtype, device=q.device)
     _require(lam.dtype == torch.float32 and lam.is_cuda and lam.device == q.device, "lam: float32 on q's GPU")
-    shapes = {1: (Hq // 2,), 2: (S, Hq // 2), 3: (B, S, Hq // 2)}
-    _require(lam.dim() in shapes and tuple(lam.shape) == shapes[lam.dim()],
-             "lam must be [Hq/2], [S, Hq/2] or [B, S, Hq/2]")
     if k.stride() != v.stride():
         raise ValueError("k and v must share strides")
-    ls = (0,) * (3 - lam.dim()) + tuple(lam.stride())
     a = V2FwdArgs()
     a.batch, a.seqlen, a.q_heads, a.kv_heads, a.head_dim = B, S, Hq, k.shape[2], D
     a.dtype, a.causal = _dtype_code(q), int(bool(causal))
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.q_stride, a.kv_stride = _strides3(q), _strides3(k)
-    a.lam, a.lam_stride = _ptr(lam), (c_i64 * 3)(*ls)
+    a.lam, a.lam_stride = _ptr(lam), _lam_strides(lam, B, S, Hq // 2)
     a.softmax_scale = float(softmax_scale)
     a.out, a.o_stride = _ptr(out), _strides3(out)
+    if saves is not None:
+        for name, shape in (("lse", (B, Hq, S)), ("a_even", (B, S, Hq // 2, D)), ("a_odd", (B, S, Hq // 2, D))):
+            t = saves[name]
+            _require(t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shape
+                     and t.device == q.device, f"{name}: contiguous float32 {shape} on q's GPU")
+        a.lse, a.a_even, a.a_odd = _ptr(saves["lse"]), _ptr(saves["a_even"]), _ptr(saves["a_odd"])
     return a
 
 
@@ -379,10 +410,64 @@ def v2_fwd_launch(args: V2FwdArgs) -> None:
     _check(lib().diffattn_v2_fwd(ctypes.byref(args), _stream()), "diffattn_v2_fwd")
 
 
-def v2_fwd(q, k, v, lam, *, causal: bool = True, softmax_scale: float = 0.0, out=None):
-    """DIFF V2 prefill forward through diffattn_v2_fwd; returns out [B, S, Hq/2, D]."""
+def v2_fwd(q, k, v, lam, *, causal: bool = True, softmax_scale: float = 0.0, out=None, save: bool = False):
+    """DIFF V2 prefill forward through diffattn_v2_fwd; returns out [B, S, Hq/2, D],
+    or (out, saves) with save=True (the backward's inputs)."""
     B, S, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, S, Hq // 2, D), dtype=q.dtype, device=q.device)
-    v2_fwd_launch(v2_fwd_args(q, k, v, lam, out, causal=causal, softmax_scale=softmax_scale))
-    return out
+    saves = None
+    if save:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        saves = {"lse": torch.empty((B, Hq, S), **f32), "a_even": torch.empty((B, S, Hq // 2, D), **f32),
+                 "a_odd": torch.empty((B, S, Hq // 2, D), **f32)}
+    v2_fwd_launch(v2_fwd_args(q, k, v, lam, out, causal=causal, softmax_scale=softmax_scale, saves=saves))
+    return (out, saves) if save else out
+
+
+def v2_bwd_args(q, k, v, lam, dout, saves, dq, dk, dv, dlam, *, causal=True, softmax_scale=0.0):
+    """V2BwdArgs (workspace not yet attached); dlam is float32 [B, S, Hq/2]
+    contiguous (the per-(batch, token, pair) gradient)."""
+    a = V2BwdArgs()
+    fa = v2_fwd_args(q, k, v, lam, dout, causal=causal, softmax_scale=softmax_scale, saves=saves)
+    B, S, Hq, D = q.shape
+    _require(tuple(dq.shape) == tuple(q.shape) and tuple(dk.shape) == tuple(k.shape)
+             and tuple(dv.shape) == tuple(v.shape), "dq, dk, dv must match q, k, v")
+    _check_dev((("dq", dq), ("dk", dk), ("dv", dv)), dtype=q.dtype, device=q.device)
+    if dk.stride() != dv.stride():
+        raise ValueError("dk and dv must share strides")
+    _require(dlam.dtype == torch.float32 and dlam.is_contiguous() and tuple(dlam.shape) == (B, S, Hq // 2)
+             and dlam.device == q.device, "dlam: contiguous float32 [B, S, Hq/2] on q's GPU")
+    for name, _ in V2FwdArgs._fields_:
+        if hasattr(a, name) and name not in ("out", "o_stride"):
+            setattr(a, name, getattr(fa, name))
+    a.dout, a.do_stride = _ptr(dout), _strides3(dout)
+    a.dq, a.dq_stride = _ptr(dq), _strides3(dq)
+    a.dk, a.dv, a.dkv_stride = _ptr(dk), _ptr(dv), _strides3(dk)
+    a.dlam = _ptr(dlam)
+    return a
+
+
+def v2_bwd_workspace_size(args: V2BwdArgs) -> int:
+    return int(lib().diffattn_v2_bwd_workspace_size(ctypes.byref(args)))
+
+
+def v2_bwd_launch(args: V2BwdArgs) -> None:
+    _check(lib().diffattn_v2_bwd(ctypes.byref(args), _stream()), "diffattn_v2_bwd")
+
+
+def v2_bwd(q, k, v, lam, dout, saves, *, causal: bool = True, softmax_scale: float = 0.0):
+    """DIFF V2 prefill backward through diffattn_v2_bwd.  Returns dq, dk, dv and
+    dlam, the latter summed over the axes lam broadcast over (lam's shape)."""
+    B, S, Hq, D = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dlam = torch.empty((B, S, Hq // 2), dtype=torch.float32, device=q.device)
+    a = v2_bwd_args(q, k, v, lam, dout, saves, dq, dk, dv, dlam, causal=causal, softmax_scale=softmax_scale)
+    nbytes = v2_bwd_workspace_size(a)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    a.workspace, a.workspace_bytes = _ptr(ws), nbytes
+    v2_bwd_launch(a)
+    dl = dlam
+    if lam.dim() < 3:
+        dl = dlam.sum(dim=tuple(range(3 - lam.dim())))
+    return {"dq": dq, "dk": dk, "dv": dv, "dlam": dl}

@@ -220,35 +220,50 @@ int diffattn_bwd(const diffattn_bwd_args *a, void *stream) {
   return hip_status(diffattn::launch_bwd(p, static_cast<hipStream_t>(stream)), "backward launch");
 }
 
+// Checks shared by the V2 prefill forward and backward (shapes, pointers of
+// the forward inputs, strides, layout and offset range).
+static int check_v2_common(int B, int S, int Hq, int Hkv, int D, int dtype, const void *q, const void *k,
+                           const void *v, const float *lam, const int64_t *qs, const int64_t *kvs,
+                           const int64_t *ls, float scale) {
+  if (B < 0 || S < 0 || Hq < 2 || Hkv < 1)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0, q_heads >= 2, kv_heads >= 1");
+  if (Hq % Hkv || (Hq / Hkv) % 2)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
+                "q_heads / kv_heads must be an even integer so each even/odd pair shares a KV head");
+  if (dtype != DIFFATTN_F32 && dtype != DIFFATTN_BF16) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (!q || !k || !v || !lam) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "q, k, v and lam must be non-NULL");
+  if (!strides_ok(qs, 3) || !strides_ok(kvs, 3)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
+  if (ls[0] < 0 || ls[1] < 0 || ls[2] < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "lam strides must be >= 0");
+  if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (dtype != DIFFATTN_BF16 || D != 128)
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill is built for bf16 with head_dim 128");
+  // Key tiles are addressed with 32-bit byte offsets inside one (batch, KV head)
+  // slice, including the two tiles a workgroup may prefetch past the end.
+  if (((int64_t)S + 128) * kvs[1] * 2 >= ((int64_t)1 << 31))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs (seqlen + 128) x key-row stride below 2^30 elements");
+  return DIFFATTN_OK;
+}
+
 int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
   g_last_error.clear();
   if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->batch < 0 || a->seqlen < 0 || a->q_heads < 2 || a->kv_heads < 1)
-    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0, q_heads >= 2, kv_heads >= 1");
-  if (a->q_heads % a->kv_heads || (a->q_heads / a->kv_heads) % 2)
-    return fail(DIFFATTN_ERR_INVALID_ARGUMENT,
-                "q_heads / kv_heads must be an even integer so each even/odd pair shares a KV head");
-  if (a->dtype != DIFFATTN_F32 && a->dtype != DIFFATTN_BF16) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", a->dtype);
-  if (a->batch == 0 || a->seqlen == 0) return DIFFATTN_OK;
-  if (!a->q || !a->k || !a->v || !a->lam || !a->out)
-    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "q, k, v, lam and out must be non-NULL");
-  if (!strides_ok(a->q_stride, 3) || !strides_ok(a->kv_stride, 3) || !strides_ok(a->o_stride, 3))
-    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
-  if (a->lam_stride[0] < 0 || a->lam_stride[1] < 0 || a->lam_stride[2] < 0)
-    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "lam strides must be >= 0");
-  if (!std::isfinite(a->softmax_scale)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  if (a->dtype != DIFFATTN_BF16 || a->head_dim != 128)
-    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill is built for bf16 with head_dim 128");
+  if (a->batch == 0 || a->seqlen == 0) {
+    if (a->batch < 0 || a->seqlen < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0");
+    return DIFFATTN_OK;
+  }
+  int rc = check_v2_common(a->batch, a->seqlen, a->q_heads, a->kv_heads, a->head_dim, a->dtype, a->q, a->k, a->v,
+                           a->lam, a->q_stride, a->kv_stride, a->lam_stride, a->softmax_scale);
+  if (rc) return rc;
+  if (!a->out) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+  if (!strides_ok(a->o_stride, 3)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
+  const int nsave = (a->lse != nullptr) + (a->a_even != nullptr) + (a->a_odd != nullptr);
+  if (nsave != 0 && nsave != 3) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "give all three training saves or none");
   {
-    const void *ptrs[] = {a->q, a->k, a->v, a->out};
+    const void *ptrs[] = {a->q, a->k, a->v, a->out, a->a_even, a->a_odd};
     const int64_t *str[] = {a->q_stride, a->kv_stride, a->o_stride};
-    if (!fused_layout_ok(ptrs, 4, str, 3))
+    if (!fused_layout_ok(ptrs, 6, str, 3))
       return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs 16-byte aligned pointers and strides that are multiples of 8");
   }
-  // Key tiles are addressed with 32-bit byte offsets inside one (batch, KV head)
-  // slice, including the two tiles a workgroup may prefetch past the end.
-  if (((int64_t)a->seqlen + 128) * a->kv_stride[1] * 2 >= ((int64_t)1 << 31))
-    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs (seqlen + 128) x key-row stride below 2^30 elements");
   diffattn::V2FwdParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
@@ -259,7 +274,65 @@ int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
   p.B = a->batch; p.S = a->seqlen; p.Hq = a->q_heads; p.Hkv = a->kv_heads;
   p.causal = a->causal != 0;
   p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
+  p.lse = a->lse; p.a_even = a->a_even; p.a_odd = a->a_odd;
   return hip_status(diffattn::launch_fwd_v2(p, static_cast<hipStream_t>(stream)), "V2 prefill launch");
+}
+
+static int check_v2_bwd(const diffattn_v2_bwd_args *a) {
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  int rc = check_v2_common(a->batch, a->seqlen, a->q_heads, a->kv_heads, a->head_dim, a->dtype, a->q, a->k, a->v,
+                           a->lam, a->q_stride, a->kv_stride, a->lam_stride, a->softmax_scale);
+  if (rc) return rc;
+  if (!a->dout) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "dout must be non-NULL");
+  if (!a->lse || !a->a_even || !a->a_odd)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "backward needs the forward's three training saves");
+  if (!a->dq || !a->dk || !a->dv || !a->dlam)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "dq, dk, dv and dlam must be non-NULL");
+  if (!strides_ok(a->do_stride, 3) || !strides_ok(a->dq_stride, 3) || !strides_ok(a->dkv_stride, 3))
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
+  const void *ptrs[] = {a->q, a->k, a->v, a->dout, a->dq, a->dk, a->dv, a->a_even, a->a_odd};
+  const int64_t *str[] = {a->q_stride, a->kv_stride, a->do_stride, a->dq_stride, a->dkv_stride};
+  if (!fused_layout_ok(ptrs, 9, str, 5))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 backward needs 16-byte aligned pointers and strides that are multiples of 8");
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_v2_bwd_workspace_size(const diffattn_v2_bwd_args *a) {
+  std::string keep = g_last_error;
+  const int rc = (a && (a->batch == 0 || a->seqlen == 0)) ? DIFFATTN_OK : check_v2_bwd(a);
+  g_last_error = keep;
+  if (rc || a->batch <= 0 || a->seqlen <= 0) return 0;
+  return diffattn::v2_bwd_workspace_bytes(a->batch, a->seqlen, a->q_heads, a->kv_heads);
+}
+
+int diffattn_v2_bwd(const diffattn_v2_bwd_args *a, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0 || a->seqlen < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0");
+  if (a->batch == 0 || a->seqlen == 0) return DIFFATTN_OK;
+  int rc = check_v2_bwd(a);
+  if (rc) return rc;
+  const size_t need = diffattn::v2_bwd_workspace_bytes(a->batch, a->seqlen, a->q_heads, a->kv_heads);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(DIFFATTN_ERR_WORKSPACE, "V2 backward needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  diffattn::V2BwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.dout = a->dout;
+  p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
+  p.kvs_b = a->kv_stride[0]; p.kvs_s = a->kv_stride[1]; p.kvs_h = a->kv_stride[2];
+  p.ds_b = a->do_stride[0]; p.ds_s = a->do_stride[1]; p.ds_h = a->do_stride[2];
+  p.lam = a->lam; p.ls_b = a->lam_stride[0]; p.ls_s = a->lam_stride[1]; p.ls_p = a->lam_stride[2];
+  p.lse = a->lse; p.a_even = a->a_even; p.a_odd = a->a_odd;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.dqs_b = a->dq_stride[0]; p.dqs_s = a->dq_stride[1]; p.dqs_h = a->dq_stride[2];
+  p.dkvs_b = a->dkv_stride[0]; p.dkvs_s = a->dkv_stride[1]; p.dkvs_h = a->dkv_stride[2];
+  p.dlam = a->dlam;
+  p.B = a->batch; p.S = a->seqlen; p.Hq = a->q_heads; p.Hkv = a->kv_heads;
+  p.causal = a->causal != 0;
+  p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
+  p.workspace = a->workspace;
+  return hip_status(diffattn::launch_v2_bwd(p, static_cast<hipStream_t>(stream)), "V2 backward launch");
 }
 
 static int check_decode(const diffattn_v2_decode_args *a, int *splits_out) {

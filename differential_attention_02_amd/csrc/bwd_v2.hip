@@ -1,0 +1,560 @@
+// Backward of the DIFF V2 prefill forward on gfx950 (bf16 storage, D = 128).
+// The pages print no gradient formulas; these are the chain rule of the
+// forward (tistory page on DIFF V2, section "DIFF V2 innovations" items 1, 2
+// and 5; section "GQA compatibility").  Per batch entry and pair (even head
+// e = 2p, odd head o = 2p + 1, both reading KV head j), sigma = sigmoid(lam)
+// per token:
+//   out = A_e - sigma A_o,  A_t = P_t V,  P_t = softmax(s Q_t K^T)
+//   dlam = -sigma (1 - sigma) g . A_o                  (g = dout, per row)
+//   dV = (P_e - sigma P_o)^T g                         (one product per pair)
+//   dP = g V^T                                         (shared by both heads)
+//   E_t = g . A_t  (each head's own output, saved by the forward in float32)
+//   dS_e = P_e (dP - E_e),  dS_o = -sigma P_o (dP - E_o)
+//   dQ_t = s dS_t K,  dK = s sum_t dS_t^T Q_t (over every head reading j)
+//
+// Kernels, in launch order:
+//   v2b_pre    one wave per (batch, pair, token) row: |g| and dlam from the
+//              float32 g and the saved A_o;
+//   v2b_scales one workgroup per (batch, KV head): power-of-two scales that
+//              keep the fp16 operands below 2^13: g by the largest row norm
+//              of the pairs on the head, dS by the bound
+//              |dS| <= 2 max|g| max|V| (|A_t| <= max|V|), W = P_e - sigma P_o
+//              (|W| <= 1) by a fixed 2^12;
+//   v2b_gconv  one wave per row: g' = fp16(g 2^sg) and E_t = g' . A_t from
+//              that same fp16 g' and A_t accumulated with head t's own
+//              weights (so dS = P (dP - E) stays self-consistent where one key
+//              dominates a row and dP - E cancels);
+//   v2b_qconv  Q_e | Q_o rows to fp16 for the key-outer kernel's staging;
+//   v2b_dq     query-outer: 128 queries of one (batch, pair) per workgroup,
+//              64-key tiles; dS and dQ of both heads in registers;
+//   v2b_dkdv   key-outer: 128 keys of one (batch, KV head) per workgroup,
+//              every pair of the head, 64-query chunks double-buffered in
+//              LDS; dV and dK in registers.  No atomics: deterministic.
+// Matrix-core operands are fp16 (bf16 inputs convert exactly within fp16's
+// range) with float32 accumulation.
+#include "common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int D = 128, NT = 256;
+constexpr int QST = D + 8;   // LDS row stride (fp16) of Q / K tiles (272 B)
+constexpr int GST = D + 32;  // LDS row stride (fp16) of g / V tiles (320 B, transpose-read friendly)
+
+struct Ws2 {
+  f16 *gh;               // [B, P, S, D]  g' = g 2^sg
+  f16 *qh;               // [B, P, S, 2 D] Q_e (channels 0..127) | Q_o (128..255)
+  float *ee, *eo, *gn;   // [B, P, S]  E_e, E_o (unscaled), |g|
+  float *scales;         // [B * Hkv][4]: sg, kappa, omega, unused (exponents of 2)
+};
+
+__host__ __device__ inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline Ws2 carve2(void *base, int B, int S, int P, int Hkv) {
+  char *c = static_cast<char *>(base);
+  const size_t rows = (size_t)B * P * S;
+  Ws2 w;
+  w.gh = (f16 *)c; c += al256(rows * D * 2);
+  w.qh = (f16 *)c; c += al256(rows * 2 * D * 2);
+  w.ee = (float *)c; c += al256(rows * 4);
+  w.eo = (float *)c; c += al256(rows * 4);
+  w.gn = (float *)c; c += al256(rows * 4);
+  w.scales = (float *)c; c += al256((size_t)B * Hkv * 16);
+  return w;
+}
+
+__host__ __device__ inline size_t ws2_bytes(int B, int S, int P, int Hkv) {
+  const size_t rows = (size_t)B * P * S;
+  return al256(rows * D * 2) + al256(rows * 2 * D * 2) + 3 * al256(rows * 4) + al256((size_t)B * Hkv * 16);
+}
+
+__device__ __forceinline__ float sigmoid_of(const V2BwdParams &p, int b, int s, int pr) {
+  const float lam = p.lam[b * p.ls_b + (int64_t)s * p.ls_s + pr * p.ls_p];
+  return 1.f / (1.f + expf(-lam));
+}
+
+// ---------------------------------------------------------------------------
+// v2b_pre: one wave per (b, pair, s) row; lane holds channels 2 lane, 2 lane + 1.
+__global__ __launch_bounds__(NT) void v2b_pre_kernel(V2BwdParams p, Ws2 w) {
+  const int lane = threadIdx.x & 63;
+  const int P = p.Hq / 2;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over [B, P, S]
+  if (row >= (int64_t)p.B * P * p.S) return;
+  const int s = row % p.S;
+  const int bp = row / p.S, b = bp / P, pr = bp % P;
+  const int c = 2 * lane;
+  const bf16 *gp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c;
+  const int64_t srow = (((int64_t)b * p.S + s) * P + pr) * D;
+  const float2 ao = *(const float2 *)(p.a_odd + srow + c);
+  const float g0 = bf2f(gp[0]), g1 = bf2f(gp[1]);
+  const float gg = wave_sum(g0 * g0 + g1 * g1);
+  const float ga = wave_sum(g0 * ao.x + g1 * ao.y);
+  if (lane == 0) {
+    const float sg = sigmoid_of(p, b, s, pr);
+    w.gn[row] = sqrtf(gg);
+    p.dlam[((int64_t)b * p.S + s) * P + pr] = -sg * (1.f - sg) * ga;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// v2b_scales: one workgroup per (b, KV head j).
+__global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
+  __shared__ float red[2][NT / 64];
+  const int bj = blockIdx.x, b = bj / p.Hkv, j = bj % p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;  // pairs per KV head
+  float gm = 0.f;
+  for (int pp = 0; pp < ppk; ++pp) {
+    const int64_t base = ((int64_t)b * P + j * ppk + pp) * p.S;
+    for (int s = tid; s < p.S; s += NT) gm = fmaxf(gm, w.gn[base + s]);
+  }
+  // |V| rows of this KV head: one wave per row.
+  float vm = 0.f;
+  const bf16 *vb = (const bf16 *)p.v + b * p.kvs_b + j * p.kvs_h + 2 * lane;
+  for (int s = wave; s < p.S; s += NT / 64) {
+    const bf16 *vr = vb + (int64_t)s * p.kvs_s;
+    const float v0 = bf2f(vr[0]), v1 = bf2f(vr[1]);
+    vm = fmaxf(vm, wave_sum(v0 * v0 + v1 * v1));
+  }
+  for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+  if (lane == 0) {
+    red[0][wave] = gm;
+    red[1][wave] = vm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    vm = sqrtf(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])));
+    const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
+    const float x = 2.f * gm * vm;  // bound on |dS| before scaling by 2^sg
+    const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) : 0.f;
+    w.scales[bj * 4 + 0] = sg;
+    w.scales[bj * 4 + 1] = kap;
+    w.scales[bj * 4 + 2] = 12.f;
+    w.scales[bj * 4 + 3] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// v2b_gconv: one wave per (b, pair, s) row: g' = fp16(g 2^sg) and
+// E_e = g' . A_e, E_o = g' . A_o, stored unscaled.
+__global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
+  const int lane = threadIdx.x & 63;
+  const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)p.B * P * p.S) return;
+  const int s = row % p.S;
+  const int bp = row / p.S, b = bp / P, pr = bp % P;
+  const int bj = b * p.Hkv + pr / ppk;
+  const int c = 2 * lane;
+  const float sg = w.scales[bj * 4 + 0], f = fast_exp2(sg);
+  const bf16 *gp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c;
+  const f16x2 gh = {(f16)(bf2f(gp[0]) * f), (f16)(bf2f(gp[1]) * f)};
+  *(f16x2 *)(w.gh + row * D + c) = gh;
+  const int64_t srow = (((int64_t)b * p.S + s) * P + pr) * D;
+  const float2 ae = *(const float2 *)(p.a_even + srow + c);
+  const float2 ao = *(const float2 *)(p.a_odd + srow + c);
+  const float g0 = (float)gh[0], g1 = (float)gh[1];
+  const float eo = wave_sum(g0 * ao.x + g1 * ao.y);
+  const float ee = wave_sum(g0 * ae.x + g1 * ae.y);
+  if (lane == 0) {
+    const float un = fast_exp2(-sg);
+    w.ee[row] = ee * un;
+    w.eo[row] = eo * un;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// v2b_qconv: Q_e | Q_o rows to fp16, 8 channels per thread, into [B, P, S, 2 D].
+__global__ __launch_bounds__(NT) void v2b_qconv_kernel(V2BwdParams p, Ws2 w) {
+  const int P = p.Hq / 2;
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8 channels
+  const int64_t n = (int64_t)p.B * P * p.S * (2 * D / 8);
+  if (i >= n) return;
+  const int64_t row = i / (2 * D / 8);
+  const int ch = (int)(i % (2 * D / 8)) * 8;
+  const int s = row % p.S, bp = row / p.S, b = bp / P, pr = bp % P;
+  const int t = 2 * pr + (ch >= D);
+  const bf16 *q = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + t * p.qs_h + (ch & (D - 1));
+  const u32x4 raw = *(const u32x4 *)q;
+  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
+                   bf16x2_to_f16x2(raw[3])};
+  *(u32x4 *)(w.qh + i * 8) = h;
+}
+
+// Permutation of rows 0..31 used for the A operand of score-like products so
+// that a lane's 16 result registers are rows 8 h + 0..7 and 16 + 8 h + 0..7.
+__device__ __forceinline__ int row_perm(int i) { return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1); }
+__device__ __forceinline__ int row_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
+
+__device__ __forceinline__ f16x8 to_f16x8(const u32x4 &raw) {
+  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
+                   bf16x2_to_f16x2(raw[3])};
+  return __builtin_bit_cast(f16x8, h);
+}
+
+__device__ __forceinline__ f16x8 pack8h(const float *v) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 x = {v[i], v[i + 1]};
+    const f16x2 y = __builtin_convertvector(x, f16x2);
+    r[i] = y[0];
+    r[i + 1] = y[1];
+  }
+  return r;
+}
+
+// A operand (rows = the 32 matrix columns c0..c0+31 of a row-major fp16 tile,
+// k = 16 consecutive tile rows starting at r0) through transpose reads:
+// lane l receives column c0 + l % 32 of rows r0 + 8 (l / 32) + 0..7.
+__device__ __forceinline__ f16x8 tr_operand(const f16 *tile, int stride, int r0, int c0, int lane) {
+  const int h = lane >> 5, j = lane & 15, half16 = (lane >> 4) & 1;
+  const f16 *ptr = tile + (r0 + 8 * h + (j >> 2)) * stride + c0 + 16 * half16 + 4 * (j & 3);
+  const f16x4 lo = lds_read_tr16(ptr);
+  const f16x4 hi = lds_read_tr16(ptr + 4 * stride);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------------------
+// v2b_dq: query-outer.  Workgroup = 128 queries of one (b, pair); wave w owns
+// queries q0 + 32 w + 0..31 (lane l % 32).
+constexpr int QB = 128, KT = 64;
+
+struct SmemQ {
+  f16 k[KT * QST];
+  f16 v[KT * GST];
+};
+
+__device__ __forceinline__ void stage_kv(SmemQ &sm, const bf16 *kg, const bf16 *vg, int64_t kvs, int kbase, int S,
+                                         int tid) {
+  for (int i = tid; i < KT * (D / 8); i += NT) {
+    const int r = i >> 4, col = (i & 15) * 8, key = kbase + r;
+    u32x4 a = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
+    if (key < S) {
+      a = *(const u32x4 *)(kg + (int64_t)key * kvs + col);
+      bb = *(const u32x4 *)(vg + (int64_t)key * kvs + col);
+    }
+    *(f16x8 *)(sm.k + r * QST + col) = to_f16x8(a);
+    *(f16x8 *)(sm.v + r * GST + col) = to_f16x8(bb);
+  }
+}
+
+__global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
+  __shared__ SmemQ sm;
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
+  const int BP = p.B * P;
+  const int n_qt = (p.S + QB - 1) / QB;
+  const int bp = blockIdx.x % BP;
+  const int qt = p.causal ? n_qt - 1 - blockIdx.x / BP : blockIdx.x / BP;
+  const int b = bp / P, pr = bp % P, j = pr / ppk, bj = b * p.Hkv + j;
+  const int S = p.S;
+  const bool causal = p.causal != 0;
+  const int q0 = qt * QB, qw = q0 + wave * 32, my_q = qw + ln;
+  const float sg = w.scales[bj * 4 + 0], kap = w.scales[bj * 4 + 1];
+  const float c = p.scale * kLog2e;
+  const float fdS = fast_exp2(kap);
+  const int64_t rowb = (int64_t)bp * S;  // row base in [B, P, S]
+  const bool qok = my_q < S;
+
+  // B operands: Q_e, Q_o (S^T = K Q^T) and g' (dP'^T = V g'^T), fp16.
+  f16x8 qe[D / 16], qo[D / 16], gf[D / 16];
+  {
+    const bf16 *qp = (const bf16 *)p.q + b * p.qs_b + (int64_t)my_q * p.qs_s + 2 * pr * p.qs_h + 8 * h;
+    const f16 *gp = w.gh + (rowb + my_q) * D + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qe[kc] = qok ? to_f16x8(*(const u32x4 *)(qp + kc * 16)) : f16x8{};
+      qo[kc] = qok ? to_f16x8(*(const u32x4 *)(qp + p.qs_h + kc * 16)) : f16x8{};
+      gf[kc] = qok ? *(const f16x8 *)(gp + kc * 16) : f16x8{};
+    }
+  }
+  const int64_t lr = ((int64_t)b * p.Hq + 2 * pr) * S + my_q;
+  const float Le = qok ? p.lse[lr] * kLog2e : __builtin_inff();
+  const float Lo = qok ? p.lse[lr + S] * kLog2e : __builtin_inff();
+  const float fE = fast_exp2(sg);
+  const float ee = qok ? w.ee[rowb + my_q] * fE : 0.f;
+  const float eo = qok ? w.eo[rowb + my_q] * fE : 0.f;
+  const float sig = qok ? sigmoid_of(p, b, my_q, pr) : 0.f;
+
+  const int kend = causal ? min(S, q0 + QB) : S;
+  const int n_kt = (kend + KT - 1) / KT;
+  const int krow = row_perm(ln);
+  const int q_last = qw + 31;
+  const bf16 *kg = (const bf16 *)p.k + b * p.kvs_b + j * p.kvs_h;
+  const bf16 *vg = (const bf16 *)p.v + b * p.kvs_b + j * p.kvs_h;
+
+  f32x16 dqe[D / 32], dqo[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dqe[dt] = dqo[dt] = f32x16{};
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    stage_kv(sm, kg, vg, p.kvs_s, kt * KT, S, tid);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kt * KT + sub * 32;
+      if (sb >= S || (causal && sb > q_last)) continue;
+      f32x16 s_e = {}, s_o = {}, dp = {};
+      const f16 *ka = sm.k + (sub * 32 + krow) * QST + 8 * h;
+      const f16 *va = sm.v + (sub * 32 + krow) * GST + 8 * h;
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const f16x8 a = *(const f16x8 *)(ka + kc * 16);
+        s_e = mfma32(a, qe[kc], s_e);
+        s_o = mfma32(a, qo[kc], s_o);
+        dp = mfma32(*(const f16x8 *)(va + kc * 16), gf[kc], dp);
+      }
+      const bool need_mask = (causal && sb + 31 > qw) || sb + 32 > S;
+      float dse[16], dso[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pe = fast_exp2(fmaf(s_e[r], c, -Le));
+        float po = fast_exp2(fmaf(s_o[r], c, -Lo));
+        if (need_mask) {
+          const int key = sb + row_of_reg(r, h);
+          if (key >= S || (causal && key > my_q)) pe = po = 0.f;
+        }
+        dse[r] = pe * (dp[r] - ee) * fdS;
+        dso[r] = -sig * po * (dp[r] - eo) * fdS;
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const f16x8 be = pack8h(dse + 8 * kc2), bo = pack8h(dso + 8 * kc2);
+        const int r0 = sub * 32 + kc2 * 16;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const f16x8 a = tr_operand(sm.k, QST, r0, dt * 32, lane);
+          dqe[dt] = mfma32(a, be, dqe[dt]);
+          dqo[dt] = mfma32(a, bo, dqo[dt]);
+        }
+      }
+    }
+  }
+  if (qok) {
+    const float fq = p.scale * fast_exp2(-(kap + sg));
+    bf16 *de = (bf16 *)p.dq + b * p.dqs_b + (int64_t)my_q * p.dqs_s + 2 * pr * p.dqs_h;
+    bf16 *dO = de + p.dqs_h;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = dt * 32 + 8 * g + 4 * h;
+        *(bf16x4 *)(de + ch) = bf16x4{f2bf(dqe[dt][4 * g] * fq), f2bf(dqe[dt][4 * g + 1] * fq),
+                                      f2bf(dqe[dt][4 * g + 2] * fq), f2bf(dqe[dt][4 * g + 3] * fq)};
+        *(bf16x4 *)(dO + ch) = bf16x4{f2bf(dqo[dt][4 * g] * fq), f2bf(dqo[dt][4 * g + 1] * fq),
+                                      f2bf(dqo[dt][4 * g + 2] * fq), f2bf(dqo[dt][4 * g + 3] * fq)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// v2b_dkdv: key-outer.  Workgroup = 128 keys of one (b, KV head); wave w owns
+// keys kb + 32 w + 0..31 (lane l % 32).  Streams 64-query chunks of every
+// pair on the head through LDS.
+constexpr int KVB = 128, QCH = 64;
+
+struct SmemC {
+  f16 qe[QCH * QST];
+  f16 qo[QCH * QST];
+  f16 g[QCH * GST];
+  float le[QCH], lo[QCH], ee[QCH], eo[QCH], sig[QCH];
+};
+
+// One thread's share of a staged query chunk: eight 16-byte chunks of the
+// fp16 Q_e | Q_o rows, four of g', and (threads 0..63) one row's statistics.
+struct ChunkRegs2 {
+  u32x4 q[8], g[4];
+  float le, lo, ee, eo, sig;
+};
+
+__device__ __forceinline__ void load_chunk2(const V2BwdParams &p, const Ws2 &w, int b, int pr, int64_t rowb,
+                                            int q0, int tid, float fE, ChunkRegs2 &r) {
+  const int S = p.S;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = tid + NT * k, row = i >> 5, col = (i & 31) * 8, q = q0 + row;
+    r.q[k] = q < S ? *(const u32x4 *)(w.qh + (rowb + q) * (2 * D) + col) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
+    r.g[k] = q < S ? *(const u32x4 *)(w.gh + (rowb + q) * D + col) : u32x4{0, 0, 0, 0};
+  }
+  if (tid < QCH) {
+    const int q = q0 + tid;
+    const bool ok = q < S;
+    const int64_t lr = ((int64_t)b * p.Hq + 2 * pr) * S + q;
+    r.le = ok ? p.lse[lr] * kLog2e : __builtin_inff();
+    r.lo = ok ? p.lse[lr + S] * kLog2e : __builtin_inff();
+    r.ee = ok ? w.ee[rowb + q] * fE : 0.f;
+    r.eo = ok ? w.eo[rowb + q] * fE : 0.f;
+    r.sig = ok ? sigmoid_of(p, b, q, pr) : 0.f;
+  }
+}
+
+__device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int tid) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = tid + NT * k, row = i >> 5, col = (i & 31) * 8;
+    f16 *dq = col < D ? sm.qe + row * QST + col : sm.qo + row * QST + (col - D);
+    *(u32x4 *)dq = r.q[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8;
+    *(u32x4 *)(sm.g + row * GST + col) = r.g[k];
+  }
+  if (tid < QCH) {
+    sm.le[tid] = r.le;
+    sm.lo[tid] = r.lo;
+    sm.ee[tid] = r.ee;
+    sm.eo[tid] = r.eo;
+    sm.sig[tid] = r.sig;
+  }
+}
+
+__global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
+  __shared__ SmemC smb[2];
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
+  // Workgroup id -> (key block, batch, KV head): key blocks with the most
+  // causal work first across all heads; consecutive ids walk (batch, head).
+  const int BJ = p.B * p.Hkv;
+  const int bj = blockIdx.x % BJ, b = bj / p.Hkv, j = bj % p.Hkv;
+  const int S = p.S;
+  const bool causal = p.causal != 0;
+  const int kb = (blockIdx.x / BJ) * KVB, kw = kb + wave * 32, my_key = kw + ln;
+  const float sg = w.scales[bj * 4 + 0], kap = w.scales[bj * 4 + 1], om = w.scales[bj * 4 + 2];
+  const float c = p.scale * kLog2e;
+  const float fdS = fast_exp2(kap), fW = fast_exp2(om), fE = fast_exp2(sg);
+
+  // K (B operand of S = Q K^T) and V (B operand of dP' = g' V^T) for my key, fp16.
+  f16x8 kf[D / 16], vf[D / 16];
+  {
+    const bool ok = my_key < S;
+    const bf16 *kp = (const bf16 *)p.k + b * p.kvs_b + (int64_t)my_key * p.kvs_s + j * p.kvs_h + 8 * h;
+    const bf16 *vp = (const bf16 *)p.v + b * p.kvs_b + (int64_t)my_key * p.kvs_s + j * p.kvs_h + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      kf[kc] = ok ? to_f16x8(*(const u32x4 *)(kp + kc * 16)) : f16x8{};
+      vf[kc] = ok ? to_f16x8(*(const u32x4 *)(vp + kc * 16)) : f16x8{};
+    }
+  }
+
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dv[i] = dk[i] = f32x16{};
+
+  const int q_begin = causal ? (kb / QCH) * QCH : 0;
+  const int n_ch = q_begin < S ? (S - q_begin + QCH - 1) / QCH : 0;
+  const int n_it = n_ch * ppk;  // (pair, chunk) steps, pair-major
+  const int prow = row_perm(ln);
+  // Query chunks double-buffered in LDS: step n + 1 is loaded into registers
+  // while step n is computed, then stored to the other buffer; one barrier
+  // per step.
+  ChunkRegs2 nxt;
+  if (n_it > 0) {
+    const int pr = j * ppk;
+    load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin, tid, fE, nxt);
+    store_chunk2(smb[0], nxt, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    SmemC &sm = smb[it & 1];
+    const int q0 = q_begin + (it % n_ch) * QCH;
+    const bool more = it + 1 < n_it;
+    if (more) {
+      const int pr = j * ppk + (it + 1) / n_ch;
+      load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin + ((it + 1) % n_ch) * QCH, tid, fE, nxt);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qs = q0 + sub * 32;
+      if (qs >= S) continue;
+      if (causal && qs + 31 < kw) continue;  // every query of this sub-chunk precedes my keys
+      // S_e, S_o = Q K^T and dP' = g' V^T; lane = key, registers = queries.
+      f32x16 s_e = {}, s_o = {}, dp = {};
+      const f16 *qa = sm.qe + (sub * 32 + prow) * QST + 8 * h;
+      const f16 *qb = sm.qo + (sub * 32 + prow) * QST + 8 * h;
+      const f16 *ga = sm.g + (sub * 32 + prow) * GST + 8 * h;
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        s_e = mfma32(*(const f16x8 *)(qa + kc * 16), kf[kc], s_e);
+        s_o = mfma32(*(const f16x8 *)(qb + kc * 16), kf[kc], s_o);
+        dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
+      }
+      const bool need_mask = (causal && qs < kw + 31) || kw + 32 > S || qs + 32 > S;
+      float wv[16], dse[16], dso[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = sub * 32 + row_of_reg(r, h);
+        float pe = fast_exp2(fmaf(s_e[r], c, -sm.le[qi]));
+        float po = fast_exp2(fmaf(s_o[r], c, -sm.lo[qi]));
+        if (need_mask) {
+          const int q = q0 + qi;
+          if (my_key >= S || q >= S || (causal && my_key > q)) pe = po = 0.f;
+        }
+        const float sq = sm.sig[qi];
+        wv[r] = (pe - sq * po) * fW;
+        dse[r] = pe * (dp[r] - sm.ee[qi]) * fdS;
+        dso[r] = -sq * po * (dp[r] - sm.eo[qi]) * fdS;
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const f16x8 wb = pack8h(wv + 8 * kc2), be = pack8h(dse + 8 * kc2), bo = pack8h(dso + 8 * kc2);
+        const int r0 = sub * 32 + kc2 * 16;
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct) {
+          dv[ct] = mfma32(tr_operand(sm.g, GST, r0, ct * 32, lane), wb, dv[ct]);
+          dk[ct] = mfma32(tr_operand(sm.qe, QST, r0, ct * 32, lane), be, dk[ct]);
+          dk[ct] = mfma32(tr_operand(sm.qo, QST, r0, ct * 32, lane), bo, dk[ct]);
+        }
+      }
+    }
+    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid);
+    __syncthreads();
+  }
+
+  // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
+  if (my_key < S) {
+    const float fv = fast_exp2(-(om + sg));
+    const float fk = p.scale * fast_exp2(-(kap + sg));
+    bf16 *dvp = (bf16 *)p.dv + b * p.dkvs_b + (int64_t)my_key * p.dkvs_s + j * p.dkvs_h;
+    bf16 *dkp = (bf16 *)p.dk + b * p.dkvs_b + (int64_t)my_key * p.dkvs_s + j * p.dkvs_h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct) {
+        const int ch = ct * 32 + 8 * g + 4 * h;
+        *(bf16x4 *)(dvp + ch) = bf16x4{f2bf(dv[ct][4 * g] * fv), f2bf(dv[ct][4 * g + 1] * fv),
+                                       f2bf(dv[ct][4 * g + 2] * fv), f2bf(dv[ct][4 * g + 3] * fv)};
+        *(bf16x4 *)(dkp + ch) = bf16x4{f2bf(dk[ct][4 * g] * fk), f2bf(dk[ct][4 * g + 1] * fk),
+                                       f2bf(dk[ct][4 * g + 2] * fk), f2bf(dk[ct][4 * g + 3] * fk)};
+      }
+  }
+}
+
+}  // namespace
+
+size_t v2_bwd_workspace_bytes(int B, int S, int Hq, int Hkv) { return ws2_bytes(B, S, Hq / 2, Hkv); }
+
+hipError_t launch_v2_bwd(const V2BwdParams &p, hipStream_t st) {
+  const int P = p.Hq / 2;
+  Ws2 w = carve2(p.workspace, p.B, p.S, P, p.Hkv);
+  const int64_t rows = (int64_t)p.B * P * p.S;
+  hipLaunchKernelGGL(v2b_pre_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_scales_kernel, dim3(p.B * p.Hkv), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_gconv_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
+  const int n_qt = (p.S + QB - 1) / QB;
+  hipLaunchKernelGGL(v2b_dq_kernel, dim3(n_qt * p.B * P), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_dkdv_kernel, dim3((p.S + KVB - 1) / KVB * p.B * p.Hkv), dim3(NT), 0, st, p, w);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -118,10 +118,11 @@ __device__ __forceinline__ void pass1_tile(const SmemV2 &sm, int kbase, int krow
   }
 }
 
-template <bool MASKED>
+template <bool MASKED, bool SAVE>
 __device__ __forceinline__ void pass2_tile(const SmemV2 &sm, int kbase, int krow, int lane, const bf16x8 *qe,
-                                           const bf16x8 *qo, float c, float sig, float Les, float Los, f32x16 *o,
-                                           int S, bool causal, int qw, int my_q) {
+                                           const bf16x8 *qo, float c, float sig, float Les, float Los, float fe,
+                                           float fo, f32x16 *o, f32x16 *ae, f32x16 *ao, int S, bool causal, int qw,
+                                           int my_q) {
   const int h = lane >> 5;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
@@ -130,15 +131,32 @@ __device__ __forceinline__ void pass2_tile(const SmemV2 &sm, int kbase, int krow
     f32x16 se, so;
     scores2(sm, sub, krow, h, qe, qo, se, so);
     if (MASKED && ((causal && sb + 31 > qw) || sb + 32 > S)) mask_scores(se, so, sb, h, S, causal, my_q);
-    float w[16];
+    float w[16], we[16], wo[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) w[r] = fast_exp2(fmaf(se[r], c, -Les)) - sig * fast_exp2(fmaf(so[r], c, -Los));
+    for (int r = 0; r < 16; ++r) {
+      const float xe = fast_exp2(fmaf(se[r], c, -Les)), xo = fast_exp2(fmaf(so[r], c, -Los));
+      w[r] = xe - sig * xo;
+      if (SAVE) {
+        we[r] = xe * fe;
+        wo[r] = xo * fo;
+      }
+    }
     const f16x8 wb[2] = {pack8(w), pack8(w + 8)};
     pv_step_tile<VST, D / 32>(sm.v, sub, lane, wb, o);
+    if (SAVE) {
+      const f16x8 web[2] = {pack8(we), pack8(we + 8)}, wob[2] = {pack8(wo), pack8(wo + 8)};
+      pv_step_tile<VST, D / 32>(sm.v, sub, lane, web, ae);
+      pv_step_tile<VST, D / 32>(sm.v, sub, lane, wob, ao);
+    }
   }
 }
 
-__global__ __launch_bounds__(NT, 2) void fwd_v2_kernel(V2FwdParams p) {
+// Training mode (SAVE) also accumulates each head's own output A_even, A_odd
+// with its own fp16 weights and writes, per row, both heads' natural-log
+// partition functions and both outputs in float32: the backward needs
+// g . A_t of each head consistent with that head's probabilities.
+template <bool SAVE>
+__global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p) {
   __shared__ SmemV2 sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
@@ -202,28 +220,36 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_kernel(V2FwdParams p) {
   lse_finish(mo, lo, Mo, Lo);
   const float sg = row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo));
   const float Les = Le - sg, Los = Lo - sg;
+  // Each head's own weights just under 2^15 for A_even and A_odd.
+  const float sge = SAVE ? row_scale_log2(fast_exp2(Me - Le)) : 0.f;
+  const float sgo = SAVE ? row_scale_log2(fast_exp2(Mo - Lo)) : 0.f;
+  const float fe = fast_exp2(sge - sg), fo = fast_exp2(sgo - sg);
 
   // ---------------- pass 2: O = (P_e - sigmoid(lambda) P_o) V ----------------
-  f32x16 o[D / 32];
+  f32x16 o[D / 32], ae[SAVE ? D / 32 : 1], ao[SAVE ? D / 32 : 1];
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) o[ct] = f32x16{};
+#pragma unroll
+  for (int ct = 0; ct < (SAVE ? D / 32 : 1); ++ct) ae[ct] = ao[ct] = f32x16{};
   ld.load(0, true, nxt);
   store_tile(sm[0], nxt, tid, true);
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
-    pass2_tile<false>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, o, S, causal, qw, my_q);
+    pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
+                            my_q);
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
-    pass2_tile<true>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, o, S, causal, qw, my_q);
+    pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
+                           my_q);
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
 
-  // ---------------- epilogue: unscale, store bf16 ----------------
+  // ---------------- epilogue: unscale, store bf16 (and the training saves) ----------------
   if (qok) {
     const float f = fast_exp2(-sg);
     bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + pr * p.os_h;
@@ -236,6 +262,25 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_kernel(V2FwdParams p) {
                           f2bf(o[ct][4 * g + 3] * f)};
         *(bf16x4 *)(out + ch) = y;
       }
+    if (SAVE) {
+      if (h == 0) {
+        const int64_t lr = ((int64_t)b * p.Hq + te) * S + my_q;
+        p.lse[lr] = Le * kLn2;
+        p.lse[lr + S] = Lo * kLn2;
+      }
+      const float fa = fast_exp2(-sge), fb = fast_exp2(-sgo);
+      const int64_t srow = (((int64_t)b * S + my_q) * npair + pr) * D;
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = ct * 32 + 8 * g + 4 * h;
+          *(f32x4 *)(p.a_even + srow + ch) = f32x4{ae[ct][4 * g] * fa, ae[ct][4 * g + 1] * fa,
+                                                   ae[ct][4 * g + 2] * fa, ae[ct][4 * g + 3] * fa};
+          *(f32x4 *)(p.a_odd + srow + ch) = f32x4{ao[ct][4 * g] * fb, ao[ct][4 * g + 1] * fb,
+                                                  ao[ct][4 * g + 2] * fb, ao[ct][4 * g + 3] * fb};
+        }
+    }
   }
 }
 
@@ -243,7 +288,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_kernel(V2FwdParams p) {
 
 hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st) {
   const int n_qt = (p.S + BM - 1) / BM;
-  hipLaunchKernelGGL(fwd_v2_kernel, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);
+  if (p.lse)
+    hipLaunchKernelGGL(fwd_v2_kernel<true>, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL(fwd_v2_kernel<false>, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 

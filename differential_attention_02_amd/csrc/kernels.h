@@ -64,6 +64,24 @@ struct V2FwdParams {
   int B, S, Hq, Hkv;
   int causal;
   float scale;
+  float *lse;            // training saves (all or none): [B, Hq, S] natural-log partition functions,
+  float *a_even, *a_odd; // [B, S, Hq/2, D] each head's own output (attn_2p, attn_2p+1)
+};
+
+// DIFF V2 prefill backward (bf16, D = 128).
+struct V2BwdParams {
+  const void *q, *k, *v, *dout;
+  int64_t qs_b, qs_s, qs_h, kvs_b, kvs_s, kvs_h, ds_b, ds_s, ds_h;
+  const float *lam;
+  int64_t ls_b, ls_s, ls_p;
+  const float *lse, *a_even, *a_odd;
+  void *dq, *dk, *dv;
+  int64_t dqs_b, dqs_s, dqs_h, dkvs_b, dkvs_s, dkvs_h;
+  float *dlam;  // [B, S, Hq/2]
+  int B, S, Hq, Hkv;
+  int causal;
+  float scale;
+  void *workspace;
 };
 
 // Reference vector-ALU forward: any supported (d, dv), f32 or bf16.
@@ -72,6 +90,8 @@ hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipS
 hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st);
 
 hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st);
+size_t v2_bwd_workspace_bytes(int B, int S, int Hq, int Hkv);
+hipError_t launch_v2_bwd(const V2BwdParams &p, hipStream_t st);
 
 size_t bwd_workspace_bytes(int B, int S, int H, int d, int dv);
 hipError_t launch_bwd(const BwdParams &p, hipStream_t st);

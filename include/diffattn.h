@@ -25,6 +25,7 @@
  *   - DIFF V2 prefill forward: the same operator over whole sequences (causal
  *     or not), with a sigmoid input per token and pair [same sections; item 5
  *     makes lambda per token and per head].
+ *   - DIFF V2 prefill backward: its gradients by the chain rule.
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a device pointer owned by the caller (for example
@@ -182,6 +183,11 @@ typedef struct diffattn_v2_decode_args {
  *   where attn_t = softmax(s q_t K^T) V over keys j <= i (causal) or all keys,
  *   in fp32 arithmetic with fp16/bf16 matrix-core operands, rounded to bf16.
  *   softmax_scale <= 0 selects s = 1/sqrt(D).
+ *   Training saves (all three non-NULL, or all NULL), float32, contiguous:
+ *     lse [B, Hq, S]: natural-log partition function of each query head's
+ *       scaled scores;
+ *     a_even, a_odd [B, S, Hq/2, D]: each head's own output attn_2p and
+ *       attn_2p+1.
  *   batch = 0 or seqlen = 0 is an empty problem: DIFFATTN_OK, nothing read.
  */
 typedef struct diffattn_v2_fwd_args {
@@ -195,7 +201,44 @@ typedef struct diffattn_v2_fwd_args {
   float softmax_scale;
   void *out;
   int64_t o_stride[3];
+  float *lse;   /* training saves, all three or none (see above) */
+  float *a_even;
+  float *a_odd;
 } diffattn_v2_fwd_args;
+
+/*
+ * DIFF V2 prefill backward arguments: gradients of L = <dout, out> for a
+ * diffattn_v2_fwd call with the same inputs and flags that wrote the three
+ * training saves (bf16, D = 128).
+ *   dout [B, S, Hq/2, D] (strides do_stride).  Outputs: dq [B, S, Hq, D]
+ *   (strides dq_stride); dk, dv [B, S, Hkv, D] sharing dkv_stride (summed over
+ *   every query head that reads the KV head), all bf16; dlam: device float32
+ *   [B, S, Hq/2] contiguous, the gradient for a separate lam value per
+ *   (batch, token, pair) (for a broadcast lam, sum it over the broadcast axes).
+ *   Every output is fully written; nothing is accumulated into.
+ *   workspace: at least diffattn_v2_bwd_workspace_size() bytes, 256-byte
+ *   aligned; its contents on entry do not matter.
+ */
+typedef struct diffattn_v2_bwd_args {
+  int32_t batch, seqlen, q_heads, kv_heads, head_dim;
+  int32_t dtype, causal;
+  const void *q, *k, *v;
+  int64_t q_stride[3];
+  int64_t kv_stride[3];
+  const float *lam;
+  int64_t lam_stride[3];
+  float softmax_scale;
+  const void *dout;
+  int64_t do_stride[3];
+  const float *lse, *a_even, *a_odd;
+  void *dq;
+  int64_t dq_stride[3];
+  void *dk, *dv;
+  int64_t dkv_stride[3];
+  float *dlam;
+  void *workspace;
+  size_t workspace_bytes;
+} diffattn_v2_bwd_args;
 
 /* Forward pass. Returns DIFFATTN_OK or a negative status. */
 int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
@@ -214,6 +257,12 @@ size_t diffattn_v2_decode_workspace_size(const diffattn_v2_decode_args *args);
 
 /* DIFF V2 prefill forward. Returns DIFFATTN_OK or a negative status. */
 int diffattn_v2_fwd(const diffattn_v2_fwd_args *args, void *stream);
+
+/* DIFF V2 prefill backward. Returns DIFFATTN_OK or a negative status. */
+int diffattn_v2_bwd(const diffattn_v2_bwd_args *args, void *stream);
+
+/* Workspace bytes diffattn_v2_bwd needs for these arguments (0 if invalid). */
+size_t diffattn_v2_bwd_workspace_size(const diffattn_v2_bwd_args *args);
 
 /* lambda_init for layer index l >= 1: 0.8 - 0.6 exp(-0.3 (l - 1)); NaN for l < 1. */
 float diffattn_lambda_init(int layer);

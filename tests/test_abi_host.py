@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -199,6 +199,62 @@ def test_v2_fwd_rejects(field, value, code):
     assert B.lib().diffattn_last_error() != b""
 
 
+@host_only
+def test_v2_fwd_saves_all_or_none():
+    a = _v2_args(lse=FAKE)
+    assert B.lib().diffattn_v2_fwd(ctypes.byref(a), None) == -1
+
+
+def _v2b_args(**kw):
+    a = B.V2BwdArgs()
+    f = _v2_args()
+    for name, _ in B.V2BwdArgs._fields_:
+        if hasattr(f, name):
+            setattr(a, name, getattr(f, name))
+    a.dout = a.dq = a.dk = a.dv = a.dlam = FAKE
+    a.lse = a.a_even = a.a_odd = FAKE
+    a.do_stride = (ctypes.c_int64 * 3)(256 * 2 * 128, 2 * 128, 128)
+    a.dq_stride = (ctypes.c_int64 * 3)(256 * 4 * 128, 4 * 128, 128)
+    a.dkv_stride = (ctypes.c_int64 * 3)(256 * 2 * 128, 2 * 128, 128)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_v2_bwd_workspace_and_empty_call():
+    lib = B.lib()
+    a = _v2b_args()
+    n = lib.diffattn_v2_bwd_workspace_size(ctypes.byref(a))
+    assert n >= 1 * 2 * 256 * 128 * 2 * 3   # fp16 g' and Q_e | Q_o rows
+    a.batch = 0
+    assert lib.diffattn_v2_bwd(ctypes.byref(a), None) == 0
+    assert lib.diffattn_v2_bwd_workspace_size(ctypes.byref(a)) == 0
+
+
+@host_only
+@pytest.mark.parametrize("field,value,code", [
+    ("lse", None, -1), ("a_odd", None, -1), ("dlam", None, -1), ("dout", None, -1), ("dk", None, -1),
+    ("q_heads", 6, -1), ("head_dim", 64, -2), ("dq", FAKE + 8, -2),
+    ("do_stride", (ctypes.c_int64 * 3)(1, 0, 128), -1),
+])
+def test_v2_bwd_rejects(field, value, code):
+    a = _v2b_args(**{field: value})
+    a.workspace, a.workspace_bytes = FAKE, 1 << 40
+    assert B.lib().diffattn_v2_bwd(ctypes.byref(a), None) == code
+    assert B.lib().diffattn_last_error() != b""
+
+
+@host_only
+def test_v2_bwd_rejects_small_workspace():
+    lib = B.lib()
+    a = _v2b_args()
+    n = lib.diffattn_v2_bwd_workspace_size(ctypes.byref(a))
+    a.workspace, a.workspace_bytes = FAKE, n - 1
+    assert lib.diffattn_v2_bwd(ctypes.byref(a), None) == -3
+    a.workspace, a.workspace_bytes = FAKE + 16, n
+    assert lib.diffattn_v2_bwd(ctypes.byref(a), None) == -1
+
+
 def test_bwd_rejects_without_saves():
     a = B.BwdArgs()
     a.batch, a.seqlen, a.heads, a.head_dim, a.v_dim = 1, 128, 2, 64, 128
@@ -225,7 +281,8 @@ def test_ctypes_layout_matches_c_compiler(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     checks = {"diffattn_fwd_args": B.FwdArgs, "diffattn_bwd_args": B.BwdArgs,
-              "diffattn_v2_decode_args": B.DecodeArgs, "diffattn_v2_fwd_args": B.V2FwdArgs}
+              "diffattn_v2_decode_args": B.DecodeArgs, "diffattn_v2_fwd_args": B.V2FwdArgs,
+              "diffattn_v2_bwd_args": B.V2BwdArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "diffattn.h"', "int main(void) {"]
     for cname, ct in checks.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')

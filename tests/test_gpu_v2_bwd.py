@@ -1,0 +1,157 @@
+"""GPU parity of the DIFF V2 prefill training path (diffattn_v2_fwd with
+training saves, then diffattn_v2_bwd, through the C ABI) against the float64
+oracle: the saves themselves, gradients on ragged causal and full-attention
+cases, groups of two and four query heads per KV head, peaked maps, broadcast
+lambda, and (batch, pair) slices of the full 4 x 4096-token workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differential_attention_02_amd import binding as B
+from differential_attention_02_amd import workloads
+from tests.parity import as_f64, assert_bf16_grad, assert_bf16_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _inputs(seed, **kw):
+    return workloads.make_v2_prefill_inputs("v2_prefill_4k", seed=seed, **kw)
+
+
+def _dout(inp, seed):
+    g = torch.Generator().manual_seed(seed)
+    B, S, Hq, D = inp["q"].shape
+    return torch.randn((B, S, Hq // 2, D), generator=g).to(torch.bfloat16)
+
+
+def _run(inp, dout, causal=True, lam=None):
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    lam = (inp["lam"] if lam is None else lam).cuda()
+    out, saves = B.v2_fwd(q, k, v, lam, causal=causal, save=True)
+    g = B.v2_bwd(q, k, v, lam, dout.cuda(), saves, causal=causal)
+    torch.cuda.synchronize()
+    return out, saves, g
+
+
+def _ref(inp, dout, causal=True, lam=None):
+    lam = inp["lam"] if lam is None else lam
+    return oracle.v2_prefill_bwd(as_f64(inp["q"]), as_f64(inp["k"]), as_f64(inp["v"]), as_f64(lam),
+                                 as_f64(dout), causal=causal)
+
+
+def _check_grads(g, ref, what, lam_shape=None):
+    for n in ("dq", "dk", "dv"):
+        if not np.any(ref[n]):   # e.g. a one-token sequence: softmax over one key has no gradient
+            err = float(np.abs(as_f64(g[n])).max())
+            print(f"[parity] {what} {n}: reference is zero, max-abs {err:.3e}", flush=True)
+            assert err <= 1e-6, (what, n)
+            continue
+        assert_bf16_grad(g[n], ref[n], f"{what} {n}")
+    dl = ref["dlam"]
+    if lam_shape is not None and len(lam_shape) < 3:
+        dl = dl.sum(axis=tuple(range(3 - len(lam_shape))))
+    got = as_f64(g["dlam"])
+    err = np.abs(got - dl).max() / max(np.abs(dl).max(), 1e-30)
+    print(f"[parity] {what} dlam: max-abs / max|ref| {err:.3e}", flush=True)
+    assert err <= 1e-2, (what, err)
+
+
+def test_saves_match_oracle():
+    """lse: each query head's natural-log partition function; a_even, a_odd:
+    each head's own attention output."""
+    _note("v2 saves")
+    inp = _inputs(20, batch=2, seqlen=200, q_heads=8, kv_heads=4)
+    out, saves, _ = _run(inp, _dout(inp, 1))
+    q, k, v, lam = (as_f64(inp[n]) for n in ("q", "k", "v", "lam"))
+    ref = oracle.v2_prefill_fwd(q, k, v, lam)
+    assert_bf16_rows(out, ref, "v2 save-mode out")
+    # each head's own attention: switch the odd term off (sigmoid(-800) = 0),
+    # with the odd heads moved to the even slots for a_odd
+    off = np.full_like(lam, -800.0)
+    assert_bf16_rows(saves["a_even"], oracle.v2_prefill_fwd(q, k, v, off), "v2 a_even")
+    qs = q.copy()
+    qs[:, :, 0::2] = q[:, :, 1::2]
+    assert_bf16_rows(saves["a_odd"], oracle.v2_prefill_fwd(qs, k, v, off), "v2 a_odd")
+    # natural-log partition functions of each head's scaled causal scores
+    Bn, S, Hq, D = q.shape
+    lse = as_f64(saves["lse"])
+    for b in range(Bn):
+        for t in range(Hq):
+            s = q[b, :, t] @ k[b, :, t // 2].T / np.sqrt(D)
+            s = np.where(np.arange(S)[None, :] > np.arange(S)[:, None], -np.inf, s)
+            m = s.max(axis=1)
+            want = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+            np.testing.assert_allclose(lse[b, t], want, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("S", [1, 33, 64, 129, 300])
+def test_grads_causal(S):
+    _note(f"v2 bwd causal S={S}")
+    inp = _inputs(30 + S, batch=2, seqlen=S, q_heads=4, kv_heads=2)
+    d = _dout(inp, S)
+    _, _, g = _run(inp, d)
+    _check_grads(g, _ref(inp, d), f"v2 bwd causal S={S}")
+
+
+@pytest.mark.parametrize("S", [70, 256])
+def test_grads_full_attention(S):
+    _note(f"v2 bwd non-causal S={S}")
+    inp = _inputs(40 + S, batch=1, seqlen=S, q_heads=4, kv_heads=2)
+    d = _dout(inp, S)
+    _, _, g = _run(inp, d, causal=False)
+    _check_grads(g, _ref(inp, d, causal=False), f"v2 bwd non-causal S={S}")
+
+
+def test_grads_group_of_four():
+    """Two pairs share each KV head: dK and dV sum over both pairs."""
+    _note("v2 bwd group 4")
+    inp = _inputs(50, batch=1, seqlen=230, q_heads=8, kv_heads=2)
+    d = _dout(inp, 5)
+    _, _, g = _run(inp, d)
+    _check_grads(g, _ref(inp, d), "v2 bwd group 4")
+
+
+def test_grads_peaked_maps():
+    _note("v2 bwd peaked")
+    inp = _inputs(51, batch=1, seqlen=190, q_heads=4, kv_heads=2, input_scale=1.0)
+    d = _dout(inp, 6)
+    _, _, g = _run(inp, d)
+    _check_grads(g, _ref(inp, d), "v2 bwd peaked")
+
+
+def test_grads_broadcast_lambda():
+    _note("v2 bwd lambda per pair")
+    inp = _inputs(52, batch=2, seqlen=150, q_heads=4, kv_heads=2)
+    lam = torch.tensor([1.5, -0.4])
+    d = _dout(inp, 7)
+    _, _, g = _run(inp, d, lam=lam)
+    _check_grads(g, _ref(inp, d, lam=lam), "v2 bwd lambda per pair", lam_shape=tuple(lam.shape))
+
+
+def test_full_workload_slices():
+    """The 4 x 4096-token, 24-query-head workload: every output of three
+    (batch, pair) slices against the oracle run on that slice alone (at two
+    query heads per KV head a slice's dK and dV depend on its pair only), and
+    the shift invariant (sum of dK over keys = 0) on every KV head."""
+    cfg = workloads.CONFIGS["v2_prefill_4k"]
+    _note(f"v2 bwd full workload {cfg}")
+    inp = _inputs(60)
+    d = _dout(inp, 8)
+    _, _, g = _run(inp, d)
+    for b, pr in ((0, 0), (2, 7), (3, 11)):
+        sl = {"q": inp["q"][b:b + 1, :, 2 * pr:2 * pr + 2], "k": inp["k"][b:b + 1, :, pr:pr + 1],
+              "v": inp["v"][b:b + 1, :, pr:pr + 1], "lam": inp["lam"][b:b + 1, :, pr:pr + 1]}
+        ref = _ref(sl, d[b:b + 1, :, pr:pr + 1])
+        got = {"dq": g["dq"][b:b + 1, :, 2 * pr:2 * pr + 2], "dk": g["dk"][b:b + 1, :, pr:pr + 1],
+               "dv": g["dv"][b:b + 1, :, pr:pr + 1], "dlam": g["dlam"][b:b + 1, :, pr:pr + 1]}
+        _check_grads(got, ref, f"v2 bwd full workload b={b} pair={pr}")
+    dk = as_f64(g["dk"])
+    rms = np.sqrt(np.mean(dk * dk))
+    worst = np.abs(dk.sum(axis=1)).max() / (rms * np.sqrt(cfg.seqlen))
+    print(f"[parity] v2 bwd sum_keys dK / (rms sqrt(S)) = {worst:.3e}", flush=True)
+    assert worst < 0.05
