@@ -12,7 +12,9 @@ Also reported under "extra": the 64K-token forward, the 8K training step
 (GB/s of K/V cache + query + output bytes), and the DIFF V2 prefill forward
 (batch 4, 4096 causal tokens, 24 query heads over 12 KV heads, D 128: 1024
 flop per unmasked (query, key, pair of query heads), two QK^T and two PV
-products of width 128).
+products of width 128), and its training step (forward with saves + backward,
+2048 more flop per unmasked (query, key, pair): recomputed QK^T of both heads,
+one shared dP, one merged dV, dQ and dK of both heads).
 Each timing: W untimed launches, then exactly K launches between two
 synchronisations; HIP events on the launch stream give the average launch
 duration used for the roofline.  "cpu_baseline" times the float64 oracle on a
@@ -40,6 +42,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FLOP_PER_PAIR_FWD = 768
 FLOP_PER_PAIR_BWD = 1280
 FLOP_PER_PAIR_V2 = 8 * 128     # per (query, key, even/odd pair of query heads), D = 128
+# V2 backward per (query, key, pair): recomputed Q K^T of both heads 512, shared dP 256, merged dV 256,
+# dQ of both heads 512, dK of both heads 512.
+FLOP_PER_PAIR_V2_BWD = 16 * 128
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -207,6 +212,43 @@ def _gpu_v2_prefill(steps, warmup):
             "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
+def _gpu_v2_train(steps, warmup):
+    """One DIFF V2 training step at the 4K V2 workload: forward with the
+    training saves, then the backward, on random upstream gradients."""
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["v2_prefill_4k"]
+    inp = workloads.make_v2_prefill_inputs(cfg)
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    Bn, S, Hq, D = q.shape
+    gen = torch.Generator().manual_seed(1)
+    dout = torch.randn((Bn, S, Hq // 2, D), generator=gen).to(torch.bfloat16).cuda()
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = torch.empty((Bn, S, Hq // 2, D), dtype=q.dtype, device="cuda")
+    saves = {"lse": torch.empty((Bn, Hq, S), **f32), "a_even": torch.empty((Bn, S, Hq // 2, D), **f32),
+             "a_odd": torch.empty((Bn, S, Hq // 2, D), **f32)}
+    fa = B.v2_fwd_args(q, k, v, lam, out, causal=cfg.causal, saves=saves)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dlam = torch.empty((Bn, S, Hq // 2), **f32)
+    ba = B.v2_bwd_args(q, k, v, lam, dout, saves, dq, dk, dv, dlam, causal=cfg.causal)
+    nbytes = B.v2_bwd_workspace_size(ba)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ba.workspace, ba.workspace_bytes = ws.data_ptr(), nbytes
+
+    def step():
+        B.v2_fwd_launch(fa)
+        B.v2_bwd_launch(ba)
+
+    each = []
+    wall, per = _time_launches(step, steps, warmup, each)
+    pairs = Bn * (Hq // 2) * cfg.pairs
+    flops = pairs * (FLOP_PER_PAIR_V2 + FLOP_PER_PAIR_V2_BWD)
+    return {"ms_per_step": wall / steps * 1e3, "tflops": flops * steps / wall / 1e12,
+            "event_tflops": flops / per / 1e12, "flop_per_step": flops,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -283,7 +325,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k"],
+    ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k",
+                                       "v2_train_4k"],
                     default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -315,6 +358,8 @@ def main(argv=None) -> int:
             print(json.dumps({"workload": args.only, "tflops": r["tflops"], "event_tflops": r["event_tflops"]}))
         elif args.only == "train_8k":
             print(json.dumps({"workload": "train_8k", **_gpu_train(args.steps, args.warmup)}))
+        elif args.only == "v2_train_4k":
+            print(json.dumps({"workload": "v2_train_4k", **_gpu_v2_train(args.steps, args.warmup)}))
         elif args.only == "v2_prefill_4k":
             r = _gpu_v2_prefill(args.steps, args.warmup)
             print(json.dumps({"workload": "v2_prefill_4k", "tflops": r["tflops"], "event_tflops": r["event_tflops"],
@@ -357,6 +402,11 @@ def main(argv=None) -> int:
                      "unit": "TFLOP/s", "frac": v2p["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None},
         "median_ms": v2p["median_ms"], "min_ms": v2p["min_ms"],
     }
+    v2t = _gpu_v2_train(max(3, args.steps // 10), 2)
+    extra["v2_train_4k"] = {"metric": "V2 fwd+bwd TFLOP/s", "value": v2t["tflops"], "unit": "TFLOP/s",
+                            "ms_per_step": v2t["ms_per_step"], "frac_of_bf16_peak": v2t["tflops"] / PEAK_BF16_TFLOPS,
+                            "config": {"workload": "v2_train_4k: the v2_prefill_4k workload, forward with training "
+                                                   "saves then backward"}}
     cpu = None
     extra["v2_decode"]["median_ms"], extra["v2_decode"]["min_ms"] = dec["median_ms"], dec["min_ms"]
     if not args.no_cpu_baseline:

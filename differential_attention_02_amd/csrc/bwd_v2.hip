@@ -14,7 +14,8 @@
 //
 // Kernels, in launch order:
 //   v2b_pre    one wave per (batch, pair, token) row: |g| and dlam from the
-//              float32 g and the saved A_o;
+//              float32 g and the saved A_o (and |V| of the row's key when the
+//              pair is the first on its KV head);
 //   v2b_scales one workgroup per (batch, KV head): power-of-two scales that
 //              keep the fp16 operands below 2^13: g by the largest row norm
 //              of the pairs on the head, dS by the bound
@@ -46,6 +47,7 @@ struct Ws2 {
   f16 *gh;               // [B, P, S, D]  g' = g 2^sg
   f16 *qh;               // [B, P, S, 2 D] Q_e (channels 0..127) | Q_o (128..255)
   float *ee, *eo, *gn;   // [B, P, S]  E_e, E_o (unscaled), |g|
+  float *vn;             // [B, Hkv, S]  |V| rows
   float *scales;         // [B * Hkv][4]: sg, kappa, omega, unused (exponents of 2)
 };
 
@@ -60,13 +62,15 @@ __host__ __device__ inline Ws2 carve2(void *base, int B, int S, int P, int Hkv) 
   w.ee = (float *)c; c += al256(rows * 4);
   w.eo = (float *)c; c += al256(rows * 4);
   w.gn = (float *)c; c += al256(rows * 4);
+  w.vn = (float *)c; c += al256((size_t)B * Hkv * S * 4);
   w.scales = (float *)c; c += al256((size_t)B * Hkv * 16);
   return w;
 }
 
 __host__ __device__ inline size_t ws2_bytes(int B, int S, int P, int Hkv) {
   const size_t rows = (size_t)B * P * S;
-  return al256(rows * D * 2) + al256(rows * 2 * D * 2) + 3 * al256(rows * 4) + al256((size_t)B * Hkv * 16);
+  return al256(rows * D * 2) + al256(rows * 2 * D * 2) + 3 * al256(rows * 4) + al256((size_t)B * Hkv * S * 4) +
+         al256((size_t)B * Hkv * 16);
 }
 
 __device__ __forceinline__ float sigmoid_of(const V2BwdParams &p, int b, int s, int pr) {
@@ -95,6 +99,13 @@ __global__ __launch_bounds__(NT) void v2b_pre_kernel(V2BwdParams p, Ws2 w) {
     w.gn[row] = sqrtf(gg);
     p.dlam[((int64_t)b * p.S + s) * P + pr] = -sg * (1.f - sg) * ga;
   }
+  const int ppk = p.Hq / p.Hkv / 2, j = pr / ppk;
+  if (pr % ppk == 0) {  // wave-uniform
+    const bf16 *vr = (const bf16 *)p.v + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c;
+    const float v0 = bf2f(vr[0]), v1 = bf2f(vr[1]);
+    const float vv = wave_sum(v0 * v0 + v1 * v1);
+    if (lane == 0) w.vn[((int64_t)b * p.Hkv + j) * p.S + s] = sqrtf(vv);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -109,15 +120,13 @@ __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
     const int64_t base = ((int64_t)b * P + j * ppk + pp) * p.S;
     for (int s = tid; s < p.S; s += NT) gm = fmaxf(gm, w.gn[base + s]);
   }
-  // |V| rows of this KV head: one wave per row.
   float vm = 0.f;
-  const bf16 *vb = (const bf16 *)p.v + b * p.kvs_b + j * p.kvs_h + 2 * lane;
-  for (int s = wave; s < p.S; s += NT / 64) {
-    const bf16 *vr = vb + (int64_t)s * p.kvs_s;
-    const float v0 = bf2f(vr[0]), v1 = bf2f(vr[1]);
-    vm = fmaxf(vm, wave_sum(v0 * v0 + v1 * v1));
+  const float *vn = w.vn + (int64_t)bj * p.S;
+  for (int s = tid; s < p.S; s += NT) vm = fmaxf(vm, vn[s]);
+  for (int o = 32; o > 0; o >>= 1) {
+    gm = fmaxf(gm, __shfl_xor(gm, o));
+    vm = fmaxf(vm, __shfl_xor(vm, o));
   }
-  for (int o = 32; o > 0; o >>= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
   if (lane == 0) {
     red[0][wave] = gm;
     red[1][wave] = vm;
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
   __syncthreads();
   if (tid == 0) {
     gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    vm = sqrtf(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])));
+    vm = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
     const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
     const float x = 2.f * gm * vm;  // bound on |dS| before scaling by 2^sg
     const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) : 0.f;
