@@ -357,7 +357,9 @@ def main(argv=None) -> int:
             r = _gpu_attn(args.only, args.steps, args.warmup)
             print(json.dumps({"workload": args.only, "tflops": r["tflops"], "event_tflops": r["event_tflops"]}))
         elif args.only == "train_8k":
-            print(json.dumps({"workload": "train_8k", **_gpu_train(args.steps, args.warmup)}))
+            r = _gpu_train(args.steps, args.warmup)
+            r.pop("inputs", None)
+            print(json.dumps({"workload": "train_8k", **r}))
         elif args.only == "v2_train_4k":
             print(json.dumps({"workload": "v2_train_4k", **_gpu_v2_train(args.steps, args.warmup)}))
         elif args.only == "v2_prefill_4k":
@@ -399,7 +401,8 @@ def main(argv=None) -> int:
         "config": {"workload": "v2_prefill_4k: batch 4, seq 4096 causal, 24 query heads over 12 KV heads, "
                                "D 128, bf16, sigmoid input per token and pair"},
         "roofline": {"bound": "mfma", "achieved": v2p["event_tflops"], "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": v2p["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": v2p["event_tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": _traffic_from_profile("fwd_v2_v2_prefill_4k_pmc.md", V2P_SOURCES)},
         "median_ms": v2p["median_ms"], "min_ms": v2p["min_ms"],
     }
     v2t = _gpu_v2_train(max(3, args.steps // 10), 2)
