@@ -13,6 +13,7 @@ from .diffattn_oracle import (  # noqa: F401
     v2_decode,
     v2_prefill_fwd,
     v2_prefill_bwd,
+    v1_decode,
     sigmoid,
 )
 from .brute import brute_diff_attn_fwd, brute_v2_decode, brute_v2_prefill_fwd  # noqa: F401

@@ -51,6 +51,7 @@ __all__ = [
     "v2_decode",
     "v2_prefill_fwd",
     "v2_prefill_bwd",
+    "v1_decode",
 ]
 
 
@@ -369,3 +370,39 @@ def v2_prefill_bwd(q, k, v, lam, dout, *, causal: bool = True, scale: float | No
                 dk[b, :, j] += s * (dS.T @ q[b, :, t])
                 dv[b, :, j] += P.T @ dA
     return {"dq": dq, "dk": dk, "dv": dv, "dlam": dlam}
+
+
+def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lam_init: float, seqlens=None, *,
+              norm: bool = True, eps: float = 1e-5, scale: float | None = None):
+    """DIFF V1 decode step: the V1 operator for one new query token per
+    sequence over a KV cache that holds K1, K2 and V ([G]; [N] multi-head
+    section; [V2] "DIFF V1 limits" names the decode cost of this layout).
+
+    q1, q2: [B, H, d]; k1_cache, k2_cache: [B, S_kv, H, d]; v_cache:
+    [B, S_kv, H, dv].  Per batch b and head h, over the first seqlens[b] cached
+    keys (all S_kv by default; the cache already holds the new token):
+      P_m = softmax(scale q_m K_m^T),  O = (P_1 - lam P_2) V,
+      Y = O / sqrt(mean_c O^2 + eps) (1 - lam_init)   if norm, else O.
+    A sequence of length 0 yields zeros.  Returns Y [B, H, dv].
+    """
+    q1, q2, k1_cache, k2_cache, v_cache = map(_f64, (q1, q2, k1_cache, k2_cache, v_cache))
+    B, H, d = q1.shape
+    S_kv, dv = k1_cache.shape[1], v_cache.shape[-1]
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lens = np.full(B, S_kv) if seqlens is None else np.asarray(seqlens)
+    out = np.zeros((B, H, dv))
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(H):
+            maps = []
+            for q, kc in ((q1, k1_cache), (q2, k2_cache)):
+                sc = (kc[b, :n, h] @ q[b, h]) * s
+                e = np.exp(sc - np.max(sc))
+                maps.append(e / np.sum(e))
+            o = (maps[0] - lam * maps[1]) @ v_cache[b, :n, h]
+            if norm:
+                o = o / np.sqrt(np.mean(o * o) + eps) * (1.0 - lam_init)
+            out[b, h] = o
+    return out
