@@ -14,7 +14,8 @@ Also reported under "extra": the 64K-token forward, the 8K training step
 flop per unmasked (query, key, pair of query heads), two QK^T and two PV
 products of width 128), and its training step (forward with saves + backward,
 2048 more flop per unmasked (query, key, pair): recomputed QK^T of both heads,
-one shared dP, one merged dV, dQ and dK of both heads).
+one shared dP, one merged dV, dQ and dK of both heads), and the DIFF V1 decode
+over a K1/K2/V cache (GB/s of cache + query + output bytes).
 Each timing: W untimed launches, then exactly K launches between two
 synchronisations; HIP events on the launch stream give the average launch
 duration used for the roofline.  "cpu_baseline" times the float64 oracle on a
@@ -249,6 +250,29 @@ def _gpu_v2_train(steps, warmup):
             "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
+def _gpu_v1_decode(steps, warmup):
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["v1_decode"]
+    inp = workloads.make_v1_decode_inputs(cfg)
+    x = [inp[n].cuda() for n in ("q1", "q2", "k1_cache", "k2_cache", "v_cache")]
+    vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    del inp
+    out = torch.empty((cfg.batch, cfg.heads, cfg.v_dim), dtype=x[0].dtype, device="cuda")
+    args = B.v1_decode_args(*x, out, lambda_init=B.lambda_init(cfg.layer), lambda_vecs=vecs, eps=cfg.eps)
+    nbytes = B.v1_decode_workspace_size(args)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), nbytes
+    each = []
+    wall, per = _time_launches(lambda: B.v1_decode_launch(args), steps, warmup, each)
+    moved = (cfg.batch * cfg.kv_len * cfg.heads * (2 * cfg.head_dim + cfg.v_dim)
+             + 2 * cfg.batch * cfg.heads * cfg.head_dim + cfg.batch * cfg.heads * cfg.v_dim) * 2
+    return {"cfg": cfg, "bytes_per_step": moved, "gbs": moved * steps / wall / 1e9,
+            "event_gbs": moved / per / 1e9, "event_s_per_launch": per, "splits": args.num_splits,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -326,7 +350,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k",
-                                       "v2_train_4k"],
+                                       "v2_train_4k", "v1_decode"],
                     default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -360,6 +384,10 @@ def main(argv=None) -> int:
             r = _gpu_train(args.steps, args.warmup)
             r.pop("inputs", None)
             print(json.dumps({"workload": "train_8k", **r}))
+        elif args.only == "v1_decode":
+            r = _gpu_v1_decode(args.steps, args.warmup)
+            print(json.dumps({"workload": "v1_decode", "gbs": r["gbs"], "event_gbs": r["event_gbs"],
+                              "median_ms": r["median_ms"], "min_ms": r["min_ms"]}))
         elif args.only == "v2_train_4k":
             print(json.dumps({"workload": "v2_train_4k", **_gpu_v2_train(args.steps, args.warmup)}))
         elif args.only == "v2_prefill_4k":
@@ -404,6 +432,17 @@ def main(argv=None) -> int:
                      "unit": "TFLOP/s", "frac": v2p["event_tflops"] / PEAK_BF16_TFLOPS,
                      "traffic": _traffic_from_profile("fwd_v2_v2_prefill_4k_pmc.md", V2P_SOURCES)},
         "median_ms": v2p["median_ms"], "min_ms": v2p["min_ms"],
+    }
+    v1d = _gpu_v1_decode(args.steps, args.warmup)
+    extra["v1_decode"] = {
+        "metric": "V1 decode HBM GB/s", "value": v1d["gbs"], "unit": "GB/s",
+        "ms_per_step": v1d["event_s_per_launch"] * 1e3,
+        "config": {"workload": "v1_decode: B64, 16 heads, K1/K2 width 64, V width 128, KV 8192, bf16, "
+                               "lambda from 64-dim vectors, per-head RMSNorm", "num_splits": "auto"},
+        "roofline": {"bound": "hbm", "achieved": v1d["event_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": v1d["event_gbs"] / PEAK_HBM_GBS,
+                     "traffic": _traffic_from_profile("v1dec_split_v1_decode_pmc.md", DEC_SOURCES)},
+        "median_ms": v1d["median_ms"], "min_ms": v1d["min_ms"],
     }
     v2t = _gpu_v2_train(max(3, args.steps // 10), 2)
     extra["v2_train_4k"] = {"metric": "V2 fwd+bwd TFLOP/s", "value": v2t["tflops"], "unit": "TFLOP/s",

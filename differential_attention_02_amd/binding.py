@@ -69,6 +69,23 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class V1DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_i32), ("heads", c_i32), ("head_dim", c_i32), ("v_dim", c_i32), ("kv_len", c_i32),
+        ("dtype", c_i32), ("norm", c_i32),
+        ("q1", c_vp), ("q2", c_vp), ("q_stride", c_i64 * 2),
+        ("k1_cache", c_vp), ("k2_cache", c_vp), ("k_stride", c_i64 * 3),
+        ("v_cache", c_vp), ("v_stride", c_i64 * 3),
+        ("seqlens", c_vp),
+        ("lq1", c_fp), ("lk1", c_fp), ("lq2", c_fp), ("lk2", c_fp),
+        ("lambda_dim", c_i32), ("lambda_fixed", c_f32), ("lambda_init", c_f32),
+        ("softmax_scale", c_f32), ("eps", c_f32),
+        ("out", c_vp), ("o_stride", c_i64 * 2),
+        ("num_splits", c_i32),
+        ("workspace", c_vp), ("workspace_bytes", c_sz),
+    ]
+
+
 class V2FwdArgs(ctypes.Structure):
     _fields_ = [
         ("batch", c_i32), ("seqlen", c_i32), ("q_heads", c_i32), ("kv_heads", c_i32), ("head_dim", c_i32),
@@ -106,6 +123,8 @@ SIGNATURES = {
     "diffattn_bwd_workspace_size": (c_sz, [ctypes.POINTER(BwdArgs)]),
     "diffattn_v2_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v2_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeArgs)]),
+    "diffattn_v1_decode": (ctypes.c_int, [ctypes.POINTER(V1DecodeArgs), c_vp]),
+    "diffattn_v1_decode_workspace_size": (c_sz, [ctypes.POINTER(V1DecodeArgs)]),
     "diffattn_v2_fwd": (ctypes.c_int, [ctypes.POINTER(V2FwdArgs), c_vp]),
     "diffattn_v2_bwd": (ctypes.c_int, [ctypes.POINTER(V2BwdArgs), c_vp]),
     "diffattn_v2_bwd_workspace_size": (c_sz, [ctypes.POINTER(V2BwdArgs)]),
@@ -471,3 +490,71 @@ def v2_bwd(q, k, v, lam, dout, saves, *, causal: bool = True, softmax_scale: flo
     if lam.dim() < 3:
         dl = dlam.sum(dim=tuple(range(3 - lam.dim())))
     return {"dq": dq, "dk": dk, "dv": dv, "dlam": dl}
+
+
+def v1_decode_args(q1, q2, k1_cache, k2_cache, v_cache, out, *, lambda_init: float, lambda_vecs=None,
+                   lambda_fixed: float = 0.8, norm: bool = True, eps: float = 1e-5, seqlens=None,
+                   softmax_scale: float = 0.0, num_splits: int = 0):
+    """V1DecodeArgs for q1, q2 [B,H,d], k1_cache, k2_cache [B,S_kv,H,d],
+    v_cache [B,S_kv,H,dv], out [B,H,dv] (workspace not yet attached)."""
+    _require(q1.dim() == 3 and k1_cache.dim() == 4 and v_cache.dim() == 4,
+             "q must be [B, H, d], caches [B, S_kv, H, c]")
+    B, H, d = q1.shape
+    _require(tuple(q2.shape) == (B, H, d) and q2.stride() == q1.stride(), "q1 and q2 must share shape and strides")
+    _require(k1_cache.shape[0] == B and k1_cache.shape[2] == H and k1_cache.shape[3] == d,
+             "k cache shape does not match q")
+    _require(tuple(k2_cache.shape) == tuple(k1_cache.shape) and k2_cache.stride() == k1_cache.stride(),
+             "k1_cache and k2_cache must share shape and strides")
+    _require(tuple(v_cache.shape[:3]) == tuple(k1_cache.shape[:3]), "v_cache must be [B, S_kv, H, dv]")
+    dv = v_cache.shape[3]
+    _require(tuple(out.shape) == (B, H, dv), "out must be [B, H, dv]")
+    _check_dev((("q1", q1), ("q2", q2), ("k1_cache", k1_cache), ("k2_cache", k2_cache), ("v_cache", v_cache),
+                ("out", out)), dtype=q1.dtype, device=q1.device)
+    if seqlens is not None:
+        _require(seqlens.dtype == torch.int32 and seqlens.is_cuda and seqlens.device == q1.device
+                 and tuple(seqlens.shape) == (B,) and seqlens.is_contiguous(), "seqlens: int32 [B] on q's GPU")
+    a = V1DecodeArgs()
+    a.batch, a.heads, a.head_dim, a.v_dim, a.kv_len = B, H, d, dv, k1_cache.shape[1]
+    a.dtype, a.norm = _dtype_code(q1), int(bool(norm))
+    a.q1, a.q2, a.q_stride = _ptr(q1), _ptr(q2), (c_i64 * 2)(q1.stride(0), q1.stride(1))
+    a.k1_cache, a.k2_cache, a.k_stride = _ptr(k1_cache), _ptr(k2_cache), _strides3(k1_cache)
+    a.v_cache, a.v_stride = _ptr(v_cache), _strides3(v_cache)
+    a.seqlens = _ptr(seqlens)
+    if lambda_vecs is not None:
+        _require(len(lambda_vecs) == 4, "lambda_vecs must hold lq1, lk1, lq2, lk2")
+        n = lambda_vecs[0].numel()
+        for t in lambda_vecs:
+            _require(t.is_contiguous() and t.numel() == n and t.dim() == 1, "lambda vectors: 1-D, contiguous, equal length")
+        _check_dev((("lambda_vec%d" % i, t) for i, t in enumerate(lambda_vecs)), dtype=torch.float32, device=q1.device)
+        a.lq1, a.lk1, a.lq2, a.lk2 = (_ptr(t) for t in lambda_vecs)
+        a.lambda_dim = n
+    a.lambda_fixed, a.lambda_init = float(lambda_fixed), float(lambda_init)
+    a.softmax_scale, a.eps = float(softmax_scale), float(eps)
+    a.out, a.o_stride = _ptr(out), (c_i64 * 2)(out.stride(0), out.stride(1))
+    a.num_splits = int(num_splits)
+    return a
+
+
+def v1_decode_workspace_size(args: V1DecodeArgs) -> int:
+    return int(lib().diffattn_v1_decode_workspace_size(ctypes.byref(args)))
+
+
+def v1_decode_launch(args: V1DecodeArgs) -> None:
+    _check(lib().diffattn_v1_decode(ctypes.byref(args), _stream()), "diffattn_v1_decode")
+
+
+def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, *, lambda_init: float, lambda_vecs=None,
+              lambda_fixed: float = 0.8, norm: bool = True, eps: float = 1e-5, seqlens=None,
+              softmax_scale: float = 0.0, num_splits: int = 0, out=None):
+    """DIFF V1 decode step through diffattn_v1_decode; returns out [B, H, dv]."""
+    B, H, _ = q1.shape
+    if out is None:
+        out = torch.empty((B, H, v_cache.shape[3]), dtype=q1.dtype, device=q1.device)
+    a = v1_decode_args(q1, q2, k1_cache, k2_cache, v_cache, out, lambda_init=lambda_init, lambda_vecs=lambda_vecs,
+                       lambda_fixed=lambda_fixed, norm=norm, eps=eps, seqlens=seqlens,
+                       softmax_scale=softmax_scale, num_splits=num_splits)
+    nbytes = v1_decode_workspace_size(a)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q1.device)
+    a.workspace, a.workspace_bytes = _ptr(ws), nbytes
+    v1_decode_launch(a)
+    return out

@@ -335,6 +335,82 @@ int diffattn_v2_bwd(const diffattn_v2_bwd_args *a, void *stream) {
   return hip_status(diffattn::launch_v2_bwd(p, static_cast<hipStream_t>(stream)), "V2 backward launch");
 }
 
+static int check_v1_decode(const diffattn_v1_decode_args *a, int *splits_out) {
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0 || a->heads < 1 || a->kv_len < 0)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, heads >= 1, kv_len >= 0");
+  if (a->dtype != DIFFATTN_F32 && a->dtype != DIFFATTN_BF16) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "unknown dtype %d", a->dtype);
+  if (a->head_dim != 64 || a->v_dim != 128)
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "V1 decode is built for head_dim 64, v_dim 128");
+  if (!a->q1 || !a->q2 || !a->k1_cache || !a->k2_cache || !a->v_cache || !a->out)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "q1, q2, k1_cache, k2_cache, v_cache and out must be non-NULL");
+  if (a->q_stride[0] < 1 || a->q_stride[1] < 1 || a->o_stride[0] < 1 || a->o_stride[1] < 1 ||
+      !strides_ok(a->k_stride, 3) || !strides_ok(a->v_stride, 3))
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
+  const int nvec = (a->lq1 != nullptr) + (a->lk1 != nullptr) + (a->lq2 != nullptr) + (a->lk2 != nullptr);
+  if (nvec != 0 && nvec != 4) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "give all four lambda vectors or none");
+  if (nvec == 4 && a->lambda_dim < 1) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "lambda_dim must be >= 1");
+  if (nvec == 0 && !std::isfinite(a->lambda_fixed)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "lambda_fixed must be finite");
+  if (!std::isfinite(a->lambda_init)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "lambda_init must be finite");
+  if (!std::isfinite(a->softmax_scale)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (!(a->eps >= 0.f) || !std::isfinite(a->eps)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  const int64_t vec = a->dtype == DIFFATTN_BF16 ? 8 : 4;
+  if (!aligned16(a->k1_cache) || !aligned16(a->k2_cache) || !aligned16(a->v_cache) ||
+      !strides_mult(a->k_stride, 3, vec) || !strides_mult(a->v_stride, 3, vec))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "caches need 16-byte aligned rows");
+  if (a->num_splits < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  int splits = a->num_splits ? a->num_splits : diffattn::decode_auto_splits(a->batch, a->heads, a->kv_len);
+  if (splits < 1) splits = 1;
+  const int chunk = (a->kv_len + splits - 1) / splits;
+  if (chunk > diffattn::decode_max_chunk())
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "num_splits %d leaves %d keys per split (max %d)", splits, chunk,
+                diffattn::decode_max_chunk());
+  *splits_out = splits;
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_v1_decode_workspace_size(const diffattn_v1_decode_args *a) {
+  std::string keep = g_last_error;
+  int splits = 0;
+  const int rc = check_v1_decode(a, &splits);
+  g_last_error = keep;
+  if (rc) return 0;
+  return diffattn::v1_decode_workspace_bytes(a->batch, a->heads, splits);
+}
+
+int diffattn_v1_decode(const diffattn_v1_decode_args *a, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0");
+  if (a->batch == 0) return DIFFATTN_OK;
+  int splits = 0;
+  int rc = check_v1_decode(a, &splits);
+  if (rc) return rc;
+  const size_t need = diffattn::v1_decode_workspace_bytes(a->batch, a->heads, splits);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(DIFFATTN_ERR_WORKSPACE, "V1 decode needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
+  if (!aligned16(a->workspace)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  diffattn::V1DecodeParams p{};
+  p.q1 = a->q1; p.q2 = a->q2; p.k1 = a->k1_cache; p.k2 = a->k2_cache; p.v = a->v_cache;
+  p.qs_b = a->q_stride[0]; p.qs_h = a->q_stride[1];
+  p.ks_b = a->k_stride[0]; p.ks_s = a->k_stride[1]; p.ks_h = a->k_stride[2];
+  p.vs_b = a->v_stride[0]; p.vs_s = a->v_stride[1]; p.vs_h = a->v_stride[2];
+  p.os_b = a->o_stride[0]; p.os_h = a->o_stride[1];
+  p.seqlens = a->seqlens;
+  p.lq1 = a->lq1; p.lk1 = a->lk1; p.lq2 = a->lq2; p.lk2 = a->lk2;
+  p.lambda_dim = a->lambda_dim; p.lambda_fixed = a->lambda_fixed; p.lambda_init = a->lambda_init;
+  p.norm = a->norm != 0; p.eps = a->eps;
+  p.out = a->out;
+  p.B = a->batch; p.H = a->heads; p.L = a->kv_len;
+  p.splits = splits;
+  p.chunk = (a->kv_len + splits - 1) / splits;
+  if (p.chunk < 1) p.chunk = 1;
+  p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
+  p.part_o = static_cast<float *>(a->workspace);
+  p.part_ml = p.part_o + (size_t)a->batch * a->heads * 2 * splits * a->v_dim;
+  return hip_status(diffattn::launch_v1_decode(p, a->dtype, static_cast<hipStream_t>(stream)), "V1 decode launch");
+}
+
 static int check_decode(const diffattn_v2_decode_args *a, int *splits_out) {
   if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0 || a->q_heads < 2 || a->kv_heads < 1 || a->kv_len < 0)

@@ -16,6 +16,17 @@
 //     (max, sum, un-normalised output) go to the workspace.
 //   decode_combine: per (batch, pair) merges the chunks by log-sum-exp
 //     rescaling, normalises, and applies the even/odd sigmoid(lambda) combine.
+//
+// DIFF V1 decode step (glossary page "Differential Transformer", section "How
+// differential attention works"; news write-up, multi-head section; the V2
+// page's section "DIFF V1 limits" names this layout's decode cost: a cache of
+// K1, K2 and a double-width V, with V loaded once per map when each map is a
+// separate attention call).  Same split-K layout with one workgroup per (key
+// chunk, head, batch): phase 1 streams K1 and K2 rows together and scores
+// both maps, phase 2 takes each map's max and sum, phase 3 streams V once and
+// accumulates both maps' weighted rows.  The combine merges each map's chunks,
+// forms (map1 - lambda map2) V, and applies the per-head RMSNorm times
+// (1 - lambda_init).
 #include "common.h"
 #include "kernels.h"
 
@@ -254,7 +265,209 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
+constexpr int V1D = 64, V1DV = 128;
+
+template <typename T>
+__global__ __launch_bounds__(NT) void v1dec_split_kernel(V1DecodeParams p) {
+  constexpr int LPK = V1D / 8, KPW = 64 / LPK;     // K rows: 8 lanes, 8 keys per wave step
+  constexpr int LPV = V1DV / 8, KPV = 64 / LPV;    // V rows: 16 lanes, 4 keys per wave step
+  constexpr int U = 4;
+  typedef RowLoad<T> RL;
+  typedef typename RL::raw_t raw_t;
+  __shared__ float s_lds[2][MAX_CHUNK];
+  __shared__ float red[4][2][V1DV];
+  __shared__ float stat[4][2];
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int len = p.L;
+  if (p.seqlens) len = min(max(p.seqlens[b], 0), p.L);
+  const int kb = split * p.chunk;
+  const int n = max(0, min(len, kb + p.chunk) - kb);
+  const float c = p.scale * kLog2e;
+
+  // Phase 1: both maps' scores (log2 domain) of every key of the chunk.
+  {
+    const int part = lane % LPK, kl = lane / LPK;
+    float q1[8], q2[8];
+    const T *q1p = (const T *)p.q1 + b * p.qs_b + h * p.qs_h + part * 8;
+    const T *q2p = (const T *)p.q2 + b * p.qs_b + h * p.qs_h + part * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      q1[e] = (float)q1p[e] * c;
+      q2[e] = (float)q2p[e] * c;
+    }
+    const int64_t koff = b * p.ks_b + h * p.ks_h + (int64_t)kb * p.ks_s + part * 8;
+    const T *k1b = (const T *)p.k1 + koff, *k2b = (const T *)p.k2 + koff;
+    for (int base = wave * KPW * U; base < n; base += 4 * KPW * U) {
+      raw_t r1[U], r2[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int key = base + u * KPW + kl;
+        r1[u] = key < n ? RL::load(k1b + (int64_t)key * p.ks_s) : RL::zero();
+        r2[u] = key < n ? RL::load(k2b + (int64_t)key * p.ks_s) : RL::zero();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float f1[8], f2[8];
+        RL::cvt(r1[u], f1);
+        RL::cvt(r2[u], f2);
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s1 = fmaf(q1[e], f1[e], s1);
+          s2 = fmaf(q2[e], f2[e], s2);
+        }
+#pragma unroll
+        for (int o = 1; o < LPK; o <<= 1) {
+          s1 += __shfl_xor(s1, o);
+          s2 += __shfl_xor(s2, o);
+        }
+        const int key = base + u * KPW + kl;
+        if (part == 0 && key < n) {
+          s_lds[0][key] = s1;
+          s_lds[1][key] = s2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: each map's max and sum over the chunk; scores become 2^(s - m).
+  float m[2], l[2];
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) {
+    float mx = kNegInf;
+    for (int i = tid; i < n; i += NT) mx = fmaxf(mx, s_lds[mp][i]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) stat[wave][mp] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) m[mp] = fmaxf(fmaxf(stat[0][mp], stat[1][mp]), fmaxf(stat[2][mp], stat[3][mp]));
+  __syncthreads();
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) {
+    float sm = 0.f;
+    for (int i = tid; i < n; i += NT) {
+      const float e = fast_exp2(s_lds[mp][i] - m[mp]);
+      s_lds[mp][i] = e;
+      sm += e;
+    }
+    sm = wave_sum(sm);
+    if (lane == 0) stat[wave][mp] = sm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) l[mp] = (stat[0][mp] + stat[1][mp]) + (stat[2][mp] + stat[3][mp]);
+
+  // Phase 3: both maps' un-normalised P V over the chunk, V read once.
+  const int part = lane % LPV, kl = lane / LPV;
+  float a1[8], a2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a1[e] = a2[e] = 0.f;
+  const T *vb = (const T *)p.v + b * p.vs_b + h * p.vs_h + (int64_t)kb * p.vs_s + part * 8;
+  for (int base = wave * KPV * U; base < n; base += 4 * KPV * U) {
+    raw_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPV + kl;
+      r[u] = key < n ? RL::load(vb + (int64_t)key * p.vs_s) : RL::zero();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * KPV + kl;
+      if (key < n) {
+        float vf[8];
+        RL::cvt(r[u], vf);
+        const float p1 = s_lds[0][key], p2 = s_lds[1][key];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a1[e] = fmaf(p1, vf[e], a1[e]);
+          a2[e] = fmaf(p2, vf[e], a2[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    for (int o = LPV; o < 64; o <<= 1) {
+      a1[e] += __shfl_xor(a1[e], o);
+      a2[e] += __shfl_xor(a2[e], o);
+    }
+  if (kl == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      red[wave][0][part * 8 + e] = a1[e];
+      red[wave][1][part * 8 + e] = a2[e];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * V1DV; i += NT) {
+    const int mp = i / V1DV, ch = i % V1DV;
+    const float x = (red[0][mp][ch] + red[1][mp][ch]) + (red[2][mp][ch] + red[3][mp][ch]);
+    const int64_t slot = (((int64_t)b * p.H + h) * 2 + mp) * p.splits + split;
+    p.part_o[slot * V1DV + ch] = x;
+    if (ch == 0) {
+      p.part_ml[slot * 2] = n > 0 ? m[mp] : kNegInf;
+      p.part_ml[slot * 2 + 1] = n > 0 ? l[mp] : 0.f;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(V1DV) void v1dec_combine_kernel(V1DecodeParams p) {
+  __shared__ float ss_w[V1DV / 64];
+  const int h = blockIdx.x, b = blockIdx.y, ch = threadIdx.x;
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  float a[2];
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp) {
+    const int64_t slot0 = (((int64_t)b * p.H + h) * 2 + mp) * p.splits;
+    float M = kNegInf;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[(slot0 + s) * 2]);
+    float L = 0.f, acc = 0.f;
+    if (M != kNegInf) {
+      for (int s = 0; s < p.splits; ++s) {
+        const float w = fast_exp2(p.part_ml[(slot0 + s) * 2] - M);
+        L = fmaf(p.part_ml[(slot0 + s) * 2 + 1], w, L);
+        acc = fmaf(p.part_o[(slot0 + s) * V1DV + ch], w, acc);
+      }
+    }
+    a[mp] = L > 0.f ? acc / L : 0.f;
+  }
+  float o = fmaf(-lam, a[1], a[0]);
+  if (p.norm) {
+    const float ss = wave_sum(o * o);
+    if ((ch & 63) == 0) ss_w[ch >> 6] = ss;
+    __syncthreads();
+    const float ms = (ss_w[0] + ss_w[1]) * (1.f / V1DV);
+    o *= (1.f - p.lambda_init) / sqrtf(ms + p.eps);
+  }
+  T *out = (T *)p.out + b * p.os_b + h * p.os_h;
+  out[ch] = (T)o;
+}
+
 }  // namespace
+
+size_t v1_decode_workspace_bytes(int B, int H, int splits) {
+  return (size_t)B * H * 2 * splits * (V1DV + 2) * sizeof(float);
+}
+
+hipError_t launch_v1_decode(const V1DecodeParams &p, int dtype, hipStream_t st) {
+  dim3 grid(p.splits, p.H, p.B);
+  if (dtype == 0)
+    hipLaunchKernelGGL(v1dec_split_kernel<float>, grid, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL(v1dec_split_kernel<bf16>, grid, dim3(NT), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dtype == 0)
+    hipLaunchKernelGGL(v1dec_combine_kernel<float>, dim3(p.H, p.B), dim3(V1DV), 0, st, p);
+  else
+    hipLaunchKernelGGL(v1dec_combine_kernel<bf16>, dim3(p.H, p.B), dim3(V1DV), 0, st, p);
+  return hipGetLastError();
+}
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int splits) {
   return (size_t)B * Hq * splits * (D + 2) * sizeof(float);

@@ -54,6 +54,24 @@ struct DecodeParams {
   float *part_ml;  // [B, Hq, splits, 2]
 };
 
+// DIFF V1 decode step over a K1/K2/V cache (d = 64, dv = 128).
+struct V1DecodeParams {
+  const void *q1, *q2, *k1, *k2, *v;
+  int64_t qs_b, qs_h, ks_b, ks_s, ks_h, vs_b, vs_s, vs_h, os_b, os_h;
+  const int32_t *seqlens;
+  const float *lq1, *lk1, *lq2, *lk2;
+  int lambda_dim;
+  float lambda_fixed, lambda_init;
+  int norm;
+  float eps;
+  void *out;
+  int B, H, L;
+  int splits, chunk;
+  float scale;
+  float *part_o;   // [B, H, 2, splits, dv]
+  float *part_ml;  // [B, H, 2, splits, 2]
+};
+
 // DIFF V2 prefill forward: Hq query heads over Hkv KV heads, bf16, D = 128.
 struct V2FwdParams {
   const void *q, *k, *v;
@@ -97,6 +115,8 @@ size_t bwd_workspace_bytes(int B, int S, int H, int d, int dv);
 hipError_t launch_bwd(const BwdParams &p, hipStream_t st);
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int splits);
+size_t v1_decode_workspace_bytes(int B, int H, int splits);
+hipError_t launch_v1_decode(const V1DecodeParams &p, int dtype, hipStream_t st);
 int decode_max_chunk();
 int decode_auto_splits(int B, int Hkv, int L);
 hipError_t launch_decode(const DecodeParams &p, int dtype, hipStream_t st);

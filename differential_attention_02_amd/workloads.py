@@ -5,7 +5,8 @@ computes no attention, lambda or normalisation.  All draws come from a CPU
 torch.Generator seeded per call, in a fixed order:
 q1, k1, q2, k2, v, then the four lambda vectors (lq1, lk1, lq2, lk2), then the
 upstream gradient dy; for the V2 decode: q, k_cache, v_cache, lam; for the V2
-prefill: q, k, v, lam (then dy when a gradient is asked for).
+prefill: q, k, v, lam (then dy when a gradient is asked for); for the V1
+decode: q1, q2, k1_cache, k2_cache, v_cache, then the four lambda vectors.
 Each tensor is drawn in float32 one batch entry at a time, multiplied by its
 scale, and (for bf16 workloads) rounded once to bfloat16 (round to nearest
 even).  The oracle upcasts those same rounded values exactly.
@@ -17,8 +18,8 @@ import math
 
 import torch
 
-__all__ = ["AttnConfig", "DecodeConfig", "V2PrefillConfig", "CONFIGS", "make_attn_inputs",
-           "make_decode_inputs", "make_v2_prefill_inputs", "worked_example_inputs"]
+__all__ = ["AttnConfig", "DecodeConfig", "V1DecodeConfig", "V2PrefillConfig", "CONFIGS", "make_attn_inputs",
+           "make_decode_inputs", "make_v1_decode_inputs", "make_v2_prefill_inputs", "worked_example_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,6 +63,24 @@ class DecodeConfig:
 
 
 @dataclasses.dataclass(frozen=True)
+class V1DecodeConfig:
+    """A DIFF V1 decode workload: one new token per sequence over a cache of
+    K1, K2 (width d) and V (width dv)."""
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    v_dim: int
+    kv_len: int
+    dtype: torch.dtype
+    input_scale: float
+    layer: int
+    lambda_vec_dim: int = 64
+    lambda_vec_std: float = 0.1
+    eps: float = 1e-5
+
+
+@dataclasses.dataclass(frozen=True)
 class V2PrefillConfig:
     """A DIFF V2 prefill workload: whole sequences, Hq query heads over Hkv KV
     heads, a sigmoid input per (batch, token, pair)."""
@@ -98,6 +117,9 @@ CONFIGS = {
     # DIFF V2 decode: 32 query heads over 16 KV heads, cache length 8192.
     "v2_decode": DecodeConfig("v2_decode", 64, 32, 16, 128, 8192, torch.bfloat16,
                               1.0 / math.sqrt(128)),
+    # DIFF V1 decode over a K1/K2/V cache with the V2 decode's cache bytes:
+    # 16 heads of K1, K2 (64 wide) and V (128 wide), cache length 8192.
+    "v1_decode": V1DecodeConfig("v1_decode", 64, 16, 64, 128, 8192, torch.bfloat16, 1.0 / 8.0, 12),
     # DIFF V2 prefill at 4K: 24 query heads over 12 KV heads (one even/odd pair
     # per KV head), head width 128, causal.
     "v2_prefill_4k": V2PrefillConfig("v2_prefill_4k", 4, 4096, 24, 12, 128, torch.bfloat16, True,
@@ -161,6 +183,29 @@ def make_decode_inputs(cfg: DecodeConfig | str = "v2_decode", seed: int = 0, *,
     }
     lam_shape = (cfg.q_heads // 2,) if cfg.lam_shape == "per_head" else (B, cfg.q_heads // 2)
     t["lam"] = torch.randn(lam_shape, generator=gen, dtype=torch.float32)
+    t["cfg"] = cfg
+    return t
+
+
+def make_v1_decode_inputs(cfg: V1DecodeConfig | str = "v1_decode", seed: int = 0, *,
+                          batch: int | None = None, kv_len: int | None = None, heads: int | None = None) -> dict:
+    """Inputs of a DIFF V1 decode workload on the CPU: q1, q2 [B,H,d],
+    k1_cache, k2_cache [B,S_kv,H,d], v_cache [B,S_kv,H,dv], lambda_vecs."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    B = cfg.batch if batch is None else batch
+    L = cfg.kv_len if kv_len is None else kv_len
+    H = cfg.heads if heads is None else heads
+    gen = torch.Generator().manual_seed(seed)
+    t = {
+        "q1": _draw(gen, (B, H, cfg.head_dim), cfg.input_scale, cfg.dtype),
+        "q2": _draw(gen, (B, H, cfg.head_dim), cfg.input_scale, cfg.dtype),
+        "k1_cache": _draw(gen, (B, L, H, cfg.head_dim), cfg.input_scale, cfg.dtype),
+        "k2_cache": _draw(gen, (B, L, H, cfg.head_dim), cfg.input_scale, cfg.dtype),
+        "v_cache": _draw(gen, (B, L, H, cfg.v_dim), cfg.input_scale, cfg.dtype),
+    }
+    t["lambda_vecs"] = tuple(torch.randn(cfg.lambda_vec_dim, generator=gen, dtype=torch.float32) * cfg.lambda_vec_std
+                             for _ in range(4))
     t["cfg"] = cfg
     return t
 

@@ -26,6 +26,7 @@
  *     or not), with a sigmoid input per token and pair [same sections; item 5
  *     makes lambda per token and per head].
  *   - DIFF V2 prefill backward: its gradients by the chain rule.
+ *   - DIFF V1 decode: the V1 operator for one new token over a K1/K2/V cache.
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a device pointer owned by the caller (for example
@@ -240,6 +241,50 @@ typedef struct diffattn_v2_bwd_args {
   size_t workspace_bytes;
 } diffattn_v2_bwd_args;
 
+/*
+ * DIFF V1 decode arguments (one new query token per sequence) over a cache of
+ * K1, K2 and V [glossary page, section "How differential attention works";
+ * news write-up, multi-head section; the V2 page's section "DIFF V1 limits"
+ * names this cache layout's decode cost, V read once per map].  V is read
+ * once here for both maps.
+ *   q1, q2 [B, H, d] sharing q_stride (batch, head); k1_cache, k2_cache
+ *   [B, S_kv, H, d] sharing k_stride (batch, seq, head); v_cache
+ *   [B, S_kv, H, dv] (v_stride).  Supported: bf16 or f32, d = 64, dv = 128;
+ *   caches 16-byte aligned with row strides that keep rows 16-byte aligned.
+ *   seqlens: device int32[B] (NULL = every sequence has kv_len keys); values
+ *   are clamped to [0, kv_len]; a length of 0 yields a zero output row.
+ *   lambda: from the four device vectors lq1, lk1, lq2, lk2 (float32,
+ *   lambda_dim each) when all four are non-NULL, else lambda_fixed.
+ *   out [B, H, dv] (strides o_stride: batch, head), in the cache dtype:
+ *   (map1 - lambda map2) V over the cached keys, then with norm = 1 the
+ *   per-head RMSNorm (eps inside the root) times (1 - lambda_init).
+ *   softmax_scale <= 0 selects 1/sqrt(d).  num_splits: key chunks per
+ *   (batch, head) (0 = chosen by the library).  workspace: at least
+ *   diffattn_v1_decode_workspace_size() bytes, 16-byte aligned.
+ */
+typedef struct diffattn_v1_decode_args {
+  int32_t batch, heads, head_dim, v_dim, kv_len;
+  int32_t dtype, norm;
+  const void *q1, *q2;
+  int64_t q_stride[2];
+  const void *k1_cache, *k2_cache;
+  int64_t k_stride[3];
+  const void *v_cache;
+  int64_t v_stride[3];
+  const int32_t *seqlens;
+  const float *lq1, *lk1, *lq2, *lk2;
+  int32_t lambda_dim;
+  float lambda_fixed;
+  float lambda_init;
+  float softmax_scale;
+  float eps;
+  void *out;
+  int64_t o_stride[2];
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+} diffattn_v1_decode_args;
+
 /* Forward pass. Returns DIFFATTN_OK or a negative status. */
 int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
 
@@ -254,6 +299,12 @@ int diffattn_v2_decode(const diffattn_v2_decode_args *args, void *stream);
 
 /* Workspace bytes diffattn_v2_decode needs for these arguments (0 if invalid). */
 size_t diffattn_v2_decode_workspace_size(const diffattn_v2_decode_args *args);
+
+/* DIFF V1 decode step. Returns DIFFATTN_OK or a negative status. */
+int diffattn_v1_decode(const diffattn_v1_decode_args *args, void *stream);
+
+/* Workspace bytes diffattn_v1_decode needs for these arguments (0 if invalid). */
+size_t diffattn_v1_decode_workspace_size(const diffattn_v1_decode_args *args);
 
 /* DIFF V2 prefill forward. Returns DIFFATTN_OK or a negative status. */
 int diffattn_v2_fwd(const diffattn_v2_fwd_args *args, void *stream);

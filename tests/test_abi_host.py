@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -255,6 +255,53 @@ def test_v2_bwd_rejects_small_workspace():
     assert lib.diffattn_v2_bwd(ctypes.byref(a), None) == -1
 
 
+def _v1d_args(**kw):
+    a = B.V1DecodeArgs()
+    a.batch, a.heads, a.head_dim, a.v_dim, a.kv_len = 2, 16, 64, 128, 8192
+    a.dtype, a.norm = B.BF16, 1
+    a.q1 = a.q2 = a.k1_cache = a.k2_cache = a.v_cache = a.out = FAKE
+    a.q_stride = (ctypes.c_int64 * 2)(16 * 64, 64)
+    a.k_stride = (ctypes.c_int64 * 3)(8192 * 16 * 64, 16 * 64, 64)
+    a.v_stride = (ctypes.c_int64 * 3)(8192 * 16 * 128, 16 * 128, 128)
+    a.o_stride = (ctypes.c_int64 * 2)(16 * 128, 128)
+    a.lambda_fixed, a.lambda_init, a.eps = 0.8, 0.2, 1e-5
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_v1_decode_workspace_and_empty_call():
+    lib = B.lib()
+    a = _v1d_args()
+    n = lib.diffattn_v1_decode_workspace_size(ctypes.byref(a))
+    assert n > 0 and n % (2 * 16 * 2 * 130 * 4) == 0   # [B, H, 2 maps, splits, dv + 2] float32
+    a.batch = 0
+    assert lib.diffattn_v1_decode(ctypes.byref(a), None) == 0
+
+
+@host_only
+@pytest.mark.parametrize("field,value,code", [
+    ("heads", 0, -1), ("dtype", 4, -1), ("q2", None, -1), ("k2_cache", None, -1), ("out", None, -1),
+    ("head_dim", 32, -2), ("v_dim", 64, -2), ("v_cache", FAKE + 8, -2),
+    ("lq1", FAKE, -1), ("eps", -1.0, -1), ("num_splits", 2, -1), ("num_splits", -1, -1),
+    ("k_stride", (ctypes.c_int64 * 3)(8192 * 16 * 64, 16 * 64 + 4, 64), -2),
+])
+def test_v1_decode_rejects(field, value, code):
+    a = _v1d_args(**{field: value})
+    a.workspace, a.workspace_bytes = FAKE, 1 << 40
+    assert B.lib().diffattn_v1_decode(ctypes.byref(a), None) == code
+    assert B.lib().diffattn_last_error() != b""
+
+
+@host_only
+def test_v1_decode_rejects_small_workspace():
+    lib = B.lib()
+    a = _v1d_args()
+    n = lib.diffattn_v1_decode_workspace_size(ctypes.byref(a))
+    a.workspace, a.workspace_bytes = FAKE, n - 1
+    assert lib.diffattn_v1_decode(ctypes.byref(a), None) == -3
+
+
 def test_bwd_rejects_without_saves():
     a = B.BwdArgs()
     a.batch, a.seqlen, a.heads, a.head_dim, a.v_dim = 1, 128, 2, 64, 128
@@ -282,7 +329,7 @@ def test_ctypes_layout_matches_c_compiler(tmp_path):
         pytest.skip("no C compiler")
     checks = {"diffattn_fwd_args": B.FwdArgs, "diffattn_bwd_args": B.BwdArgs,
               "diffattn_v2_decode_args": B.DecodeArgs, "diffattn_v2_fwd_args": B.V2FwdArgs,
-              "diffattn_v2_bwd_args": B.V2BwdArgs}
+              "diffattn_v2_bwd_args": B.V2BwdArgs, "diffattn_v1_decode_args": B.V1DecodeArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "diffattn.h"', "int main(void) {"]
     for cname, ct in checks.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
