@@ -154,21 +154,27 @@ def _gpu_train(steps, warmup):
     vecs = [t.cuda() for t in inp["lambda_vecs"]]
     dy = inp["dy"].cuda()
     li = B.lambda_init(cfg.layer)
+    Bn, S, H, _ = x[0].shape
+    dv = x[4].shape[-1]
+    f32 = dict(dtype=torch.float32, device="cuda")
+    saves = {"lse1": torch.empty((Bn, H, S), **f32), "lse2": torch.empty((Bn, H, S), **f32),
+             "rstd": torch.empty((Bn, H, S), **f32), "o_pre": torch.empty((Bn, S, H, dv), **f32),
+             "a2": torch.empty((Bn, S, H, dv), **f32)}
+    out = torch.empty_like(x[4])
+    fa = B.fwd_args(*x, out, lambda_init=li, lambda_vecs=vecs, causal=True, eps=cfg.eps, saves=saves)
+    ba, _grads, _ws = B.bwd_args(*x, dy, saves, lambda_init=li, lambda_vecs=vecs, causal=True)
 
     def step():
-        _, saves = B.fwd(*x, lambda_init=li, lambda_vecs=vecs, causal=True, eps=cfg.eps, save=True)
-        B.bwd(*x, dy, saves, lambda_init=li, lambda_vecs=vecs, causal=True)
+        B.fwd_launch(fa)
+        B.bwd_launch(ba)
 
-    try:
-        step()
-        torch.cuda.synchronize()
-    except RuntimeError as e:
-        return {"skipped": str(e)}
-    wall, per = _time_launches(step, steps, warmup)
+    each = []
+    wall, per = _time_launches(step, steps, warmup, each)
     pairs = cfg.batch * cfg.heads * cfg.pairs
     flops = pairs * (FLOP_PER_PAIR_FWD + FLOP_PER_PAIR_BWD)
     return {"tflops": flops * steps / wall / 1e12, "ms_per_step": wall / steps * 1e3,
-            "flop_per_step": flops, "inputs": inp}
+            "event_tflops": flops / per / 1e12, "flop_per_step": flops, "inputs": inp,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
 def _gpu_decode(steps, warmup):
@@ -247,7 +253,7 @@ def _gpu_v2_train(steps, warmup):
     flops = pairs * (FLOP_PER_PAIR_V2 + FLOP_PER_PAIR_V2_BWD)
     return {"ms_per_step": wall / steps * 1e3, "tflops": flops * steps / wall / 1e12,
             "event_tflops": flops / per / 1e12, "flop_per_step": flops,
-            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3, "inputs": inp}
 
 
 def _gpu_v1_decode(steps, warmup):
@@ -328,6 +334,54 @@ def _cpu_baseline_train(inp):
                       f"rows, forward and backward; {dt:.1f} s of oracle time"}
 
 
+def _cpu_baseline_v2_prefill(inp, with_bwd=False):
+    """The float64 oracle on one (batch, pair) slice of the V2 4K workload
+    (all 4096 causal rows of both heads), forward, or forward and backward."""
+    import oracle
+    cfg = inp["cfg"]
+    sl = [inp["q"][0:1, :, 0:2], inp["k"][0:1, :, 0:1], inp["v"][0:1, :, 0:1], inp["lam"][0:1, :, 0:1]]
+    x = [t.double().numpy() for t in sl]
+    t0 = time.perf_counter()
+    oracle.v2_prefill_fwd(*x, causal=True)
+    if with_bwd:
+        gen = __import__("torch").Generator().manual_seed(2)
+        dy = __import__("torch").randn((1, cfg.seqlen, 1, cfg.head_dim), generator=gen).double().numpy()
+        oracle.v2_prefill_bwd(*x, dy, causal=True)
+    dt = time.perf_counter() - t0
+    flops = cfg.pairs * (FLOP_PER_PAIR_V2 + (FLOP_PER_PAIR_V2_BWD if with_bwd else 0))
+    what = "forward and backward" if with_bwd else "forward"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"v2_prefill_4k: 1 of {cfg.batch * cfg.q_heads // 2} (batch, pair) slices, all "
+                      f"{cfg.seqlen} causal rows, {what}; {dt:.1f} s of oracle time"}
+
+
+def _cpu_baseline_v1_decode(budget_s=8.0):
+    """The float64 oracle on whole sequences of the V1 decode workload, one
+    sequence at a time (float64 up-conversion included) until about budget_s
+    seconds have passed."""
+    import oracle
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["v1_decode"]
+    inp = workloads.make_v1_decode_inputs(cfg, batch=8)
+    li = oracle.lambda_init(cfg.layer)
+    lam = oracle.lambda_value(*[t.double().numpy() for t in inp["lambda_vecs"]], li)
+    names = ("q1", "q2", "k1_cache", "k2_cache", "v_cache")
+    done, dt = 0, 0.0
+    for b in range(8):
+        t0 = time.perf_counter()
+        x = [inp[n][b:b + 1].double().numpy() for n in names]
+        oracle.v1_decode(*x, lam, li, eps=cfg.eps)
+        dt += time.perf_counter() - t0
+        done += 1
+        if dt >= budget_s:
+            break
+    moved = done * (cfg.kv_len * cfg.heads * (2 * cfg.head_dim + cfg.v_dim) + 2 * cfg.heads * cfg.head_dim
+                    + cfg.heads * cfg.v_dim) * 2
+    return {"value": moved / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"v1_decode sequences 0-{done - 1} of {cfg.batch} (same recipe, seed 0, batch drawn 8), "
+                      f"bf16 byte count, including float64 up-conversion; {dt:.2f} s wall"}
+
+
 def _cpu_baseline_decode(sample, cfg):
     """The float64 oracle on the first 16 of the 64 sequences of the decode
     workload (same inputs as the GPU run)."""
@@ -389,7 +443,9 @@ def main(argv=None) -> int:
             print(json.dumps({"workload": "v1_decode", "gbs": r["gbs"], "event_gbs": r["event_gbs"],
                               "median_ms": r["median_ms"], "min_ms": r["min_ms"]}))
         elif args.only == "v2_train_4k":
-            print(json.dumps({"workload": "v2_train_4k", **_gpu_v2_train(args.steps, args.warmup)}))
+            r = _gpu_v2_train(args.steps, args.warmup)
+            r.pop("inputs", None)
+            print(json.dumps({"workload": "v2_train_4k", **r}))
         elif args.only == "v2_prefill_4k":
             r = _gpu_v2_prefill(args.steps, args.warmup)
             print(json.dumps({"workload": "v2_prefill_4k", "tflops": r["tflops"], "event_tflops": r["event_tflops"],
@@ -405,13 +461,19 @@ def main(argv=None) -> int:
     traffic = _traffic_from_profile("fwd_mfma_prefill_4k_pmc.md", FWD_SOURCES)
     extra = {}
     r64 = _gpu_attn("prefill_64k", max(3, args.steps // 10), 1)
-    extra["prefill_64k"] = {"metric": "fwd TFLOP/s", "value": r64["tflops"],
+    extra["prefill_64k"] = {"metric": "fwd TFLOP/s", "value": r64["tflops"], "unit": "TFLOP/s",
                             "frac_of_bf16_peak": r64["event_tflops"] / PEAK_BF16_TFLOPS,
-                            "ms_per_step": r64["wall_s"] / max(3, args.steps // 10) * 1e3}
+                            "ms_per_step": r64["wall_s"] / max(3, args.steps // 10) * 1e3,
+                            "roofline": {"bound": "mfma", "achieved": r64["event_tflops"], "peak": PEAK_BF16_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": r64["event_tflops"] / PEAK_BF16_TFLOPS,
+                                         "traffic": None}}
     tr = _gpu_train(max(3, args.steps // 10), 1)
-    extra["train_8k"] = tr if "skipped" in tr else {"metric": "fwd+bwd TFLOP/s", "value": tr["tflops"],
-                                                   "ms_per_step": tr["ms_per_step"],
-                                                   "frac_of_bf16_peak": tr["tflops"] / PEAK_BF16_TFLOPS}
+    extra["train_8k"] = {"metric": "fwd+bwd TFLOP/s", "value": tr["tflops"], "unit": "TFLOP/s",
+                         "ms_per_step": tr["ms_per_step"], "frac_of_bf16_peak": tr["tflops"] / PEAK_BF16_TFLOPS,
+                         "roofline": {"bound": "mfma", "achieved": tr["event_tflops"], "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": tr["event_tflops"] / PEAK_BF16_TFLOPS,
+                                      "traffic": None},
+                         "median_ms": tr["median_ms"], "min_ms": tr["min_ms"]}
     dec = _gpu_decode(args.steps, args.warmup)
     dec_traffic = _traffic_from_profile("decode_split_v2_decode_pmc.md", DEC_SOURCES)
     extra["v2_decode"] = {
@@ -448,14 +510,20 @@ def main(argv=None) -> int:
     extra["v2_train_4k"] = {"metric": "V2 fwd+bwd TFLOP/s", "value": v2t["tflops"], "unit": "TFLOP/s",
                             "ms_per_step": v2t["ms_per_step"], "frac_of_bf16_peak": v2t["tflops"] / PEAK_BF16_TFLOPS,
                             "config": {"workload": "v2_train_4k: the v2_prefill_4k workload, forward with training "
-                                                   "saves then backward"}}
+                                                   "saves then backward"},
+                            "roofline": {"bound": "mfma", "achieved": v2t["event_tflops"], "peak": PEAK_BF16_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": v2t["event_tflops"] / PEAK_BF16_TFLOPS,
+                                         "traffic": None},
+                            "median_ms": v2t["median_ms"], "min_ms": v2t["min_ms"]}
     cpu = None
     extra["v2_decode"]["median_ms"], extra["v2_decode"]["min_ms"] = dec["median_ms"], dec["min_ms"]
     if not args.no_cpu_baseline:
         cpu = _cpu_baseline_fwd(main_r["inputs"])
         extra["v2_decode"]["cpu_baseline"] = _cpu_baseline_decode(dec["sample"], dec["cfg"])
-        if "inputs" in tr:
-            extra["train_8k"]["cpu_baseline"] = _cpu_baseline_train(tr["inputs"])
+        extra["train_8k"]["cpu_baseline"] = _cpu_baseline_train(tr["inputs"])
+        extra["v2_prefill_4k"]["cpu_baseline"] = _cpu_baseline_v2_prefill(v2p["inputs"])
+        extra["v2_train_4k"]["cpu_baseline"] = _cpu_baseline_v2_prefill(v2t["inputs"], with_bwd=True)
+        extra["v1_decode"]["cpu_baseline"] = _cpu_baseline_v1_decode()
     line = {
         "metric": METRIC,
         "value": main_r["tflops"],

@@ -272,9 +272,10 @@ def fwd(q1, k1, q2, k2, v, *, lambda_init: float, lambda_vecs=None, lambda_fixed
 
 
 def fwd_args(q1, k1, q2, k2, v, out, *, lambda_init, lambda_vecs=None, lambda_fixed=0.8,
-             causal=True, norm=True, eps=1e-5, softmax_scale=0.0):
+             causal=True, norm=True, eps=1e-5, softmax_scale=0.0, saves=None):
     """Prebuilt FwdArgs for repeated launches (benchmarks): call
-    fwd_launch(args) to run it on the current stream."""
+    fwd_launch(args) to run it on the current stream.  saves: optional dict of
+    the five float32 training-save tensors (see fwd)."""
     _check_attn(q1, k1, q2, k2, v, out, lambda_vecs)
     B, S, H, d = q1.shape
     a = FwdArgs()
@@ -285,6 +286,14 @@ def fwd_args(q1, k1, q2, k2, v, out, *, lambda_init, lambda_vecs=None, lambda_fi
     _lambda_fields(a, lambda_vecs, lambda_fixed)
     a.lambda_init, a.softmax_scale, a.eps = float(lambda_init), float(softmax_scale), float(eps)
     a.out = _ptr(out)
+    if saves is not None:
+        dv = v.shape[-1]
+        for k, shape in (("lse1", (B, H, S)), ("lse2", (B, H, S)), ("rstd", (B, H, S)),
+                         ("o_pre", (B, S, H, dv)), ("a2", (B, S, H, dv))):
+            t = saves[k]
+            _require(tuple(t.shape) == shape and t.is_contiguous(), f"saved {k} must be contiguous {shape}")
+            _check_dev(((k, t),), dtype=torch.float32, device=q1.device)
+        a.lse1, a.lse2, a.rstd, a.o_pre, a.a2 = (_ptr(saves[k]) for k in ("lse1", "lse2", "rstd", "o_pre", "a2"))
     return a
 
 
@@ -292,13 +301,10 @@ def fwd_launch(args: FwdArgs) -> None:
     _check(lib().diffattn_fwd(ctypes.byref(args), _stream()), "diffattn_fwd")
 
 
-def bwd(q1, k1, q2, k2, v, dout, saves, *, lambda_init: float, lambda_vecs=None,
-        lambda_fixed: float = 0.8, causal: bool = True, norm: bool = True,
-        softmax_scale: float = 0.0):
-    """Gradients through diffattn_bwd for the forward run with save=True.
-
-    Returns a dict: dq1, dk1, dq2, dk2, dv (activation dtype), dlambda
-    (float32 [1]) and, with lambda_vecs, dlq1, dlk1, dlq2, dlk2."""
+def bwd_args(q1, k1, q2, k2, v, dout, saves, *, lambda_init: float, lambda_vecs=None,
+             lambda_fixed: float = 0.8, causal: bool = True, norm: bool = True, softmax_scale: float = 0.0):
+    """Prebuilt BwdArgs with its outputs and workspace allocated: returns
+    (args, grads, workspace); bwd_launch(args) runs it on the current stream."""
     _check_attn(q1, k1, q2, k2, v, dout, lambda_vecs)
     B, S, H, d = q1.shape
     dv_w0 = v.shape[-1]
@@ -329,7 +335,24 @@ def bwd(q1, k1, q2, k2, v, dout, saves, *, lambda_init: float, lambda_vecs=None,
     nbytes = lib().diffattn_bwd_workspace_size(ctypes.byref(a))
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=v.device)
     a.workspace, a.workspace_bytes = _ptr(ws), nbytes
-    _check(lib().diffattn_bwd(ctypes.byref(a), _stream()), "diffattn_bwd")
+    return a, g, ws
+
+
+def bwd_launch(args: BwdArgs) -> None:
+    _check(lib().diffattn_bwd(ctypes.byref(args), _stream()), "diffattn_bwd")
+
+
+def bwd(q1, k1, q2, k2, v, dout, saves, *, lambda_init: float, lambda_vecs=None,
+        lambda_fixed: float = 0.8, causal: bool = True, norm: bool = True,
+        softmax_scale: float = 0.0):
+    """Gradients through diffattn_bwd for the forward run with save=True.
+
+    Returns a dict: dq1, dk1, dq2, dk2, dv (activation dtype), dlambda
+    (float32 [1]) and, with lambda_vecs, dlq1, dlk1, dlq2, dlk2."""
+    a, g, ws = bwd_args(q1, k1, q2, k2, v, dout, saves, lambda_init=lambda_init, lambda_vecs=lambda_vecs,
+                        lambda_fixed=lambda_fixed, causal=causal, norm=norm, softmax_scale=softmax_scale)
+    bwd_launch(a)
+    del ws  # the stream-ordered caching allocator keeps it alive until the kernels have run
     return g
 
 
