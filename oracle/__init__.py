@@ -14,6 +14,9 @@ from .diffattn_oracle import (  # noqa: F401
     v2_prefill_fwd,
     v2_prefill_bwd,
     v1_decode,
+    fp8_quantize_rows,
+    fp8_decode,
+    diff_attn_fwd_fp8_logits,
     sigmoid,
 )
 from .brute import brute_diff_attn_fwd, brute_v2_decode, brute_v2_prefill_fwd  # noqa: F401

@@ -52,6 +52,9 @@ __all__ = [
     "v2_prefill_fwd",
     "v2_prefill_bwd",
     "v1_decode",
+    "fp8_quantize_rows",
+    "fp8_decode",
+    "diff_attn_fwd_fp8_logits",
 ]
 
 
@@ -406,3 +409,95 @@ def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lam_init: float, 
                 o = o / np.sqrt(np.mean(o * o) + eps) * (1.0 - lam_init)
             out[b, h] = o
     return out
+
+
+# ---------------------------------------------------------------------------
+# Low-bit attention logits ([N]'s quantisation discussion and [V2]'s outlook
+# name absmax dynamic post-training quantisation of the attention logits to
+# 8/6/4 bits and a low-bit FlashAttention as the kernel it enables).  The
+# reading here: Q1, K1, Q2, K2 are quantised per row (one token of one head) to
+# fp8 e4m3 with an absmax scale rounded up to a power of two, and the score
+# products use the dequantised values; everything after the scores is the
+# ordinary forward.
+
+E4M3_MAX = 448.0
+
+
+def _e4m3_table():
+    t = np.empty(256)
+    for c in range(256):
+        sgn = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            t[c] = np.nan
+        elif e == 0:
+            t[c] = sgn * m * 2.0 ** -9
+        else:
+            t[c] = sgn * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+_E4M3 = _e4m3_table()
+
+
+def fp8_decode(codes) -> np.ndarray:
+    """Values of fp8 e4m3 codes (uint8)."""
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def _round_half_even(x):
+    return np.round(x)   # numpy rounds halves to even
+
+
+def _e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Round float values with |v| <= 448 to the nearest e4m3 code, ties to the
+    even code (OCP 8-bit floating point, E4M3: 3 mantissa bits, exponent bias
+    7, subnormal step 2^-9, largest finite 448)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the e4m3 range")
+    with np.errstate(divide="ignore"):
+        ex = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ex = np.maximum(ex, -6.0)                      # subnormals share the 2^-6 binade's step
+    ulp = 2.0 ** (ex - 3)
+    q = _round_half_even(a / ulp) * ulp            # exact: a / ulp is a float with few bits
+    # encode q
+    codes = np.zeros(a.shape, dtype=np.uint8)
+    nz = q > 0
+    e_q = np.floor(np.log2(np.where(nz, q, 1.0)))
+    sub = nz & (e_q < -6)
+    norm = nz & ~sub
+    codes[sub] = (q[sub] / 2.0 ** -9).astype(np.uint8)
+    en = (e_q[norm] + 7).astype(np.int64)
+    mn = np.round((q[norm] / 2.0 ** e_q[norm] - 1.0) * 8).astype(np.int64)
+    codes[norm] = (en << 3 | mn).astype(np.uint8)
+    codes |= np.where(np.signbit(v) & (q > 0), 0x80, 0).astype(np.uint8)
+    return codes
+
+
+def fp8_quantize_rows(x):
+    """Per-row (last axis) absmax quantisation to fp8 e4m3 with a power-of-two
+    scale: e is the smallest integer with max|x_row| * 2^-e <= 448 (clamped to
+    [-120, 120]; 0 for an all-zero row), codes = RNE_e4m3(x * 2^-e).
+    Returns (codes uint8 with x's shape, e int32 with the row shape); the
+    dequantised row is fp8_decode(codes) * 2^e."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=-1)
+    m, E = np.frexp(amax)                    # amax = m 2^E, m in [0.5, 1)
+    mant, E = 2.0 * m, E - 1                 # amax = mant 2^E, mant in [1, 2)
+    e = E - 8 + (mant > 1.75)
+    e = np.where(amax > 0, np.clip(e, -120, 120), 0).astype(np.int32)
+    codes = _e4m3_encode(x * 2.0 ** (-e[..., None].astype(np.float64)))
+    return codes, e
+
+
+def diff_attn_fwd_fp8_logits(q1, k1, q2, k2, v, lam: float, lam_init: float, **kw):
+    """diff_attn_fwd with Q1, K1, Q2, K2 replaced by their per-row fp8 e4m3
+    quantisations (fp8_quantize_rows, dequantised); V and everything after the
+    scores as in diff_attn_fwd."""
+    deq = []
+    for t in (q1, k1, q2, k2):
+        c, e = fp8_quantize_rows(t)
+        deq.append(fp8_decode(c) * 2.0 ** e[..., None].astype(np.float64))
+    return diff_attn_fwd(deq[0], deq[1], deq[2], deq[3], v, lam, lam_init, **kw)
