@@ -472,7 +472,9 @@ def _e4m3_encode(v: np.ndarray) -> np.ndarray:
     en = (e_q[norm] + 7).astype(np.int64)
     mn = np.round((q[norm] / 2.0 ** e_q[norm] - 1.0) * 8).astype(np.int64)
     codes[norm] = (en << 3 | mn).astype(np.uint8)
-    codes |= np.where(np.signbit(v) & (q > 0), 0x80, 0).astype(np.uint8)
+    # The format has a signed zero: a negative value keeps its sign bit even
+    # when it rounds to zero.
+    codes |= np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
     return codes
 
 

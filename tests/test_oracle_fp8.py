@@ -31,6 +31,15 @@ def test_ties_and_subnormals_round_to_even():
     np.testing.assert_array_equal(fp8_decode(codes[0]), [448.0, 8.0, 10.0, 0.0, 2.0 ** -8, 2.0 ** -8, -16.0, 0.0])
 
 
+def test_signed_zero():
+    """Negative values that round to zero keep the sign bit (e4m3 has -0,
+    code 0x80), as torch's cast does."""
+    row = np.array([[448.0, -2.0 ** -11, 2.0 ** -11, -0.0, 0.0, -2.0 ** -10]])
+    codes, _ = fp8_quantize_rows(row)
+    np.testing.assert_array_equal(codes[0], _torch_codes(row[0]))
+    np.testing.assert_array_equal(codes[0, 1:], [0x80, 0x00, 0x80, 0x00, 0x80])
+
+
 def test_absmax_rule_and_error_bound():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((500, 64)) * np.exp(rng.uniform(-8, 8, (500, 1)))
