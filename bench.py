@@ -219,6 +219,28 @@ def _gpu_v2_prefill(steps, warmup):
             "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
+def _gpu_fp8(steps, warmup):
+    """The 4K forward with fp8 e4m3 attention logits (quantisation of Q1, K1,
+    Q2, K2 included in every step)."""
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["prefill_4k"]
+    inp = workloads.make_attn_inputs(cfg)
+    x = [inp[k].cuda() for k in ("q1", "k1", "q2", "k2", "v")]
+    vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    out = torch.empty_like(x[4])
+    args = B.fwd_args(*x, out, lambda_init=B.lambda_init(cfg.layer), lambda_vecs=vecs, causal=cfg.causal,
+                      norm=True, eps=cfg.eps)
+    ws = B.fwd_fp8_workspace(args, x[0].device)
+    each = []
+    wall, per = _time_launches(lambda: B.fwd_fp8_launch(args, ws), steps, warmup, each)
+    flops = cfg.batch * cfg.heads * cfg.pairs * FLOP_PER_PAIR_FWD
+    return {"wall_s": wall, "event_s_per_launch": per, "flop_per_step": flops,
+            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+
+
 def _gpu_v2_train(steps, warmup):
     """One DIFF V2 training step at the 4K V2 workload: forward with the
     training saves, then the backward, on random upstream gradients."""
@@ -404,7 +426,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k",
-                                       "v2_train_4k", "v1_decode"],
+                                       "v2_train_4k", "v1_decode", "prefill_4k_fp8"],
                     default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -438,6 +460,9 @@ def main(argv=None) -> int:
             r = _gpu_train(args.steps, args.warmup)
             r.pop("inputs", None)
             print(json.dumps({"workload": "train_8k", **r}))
+        elif args.only == "prefill_4k_fp8":
+            r = _gpu_fp8(args.steps, args.warmup)
+            print(json.dumps({"workload": "prefill_4k_fp8", **r}))
         elif args.only == "v1_decode":
             r = _gpu_v1_decode(args.steps, args.warmup)
             print(json.dumps({"workload": "v1_decode", "gbs": r["gbs"], "event_gbs": r["event_gbs"],
@@ -494,6 +519,17 @@ def main(argv=None) -> int:
                      "unit": "TFLOP/s", "frac": v2p["event_tflops"] / PEAK_BF16_TFLOPS,
                      "traffic": _traffic_from_profile("fwd_v2_v2_prefill_4k_pmc.md", V2P_SOURCES)},
         "median_ms": v2p["median_ms"], "min_ms": v2p["min_ms"],
+    }
+    f8 = _gpu_fp8(args.steps, args.warmup)
+    extra["prefill_4k_fp8"] = {
+        "metric": "fwd TFLOP/s with fp8 e4m3 logits", "value": f8["tflops"], "unit": "TFLOP/s",
+        "ms_per_step": f8["wall_s"] / args.steps * 1e3,
+        "config": {"workload": "prefill_4k with Q1, K1, Q2, K2 quantised per row to fp8 e4m3 (power-of-two absmax "
+                               "scale) inside every step; score products on scaled fp8 matrix instructions"},
+        "roofline": {"bound": "mfma", "achieved": f8["event_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": f8["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "note": "algorithmic 768 flop per pair against the bf16/fp16 peak (the PV product stays fp16)"},
+        "median_ms": f8["median_ms"], "min_ms": f8["min_ms"],
     }
     v1d = _gpu_v1_decode(args.steps, args.warmup)
     extra["v1_decode"] = {

@@ -120,6 +120,8 @@ class V2BwdArgs(ctypes.Structure):
 SIGNATURES = {
     "diffattn_fwd": (ctypes.c_int, [ctypes.POINTER(FwdArgs), c_vp]),
     "diffattn_bwd": (ctypes.c_int, [ctypes.POINTER(BwdArgs), c_vp]),
+    "diffattn_fwd_fp8": (ctypes.c_int, [ctypes.POINTER(FwdArgs), c_vp, c_sz, c_vp]),
+    "diffattn_fwd_fp8_workspace_size": (c_sz, [ctypes.POINTER(FwdArgs)]),
     "diffattn_bwd_workspace_size": (c_sz, [ctypes.POINTER(BwdArgs)]),
     "diffattn_v2_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v2_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeArgs)]),
@@ -299,6 +301,35 @@ def fwd_args(q1, k1, q2, k2, v, out, *, lambda_init, lambda_vecs=None, lambda_fi
 
 def fwd_launch(args: FwdArgs) -> None:
     _check(lib().diffattn_fwd(ctypes.byref(args), _stream()), "diffattn_fwd")
+
+
+def fwd_fp8_workspace(args: FwdArgs, device) -> torch.Tensor:
+    """Workspace tensor for diffattn_fwd_fp8 with these arguments."""
+    nbytes = int(lib().diffattn_fwd_fp8_workspace_size(ctypes.byref(args)))
+    _require(nbytes > 0, "invalid arguments for the fp8-logit forward: " + lib().diffattn_last_error().decode())
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def fwd_fp8_launch(args: FwdArgs, ws: torch.Tensor) -> None:
+    _check(lib().diffattn_fwd_fp8(ctypes.byref(args), _ptr(ws), ws.numel(), _stream()), "diffattn_fwd_fp8")
+
+
+def fwd_fp8(q1, k1, q2, k2, v, *, lambda_init: float, lambda_vecs=None, lambda_fixed: float = 0.8,
+            causal: bool = True, norm: bool = True, eps: float = 1e-5, softmax_scale: float = 0.0, out=None,
+            return_workspace: bool = False):
+    """Forward with fp8 e4m3 attention logits through diffattn_fwd_fp8 (per-row
+    power-of-two absmax quantisation of Q1, K1, Q2, K2).  Returns out, or
+    (out, workspace) with return_workspace=True: the workspace then holds the
+    codes (uint8 [4, B, H, S, d]: Q1, K1, Q2, K2) followed, at the next
+    256-byte boundary, by the exponents (int32 [4, B, H, S])."""
+    B, S, H, d = q1.shape
+    if out is None:
+        out = torch.empty((B, S, H, v.shape[-1]), dtype=v.dtype, device=v.device)
+    a = fwd_args(q1, k1, q2, k2, v, out, lambda_init=lambda_init, lambda_vecs=lambda_vecs,
+                 lambda_fixed=lambda_fixed, causal=causal, norm=norm, eps=eps, softmax_scale=softmax_scale)
+    ws = fwd_fp8_workspace(a, v.device)
+    fwd_fp8_launch(a, ws)
+    return (out, ws) if return_workspace else out
 
 
 def bwd_args(q1, k1, q2, k2, v, dout, saves, *, lambda_init: float, lambda_vecs=None,

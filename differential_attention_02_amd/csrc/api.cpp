@@ -151,6 +151,66 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
   return hip_status(diffattn::launch_fwd_generic(p, a->dtype, a->head_dim, a->v_dim, st), "forward launch");
 }
 
+static int check_fwd_fp8(const diffattn_fwd_args *a) {
+  int rc = check_common(a->batch, a->seqlen, a->heads, a->head_dim, a->v_dim, a->dtype, a->q1, a->k1,
+                        a->q2, a->k2, a->v, a->q_stride, a->k_stride, a->v_stride, a->lq1, a->lk1,
+                        a->lq2, a->lk2, a->lambda_dim, a->lambda_fixed, a->lambda_init, a->softmax_scale);
+  if (rc) return rc;
+  if (!a->out) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+  if (!strides_ok(a->o_stride, 3)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "out strides must be positive");
+  if (!(a->eps >= 0.f) || !std::isfinite(a->eps)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (a->lse1 || a->lse2 || a->rstd || a->o_pre || a->a2)
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "the fp8-logit forward has no training saves");
+  if (a->dtype != DIFFATTN_BF16 || a->head_dim != 64 || a->v_dim != 128)
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "the fp8-logit forward is built for bf16 with head_dim 64, v_dim 128");
+  const void *ptrs[] = {a->q1, a->k1, a->q2, a->k2, a->v, a->out};
+  const int64_t *str[] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
+  if (!fused_layout_ok(ptrs, 6, str, 4))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "fp8-logit forward needs 16-byte aligned pointers and strides that are multiples of 8");
+  const int64_t vspan = (int64_t)a->seqlen * a->v_stride[1] * 2;
+  const int64_t cspan = (int64_t)a->batch * a->heads * a->seqlen * 64;
+  if (vspan >= ((int64_t)1 << 31) || cspan >= ((int64_t)1 << 31))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "fp8-logit forward needs V and code slices below 2^31 bytes");
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_fwd_fp8_workspace_size(const diffattn_fwd_args *a) {
+  std::string keep = g_last_error;
+  const int rc = (!a || a->batch <= 0 || a->seqlen <= 0) ? DIFFATTN_ERR_INVALID_ARGUMENT : check_fwd_fp8(a);
+  g_last_error = keep;
+  if (rc) return 0;
+  return diffattn::fwd_fp8_workspace_bytes(a->batch, a->seqlen, a->heads);
+}
+
+int diffattn_fwd_fp8(const diffattn_fwd_args *a, void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0 || a->seqlen < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0");
+  if (a->batch == 0 || a->seqlen == 0) return DIFFATTN_OK;
+  int rc = check_fwd_fp8(a);
+  if (rc) return rc;
+  const size_t need = diffattn::fwd_fp8_workspace_bytes(a->batch, a->seqlen, a->heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(DIFFATTN_ERR_WORKSPACE, "fp8-logit forward needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  diffattn::FwdParams p{};
+  p.q1 = a->q1; p.k1 = a->k1; p.q2 = a->q2; p.k2 = a->k2; p.v = a->v;
+  p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
+  p.ks_b = a->k_stride[0]; p.ks_s = a->k_stride[1]; p.ks_h = a->k_stride[2];
+  p.vs_b = a->v_stride[0]; p.vs_s = a->v_stride[1]; p.vs_h = a->v_stride[2];
+  p.os_b = a->o_stride[0]; p.os_s = a->o_stride[1]; p.os_h = a->o_stride[2];
+  p.out = a->out;
+  p.B = a->batch; p.S = a->seqlen; p.H = a->heads;
+  p.causal = a->causal != 0; p.norm = a->norm != 0;
+  p.lq1 = a->lq1; p.lk1 = a->lk1; p.lq2 = a->lq2; p.lk2 = a->lk2;
+  p.lambda_dim = a->lambda_dim; p.lambda_fixed = a->lambda_fixed; p.lambda_init = a->lambda_init;
+  p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
+  p.eps = a->eps;
+  p.lambda_out = a->lambda_out;
+  return hip_status(diffattn::launch_fwd_fp8(p, workspace, static_cast<hipStream_t>(stream)), "fp8-logit forward launch");
+}
+
 static int check_bwd(const diffattn_bwd_args *a) {
   if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
   int rc = check_common(a->batch, a->seqlen, a->heads, a->head_dim, a->v_dim, a->dtype, a->q1, a->k1,

@@ -106,6 +106,10 @@ struct V2BwdParams {
 hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipStream_t st);
 // Fused bf16 matrix-core forward, d = 64, dv = 128.
 hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st);
+// The same forward with fp8 e4m3 score operands (per-row power-of-two absmax
+// scales); the workspace holds the codes and exponents.
+size_t fwd_fp8_workspace_bytes(int B, int S, int H);
+hipError_t launch_fwd_fp8(const FwdParams &p, void *workspace, hipStream_t st);
 
 hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st);
 size_t v2_bwd_workspace_bytes(int B, int S, int Hq, int Hkv);

@@ -27,6 +27,7 @@
  *     makes lambda per token and per head].
  *   - DIFF V2 prefill backward: its gradients by the chain rule.
  *   - DIFF V1 decode: the V1 operator for one new token over a K1/K2/V cache.
+ *   - DIFF V1 forward with fp8 e4m3 attention logits (per-row absmax scaling).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a device pointer owned by the caller (for example
@@ -287,6 +288,23 @@ typedef struct diffattn_v1_decode_args {
 
 /* Forward pass. Returns DIFFATTN_OK or a negative status. */
 int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
+
+/*
+ * Forward pass with fp8 attention logits: Q1, K1, Q2, K2 are quantised per row
+ * (one token of one head) to fp8 e4m3 with a power-of-two absmax scale (e the
+ * smallest integer with max|row| 2^-e <= 448, clamped to [-120, 120]; codes
+ * rounded to nearest even), and the score products use the dequantised
+ * values; everything else is diffattn_fwd [the low-bit attention-logit
+ * quantisation and "low-bit FlashAttention" discussed on the V2 page's outlook
+ * section and the news write-up].  Same arguments as diffattn_fwd without
+ * training saves; supported: bf16 with head_dim 64, v_dim 128.  workspace: at
+ * least diffattn_fwd_fp8_workspace_size() bytes, 256-byte aligned (it receives
+ * the codes and exponents).
+ */
+int diffattn_fwd_fp8(const diffattn_fwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes diffattn_fwd_fp8 needs for these arguments (0 if invalid). */
+size_t diffattn_fwd_fp8_workspace_size(const diffattn_fwd_args *args);
 
 /* Backward pass. Returns DIFFATTN_OK or a negative status. */
 int diffattn_bwd(const diffattn_bwd_args *args, void *stream);

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -100,6 +100,34 @@ def test_fwd_rejects_bad_strides():
     a = _fwd_args()
     a.k_stride = (ctypes.c_int64 * 3)(128 * 2 * 64, 2 * 64 + 4, 64)   # rows not 16-byte aligned
     assert _fwd(a) == -2
+
+
+@host_only
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", B.F32, -2), ("head_dim", 32, -2), ("lse1", FAKE, -1), ("q1", FAKE + 4, -2), ("out", None, -1),
+])
+def test_fwd_fp8_rejects(field, value, code):
+    a = _fwd_args(**{field: value})
+    if field == "lse1":   # all five saves: a valid training request, which this entry point refuses
+        a.lse2 = a.rstd = a.o_pre = a.a2 = FAKE
+        code = -2
+    assert B.lib().diffattn_fwd_fp8(ctypes.byref(a), FAKE, 1 << 40, None) == code
+    assert B.lib().diffattn_last_error() != b""
+
+
+def test_fwd_fp8_workspace_size():
+    a = _fwd_args()
+    n = B.lib().diffattn_fwd_fp8_workspace_size(ctypes.byref(a))
+    rows = 1 * 2 * 128
+    assert n >= 4 * rows * 64 + 4 * rows * 4
+
+
+@host_only
+def test_fwd_fp8_rejects_small_workspace():
+    a = _fwd_args()
+    n = B.lib().diffattn_fwd_fp8_workspace_size(ctypes.byref(a))
+    assert B.lib().diffattn_fwd_fp8(ctypes.byref(a), FAKE, n - 1, None) == -3
+    assert B.lib().diffattn_fwd_fp8(ctypes.byref(a), FAKE + 16, n, None) == -1
 
 
 @host_only
