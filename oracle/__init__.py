@@ -13,6 +13,7 @@ from .diffattn_oracle import (  # noqa: F401
     v2_decode,
     v2_prefill_fwd,
     v2_prefill_bwd,
+    v2_prefill_fwd_block_sparse,
     v1_decode,
     fp8_quantize_rows,
     fp8_decode,

@@ -52,6 +52,7 @@ __all__ = [
     "v2_prefill_fwd",
     "v2_prefill_bwd",
     "v1_decode",
+    "v2_prefill_fwd_block_sparse",
     "fp8_quantize_rows",
     "fp8_decode",
     "diff_attn_fwd_fp8_logits",
@@ -408,6 +409,49 @@ def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lam_init: float, 
             if norm:
                 o = o / np.sqrt(np.mean(o * o) + eps) * (1.0 - lam_init)
             out[b, h] = o
+    return out
+
+
+def v2_prefill_fwd_block_sparse(q, k, v, lam, block_mask, *, q_block: int = 128, k_block: int = 64,
+                                causal: bool = True, scale: float | None = None):
+    """DIFF V2 forward restricted to selected key blocks, one selection per
+    even/odd head pair ([V2] "practical considerations": DIFF V2 works with
+    sparse attention frameworks by selecting blocks per head pair inside a GQA
+    group; [G]'s neighbouring glossary entry: sparse attention scores only a
+    fixed subset of token pairs and sets every other weight to 0).
+
+    block_mask: bool [B, Hq/2, ceil(S / q_block), ceil(S / k_block)]; query i
+    of pair p may attend key j iff block_mask[b, p, i // q_block, j // k_block]
+    (and j <= i when causal).  Both heads of the pair use the pair's
+    selection; each head's softmax runs over its allowed keys only.  A row
+    with no allowed key gives zeros.  Returns [B, S, Hq/2, D].
+    """
+    q, k, v = map(_f64, (q, k, v))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv or (Hq // Hkv) % 2:
+        raise ValueError("each even/odd query-head pair must share a KV head")
+    group = Hq // Hkv
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lam = np.broadcast_to(_f64(lam), (B, S, Hq // 2))
+    block_mask = np.asarray(block_mask, dtype=bool)
+    rows = np.arange(S)
+    out = np.zeros((B, S, Hq // 2, D))
+    for b in range(B):
+        for p in range(Hq // 2):
+            allowed = block_mask[b, p][rows[:, None] // q_block, rows[None, :] // k_block]
+            if causal:
+                allowed &= rows[None, :] <= rows[:, None]
+            live = allowed.any(axis=1)
+            attn = []
+            for t in (2 * p, 2 * p + 1):
+                j = t // group
+                sc = np.where(allowed, (q[b, :, t] @ k[b, :, j].T) * s, -np.inf)
+                m = np.where(live, sc.max(axis=1), 0.0)
+                e = np.where(allowed, np.exp(sc - m[:, None]), 0.0)
+                den = np.where(live, e.sum(axis=1), 1.0)
+                attn.append((e / den[:, None]) @ v[b, :, j])
+            out[b, :, p] = attn[0] - sigmoid(lam[b, :, p])[:, None] * attn[1]
     return out
 
 
