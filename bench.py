@@ -15,7 +15,9 @@ flop per unmasked (query, key, pair of query heads), two QK^T and two PV
 products of width 128), and its training step (forward with saves + backward,
 2048 more flop per unmasked (query, key, pair): recomputed QK^T of both heads,
 one shared dP, one merged dV, dQ and dK of both heads), and the DIFF V1 decode
-over a K1/K2/V cache (GB/s of cache + query + output bytes).
+over a K1/K2/V cache (GB/s of cache + query + output bytes), and the
+block-sparse DIFF V2 forward over a seeded selection of 16 64-key tiles per
+128-row query tile (1024 flop per selected (query, key, pair)).
 Each timing: W untimed launches, then exactly K launches between two
 synchronisations; HIP events on the launch stream give the average launch
 duration used for the roofline.  "cpu_baseline" times the float64 oracle on a
@@ -219,6 +221,37 @@ def _gpu_v2_prefill(steps, warmup):
             "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
+def _sparse_selection(cfg):
+    """The block-sparse workload's seeded selection (seed 0): per (batch, pair,
+    128-row query tile) 16 of the 64-key tiles: the first, the four ending at
+    the tile's last row, and 11 drawn at random from the earlier ones."""
+    from differential_attention_02_amd import workloads
+    mask = workloads.make_block_selection(cfg.batch, cfg.q_heads // 2, cfg.seqlen, budget=16, sink=1, local=4, seed=0)
+    return mask, workloads.block_pairs(mask, cfg.seqlen)
+
+
+def _gpu_v2_sparse(steps, warmup):
+    """The V2 4K forward over the seeded block selection; flop counted over
+    the selected (query, key, pair) triples only."""
+    import torch
+    from differential_attention_02_amd import binding as B
+    from differential_attention_02_amd import workloads
+    cfg = workloads.CONFIGS["v2_prefill_4k"]
+    inp = workloads.make_v2_prefill_inputs(cfg)
+    mask, pairs = _sparse_selection(cfg)
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    idx, cnt = B.v2_block_lists(mask.cuda())
+    out = torch.empty((cfg.batch, cfg.seqlen, cfg.q_heads // 2, cfg.head_dim), dtype=q.dtype, device="cuda")
+    args = B.v2_fwd_args(q, k, v, lam, out, causal=cfg.causal)
+    each = []
+    wall, per = _time_launches(lambda: B.v2_fwd_sparse_launch(args, idx, cnt), steps, warmup, each)
+    flops = pairs * FLOP_PER_PAIR_V2
+    return {"wall_s": wall, "event_s_per_launch": per, "flop_per_step": flops, "density": pairs / (
+            cfg.batch * (cfg.q_heads // 2) * cfg.pairs), "tflops": flops * steps / wall / 1e12,
+            "event_tflops": flops / per / 1e12, "inputs": inp, "mask": mask,
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+
+
 def _gpu_fp8(steps, warmup):
     """The 4K forward with fp8 e4m3 attention logits (quantisation of Q1, K1,
     Q2, K2 included in every step)."""
@@ -377,6 +410,24 @@ def _cpu_baseline_v2_prefill(inp, with_bwd=False):
                       f"{cfg.seqlen} causal rows, {what}; {dt:.1f} s of oracle time"}
 
 
+def _cpu_baseline_v2_sparse(inp, mask):
+    """The float64 oracle's block-sparse forward on one (batch, pair) slice of
+    the block-sparse workload (all 4096 rows of both heads)."""
+    import oracle
+    from differential_attention_02_amd import workloads
+    cfg = inp["cfg"]
+    sl = [inp["q"][0:1, :, 0:2], inp["k"][0:1, :, 0:1], inp["v"][0:1, :, 0:1], inp["lam"][0:1, :, 0:1]]
+    x = [t.double().numpy() for t in sl]
+    m = mask[0:1, 0:1]
+    t0 = time.perf_counter()
+    oracle.v2_prefill_fwd_block_sparse(*x, m.numpy(), causal=True)
+    dt = time.perf_counter() - t0
+    flops = workloads.block_pairs(m, cfg.seqlen) * FLOP_PER_PAIR_V2
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"v2_sparse_4k: 1 of {cfg.batch * cfg.q_heads // 2} (batch, pair) slices, all "
+                      f"{cfg.seqlen} rows, selected pairs only; {dt:.1f} s of oracle time"}
+
+
 def _cpu_baseline_v1_decode(budget_s=8.0):
     """The float64 oracle on whole sequences of the V1 decode workload, one
     sequence at a time (float64 up-conversion included) until about budget_s
@@ -426,7 +477,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k",
-                                       "v2_train_4k", "v1_decode", "prefill_4k_fp8"],
+                                       "v2_train_4k", "v1_decode", "prefill_4k_fp8", "v2_sparse_4k"],
                     default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -471,6 +522,10 @@ def main(argv=None) -> int:
             r = _gpu_v2_train(args.steps, args.warmup)
             r.pop("inputs", None)
             print(json.dumps({"workload": "v2_train_4k", **r}))
+        elif args.only == "v2_sparse_4k":
+            r = _gpu_v2_sparse(args.steps, args.warmup)
+            print(json.dumps({"workload": "v2_sparse_4k", "tflops": r["tflops"], "event_tflops": r["event_tflops"],
+                              "density": r["density"], "median_ms": r["median_ms"], "min_ms": r["min_ms"]}))
         elif args.only == "v2_prefill_4k":
             r = _gpu_v2_prefill(args.steps, args.warmup)
             print(json.dumps({"workload": "v2_prefill_4k", "tflops": r["tflops"], "event_tflops": r["event_tflops"],
@@ -520,6 +575,19 @@ def main(argv=None) -> int:
                      "traffic": _traffic_from_profile("fwd_v2_v2_prefill_4k_pmc.md", V2P_SOURCES)},
         "median_ms": v2p["median_ms"], "min_ms": v2p["min_ms"],
     }
+    v2s = _gpu_v2_sparse(args.steps, args.warmup)
+    extra["v2_sparse_4k"] = {
+        "metric": "block-sparse V2 prefill fwd TFLOP/s", "value": v2s["tflops"], "unit": "TFLOP/s",
+        "ms_per_step": v2s["wall_s"] / args.steps * 1e3,
+        "config": {"workload": "v2_sparse_4k: the v2_prefill_4k workload with one key-block selection per "
+                               "(batch, head pair, 128-row query tile): 16 of the 64-key tiles (the first, the "
+                               "four ending at the tile's last row, 11 random earlier ones; seed 0)",
+                   "density": v2s["density"]},
+        "roofline": {"bound": "mfma", "achieved": v2s["event_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": v2s["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "note": "1024 flop per selected (query, key, pair) triple"},
+        "median_ms": v2s["median_ms"], "min_ms": v2s["min_ms"],
+    }
     f8 = _gpu_fp8(args.steps, args.warmup)
     extra["prefill_4k_fp8"] = {
         "metric": "fwd TFLOP/s with fp8 e4m3 logits", "value": f8["tflops"], "unit": "TFLOP/s",
@@ -560,6 +628,7 @@ def main(argv=None) -> int:
         extra["v2_prefill_4k"]["cpu_baseline"] = _cpu_baseline_v2_prefill(v2p["inputs"])
         extra["v2_train_4k"]["cpu_baseline"] = _cpu_baseline_v2_prefill(v2t["inputs"], with_bwd=True)
         extra["v1_decode"]["cpu_baseline"] = _cpu_baseline_v1_decode()
+        extra["v2_sparse_4k"]["cpu_baseline"] = _cpu_baseline_v2_sparse(v2s["inputs"], v2s["mask"])
     line = {
         "metric": METRIC,
         "value": main_r["tflops"],

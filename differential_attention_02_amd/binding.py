@@ -129,6 +129,7 @@ SIGNATURES = {
     "diffattn_v1_decode_workspace_size": (c_sz, [ctypes.POINTER(V1DecodeArgs)]),
     "diffattn_v2_fwd": (ctypes.c_int, [ctypes.POINTER(V2FwdArgs), c_vp]),
     "diffattn_v2_bwd": (ctypes.c_int, [ctypes.POINTER(V2BwdArgs), c_vp]),
+    "diffattn_v2_fwd_sparse": (ctypes.c_int, [ctypes.POINTER(V2FwdArgs), c_vp, c_vp, c_i32, c_vp]),
     "diffattn_v2_bwd_workspace_size": (c_sz, [ctypes.POINTER(V2BwdArgs)]),
     "diffattn_lambda_init": (c_f32, [ctypes.c_int]),
     "diffattn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -611,4 +612,44 @@ def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, *, lambda_init: float, lambda
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q1.device)
     a.workspace, a.workspace_bytes = _ptr(ws), nbytes
     v1_decode_launch(a)
+    return out
+
+
+def v2_block_lists(block_mask: torch.Tensor):
+    """(block_idx, block_cnt) int32 device tensors from a bool block mask
+    [B, Hq/2, ceil(S/128), ceil(S/64)] (host or device): the selected 64-key
+    tiles of each (batch, pair, query tile), ascending."""
+    m = block_mask.to(torch.bool)
+    cnt = m.sum(dim=-1).to(torch.int32)
+    max_blocks = max(int(cnt.max().item()), 1)
+    n_kb = m.shape[-1]
+    ar = torch.arange(n_kb, device=m.device).expand_as(m)
+    key = torch.where(m, ar, ar + n_kb)                  # selected tiles first, in order
+    idx = torch.sort(key, dim=-1).values[..., :max_blocks].to(torch.int32)
+    idx = torch.where(idx < n_kb, idx, torch.full_like(idx, -1))
+    return idx.contiguous(), cnt.contiguous()
+
+
+def v2_fwd_sparse_launch(args: V2FwdArgs, block_idx, block_cnt) -> None:
+    _check(lib().diffattn_v2_fwd_sparse(ctypes.byref(args), _ptr(block_idx), _ptr(block_cnt),
+                                        int(block_idx.shape[-1]), _stream()), "diffattn_v2_fwd_sparse")
+
+
+def v2_fwd_sparse(q, k, v, lam, block_idx, block_cnt, *, causal: bool = True, softmax_scale: float = 0.0, out=None):
+    """Block-sparse DIFF V2 prefill forward through diffattn_v2_fwd_sparse;
+    block_idx [B, Hq/2, ceil(S/128), max_blocks], block_cnt [B, Hq/2,
+    ceil(S/128)] (int32 on q's GPU, e.g. from v2_block_lists)."""
+    B, S, Hq, D = q.shape
+    n_qt = (S + 127) // 128
+    _require(block_idx.dtype == torch.int32 and block_cnt.dtype == torch.int32 and block_idx.is_cuda
+             and block_cnt.is_cuda and block_idx.device == q.device and block_cnt.device == q.device,
+             "block lists: int32 on q's GPU")
+    _require(tuple(block_cnt.shape) == (B, Hq // 2, n_qt) and block_cnt.is_contiguous(),
+             "block_cnt must be contiguous [B, Hq/2, ceil(S/128)]")
+    _require(block_idx.dim() == 4 and tuple(block_idx.shape[:3]) == (B, Hq // 2, n_qt) and block_idx.is_contiguous(),
+             "block_idx must be contiguous [B, Hq/2, ceil(S/128), max_blocks]")
+    if out is None:
+        out = torch.empty((B, S, Hq // 2, D), dtype=q.dtype, device=q.device)
+    v2_fwd_sparse_launch(v2_fwd_args(q, k, v, lam, out, causal=causal, softmax_scale=softmax_scale), block_idx,
+                         block_cnt)
     return out

@@ -338,6 +338,43 @@ int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
   return hip_status(diffattn::launch_fwd_v2(p, static_cast<hipStream_t>(stream)), "V2 prefill launch");
 }
 
+int diffattn_v2_fwd_sparse(const diffattn_v2_fwd_args *a, const int32_t *block_idx, const int32_t *block_cnt,
+                           int32_t max_blocks, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch == 0 || a->seqlen == 0) {
+    if (a->batch < 0 || a->seqlen < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0, seqlen >= 0");
+    return DIFFATTN_OK;
+  }
+  int rc = check_v2_common(a->batch, a->seqlen, a->q_heads, a->kv_heads, a->head_dim, a->dtype, a->q, a->k, a->v,
+                           a->lam, a->q_stride, a->kv_stride, a->lam_stride, a->softmax_scale);
+  if (rc) return rc;
+  if (!a->out) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+  if (!strides_ok(a->o_stride, 3)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "strides must be positive");
+  if (a->lse || a->a_even || a->a_odd)
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "the block-sparse forward has no training saves");
+  if (!block_idx || !block_cnt) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "block_idx and block_cnt must be non-NULL");
+  if (max_blocks < 1 || max_blocks > 1024) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "max_blocks must be in [1, 1024]");
+  {
+    const void *ptrs[] = {a->q, a->k, a->v, a->out};
+    const int64_t *str[] = {a->q_stride, a->kv_stride, a->o_stride};
+    if (!fused_layout_ok(ptrs, 4, str, 3))
+      return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs 16-byte aligned pointers and strides that are multiples of 8");
+  }
+  diffattn::V2FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v;
+  p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
+  p.kvs_b = a->kv_stride[0]; p.kvs_s = a->kv_stride[1]; p.kvs_h = a->kv_stride[2];
+  p.os_b = a->o_stride[0]; p.os_s = a->o_stride[1]; p.os_h = a->o_stride[2];
+  p.lam = a->lam; p.ls_b = a->lam_stride[0]; p.ls_s = a->lam_stride[1]; p.ls_p = a->lam_stride[2];
+  p.out = a->out;
+  p.B = a->batch; p.S = a->seqlen; p.Hq = a->q_heads; p.Hkv = a->kv_heads;
+  p.causal = a->causal != 0;
+  p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
+  p.blk_idx = block_idx; p.blk_cnt = block_cnt; p.max_blocks = max_blocks;
+  return hip_status(diffattn::launch_fwd_v2(p, static_cast<hipStream_t>(stream)), "block-sparse V2 prefill launch");
+}
+
 static int check_v2_bwd(const diffattn_v2_bwd_args *a) {
   if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
   int rc = check_v2_common(a->batch, a->seqlen, a->q_heads, a->kv_heads, a->head_dim, a->dtype, a->q, a->k, a->v,

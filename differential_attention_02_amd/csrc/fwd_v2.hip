@@ -34,6 +34,7 @@ namespace diffattn {
 namespace {
 
 constexpr int D = 128, BM = 128, BN = 64, NT = 256;
+constexpr int kMaxBlocks = 1024;  // key tiles a sparse query tile may list (64K keys)
 constexpr int KST = D + 8;   // LDS row stride of the K tile, bf16 elements (272 B)
 constexpr int VST = D + 32;  // LDS row stride of the V tile, fp16 elements (320 B)
 
@@ -284,11 +285,132 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   }
 }
 
+// Block-sparse variant (one key-block selection per even/odd pair: sparse
+// attention frameworks select blocks per head pair inside a GQA group, tistory
+// page on DIFF V2, section on practical considerations).  The caller lists,
+// per (batch, pair, 128-row query tile), the 64-key tiles the pair may attend
+// (ascending); each head's softmax runs over the listed keys (with the causal
+// mask inside them), every other weight being zero.  Entries outside the
+// sequence, past the query tile (causal) or not above the previous accepted
+// entry are skipped; a row that sees no key gets zeros.  Same two passes
+// and staging as the dense kernel, walking the list instead of 0..n.
+__global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
+  __shared__ SmemV2 sm[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, h = lane >> 5;
+  const int npair = p.Hq / 2;
+  const int BP = p.B * npair;
+  const int n_qt = (p.S + BM - 1) / BM;
+  const int bp = blockIdx.x % BP;
+  const int qt_i = blockIdx.x / BP;
+  const int qt = p.causal ? n_qt - 1 - qt_i : qt_i;
+  const int b = bp / npair, pr = bp % npair;
+  const int te = 2 * pr, j = te / (p.Hq / p.Hkv);
+  const int q0 = qt * BM, qw = q0 + wave * 32, my_q = qw + ln;
+  const int S = p.S;
+  const bool causal = p.causal != 0;
+  const bool qok = my_q < S;
+  const float c = p.scale * kLog2e;
+  const float lam = qok ? p.lam[b * p.ls_b + (int64_t)my_q * p.ls_s + pr * p.ls_p] : 0.f;
+  const float sig = 1.f / (1.f + expf(-lam));
+
+  // This query tile's list of key tiles (read by every thread; uniform).
+  const int64_t li = (int64_t)bp * n_qt + qt;
+  const int cnt = min(min(max(p.blk_cnt[li], 0), p.max_blocks), kMaxBlocks);
+  const int32_t *lst = p.blk_idx + li * p.max_blocks;
+  const int n_ktot = (S + BN - 1) / BN;
+  const int kt_lim = causal ? min(n_ktot, (q0 + BM + BN - 1) / BN) : n_ktot;  // tiles past the last row see nothing
+
+  LoaderV2 ld;
+  ld.init((const bf16 *)p.k + b * p.kvs_b + j * p.kvs_h, (const bf16 *)p.v + b * p.kvs_b + j * p.kvs_h, p.kvs_s, S,
+          tid);
+
+  bf16x8 qe[D / 16], qo[D / 16];
+  {
+    const bf16 *q = (const bf16 *)p.q + b * p.qs_b + (int64_t)my_q * p.qs_s + 8 * h;
+    const bf16 *qev = q + te * p.qs_h, *qov = q + (te + 1) * p.qs_h;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qe[kc] = qok ? *(const bf16x8 *)(qev + kc * 16) : bf16x8{};
+      qo[kc] = qok ? *(const bf16x8 *)(qov + kc * 16) : bf16x8{};
+    }
+  }
+  const int krow = k_row_perm(ln);
+  // The valid list entries (tile index in [0, kt_lim)), compacted into LDS.
+  __shared__ int tiles[kMaxBlocks];
+  __shared__ int n_tiles;
+  if (tid == 0) {  // ascending, in range; entries not above the last accepted one are ignored
+    int n = 0, last = -1;
+    for (int i = 0; i < cnt; ++i) {
+      const int t = lst[i];
+      if (t > last && t < kt_lim) tiles[n++] = last = t;
+    }
+    n_tiles = n;
+  }
+  __syncthreads();
+  const int n_valid = __builtin_amdgcn_readfirstlane(n_tiles);
+
+  // ---------------- pass 1 ----------------
+  float me = kNegInf, le = 0.f, mo = kNegInf, lo = 0.f;
+  TileRegsV2 nxt;
+  ld.load((n_valid > 0 ? tiles[0] : 0) * BN, false, nxt);
+  store_tile(sm[0], nxt, tid, false);
+  __syncthreads();
+  for (int n = 0; n < n_valid; ++n) {
+    const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
+    const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
+    ld.load(nk * BN, false, nxt);
+    pass1_tile<true>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    store_tile(sm[(n + 1) & 1], nxt, tid, false);
+    __syncthreads();
+  }
+  float Me, Le, Mo, Lo;
+  lse_finish(me, le, Me, Le);
+  lse_finish(mo, lo, Mo, Lo);
+  const bool live = Le != kNegInf;  // the row saw at least one key (both heads see the same keys)
+  const float sg = live ? row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo)) : 0.f;
+  const float Les = live ? Le - sg : __builtin_inff(), Los = live ? Lo - sg : __builtin_inff();
+
+  // ---------------- pass 2 ----------------
+  f32x16 o[D / 32], dummy[1];
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) o[ct] = f32x16{};
+  ld.load((n_valid > 0 ? tiles[0] : 0) * BN, true, nxt);
+  store_tile(sm[0], nxt, tid, true);
+  __syncthreads();
+  for (int n = 0; n < n_valid; ++n) {
+    const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
+    const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
+    ld.load(nk * BN, true, nxt);
+    pass2_tile<true, false>(sm[n & 1], cur * BN, krow, lane, qe, qo, c, sig, Les, Los, 1.f, 1.f, o, dummy, dummy, S,
+                            causal, qw, my_q);
+    store_tile(sm[(n + 1) & 1], nxt, tid, true);
+    __syncthreads();
+  }
+
+  if (qok) {
+    const float f = live ? fast_exp2(-sg) : 0.f;
+    bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + pr * p.os_h;
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = ct * 32 + 8 * g + 4 * h;
+        const bf16x4 y = {f2bf(o[ct][4 * g] * f), f2bf(o[ct][4 * g + 1] * f), f2bf(o[ct][4 * g + 2] * f),
+                          f2bf(o[ct][4 * g + 3] * f)};
+        *(bf16x4 *)(out + ch) = y;
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st) {
   const int n_qt = (p.S + BM - 1) / BM;
-  if (p.lse)
+  if (p.blk_idx)
+    hipLaunchKernelGGL(fwd_v2_sparse_kernel, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);
+  else if (p.lse)
     hipLaunchKernelGGL(fwd_v2_kernel<true>, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL(fwd_v2_kernel<false>, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);

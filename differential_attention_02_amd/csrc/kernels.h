@@ -84,6 +84,10 @@ struct V2FwdParams {
   float scale;
   float *lse;            // training saves (all or none): [B, Hq, S] natural-log partition functions,
   float *a_even, *a_odd; // [B, S, Hq/2, D] each head's own output (attn_2p, attn_2p+1)
+  // Block-sparse selection (null for dense): per (batch, pair, 128-row query
+  // tile), blk_cnt entries of blk_idx (64-key tile indices, ascending).
+  const int32_t *blk_idx, *blk_cnt;
+  int max_blocks;
 };
 
 // DIFF V2 prefill backward (bf16, D = 128).

@@ -234,6 +234,46 @@ def make_v2_prefill_inputs(cfg: V2PrefillConfig | str = "v2_prefill_4k", seed: i
     return t
 
 
+def make_block_selection(batch: int, pairs: int, seqlen: int, *, budget: int = 16, sink: int = 1, local: int = 4,
+                         seed: int = 0, causal: bool = True, q_block: int = 128, k_block: int = 64) -> torch.Tensor:
+    """A seeded key-block selection per (batch, head pair, query block): bool
+    [B, P, ceil(S / q_block), ceil(S / k_block)].  Each query block keeps the
+    first `sink` key blocks, the `local` key blocks that end at its own last
+    row, and random other key blocks (uniform, without repeats) up to `budget`
+    blocks; with causal set only key blocks that start at or before the query
+    block's last row are eligible, so early query blocks keep all of theirs."""
+    nqb = (seqlen + q_block - 1) // q_block
+    nkb = (seqlen + k_block - 1) // k_block
+    gen = torch.Generator().manual_seed(seed)
+    score = torch.rand((batch, pairs, nqb, nkb), generator=gen)
+    kb = torch.arange(nkb)[None, :]
+    hi = torch.clamp((torch.arange(nqb)[:, None] + 1) * q_block, max=seqlen)   # one past the block's last row
+    end = (hi + k_block - 1) // k_block                                        # key blocks up to that row
+    forced = (kb < sink) | ((kb >= end - local) & (kb < end))
+    eligible = kb < end if causal else torch.ones((nqb, nkb), dtype=torch.bool)
+    score = torch.where(forced, torch.full_like(score, 2.0), score)
+    score = torch.where(eligible, score, torch.full_like(score, -1.0))
+    top = torch.topk(score, min(budget, nkb), dim=-1)
+    mask = torch.zeros_like(score, dtype=torch.bool)
+    mask.scatter_(-1, top.indices, top.values >= 0)
+    return mask
+
+
+def block_pairs(mask: torch.Tensor, seqlen: int, *, causal: bool = True, q_block: int = 128,
+                k_block: int = 64) -> int:
+    """Number of (query, key, pair) triples a block selection lets through."""
+    nqb, nkb = mask.shape[-2:]
+    rows = torch.arange(seqlen)
+    keys = torch.arange(seqlen)
+    per = torch.zeros((nqb, nkb), dtype=torch.int64)     # allowed pairs inside each (query block, key block)
+    for t in range(nqb):
+        r = rows[t * q_block:(t + 1) * q_block]
+        for i in range(nkb):
+            k = keys[i * k_block:(i + 1) * k_block]
+            per[t, i] = int(((k[None, :] <= r[:, None]) if causal else torch.ones(len(r), len(k))).sum())
+    return int((mask.to(torch.int64) * per).sum())
+
+
 def worked_example_inputs(n: int = 6, d: int = 8, seed: int = 0):
     """The glossary page's worked example draw: seed 0, one randn(4, n, d) call
     split into q1, k1, q2, k2, then randn(n, 2d) for v (float32)."""

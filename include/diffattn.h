@@ -26,6 +26,7 @@
  *     or not), with a sigmoid input per token and pair [same sections; item 5
  *     makes lambda per token and per head].
  *   - DIFF V2 prefill backward: its gradients by the chain rule.
+ *   - Block-sparse DIFF V2 prefill forward (key blocks selected per head pair).
  *   - DIFF V1 decode: the V1 operator for one new token over a K1/K2/V cache.
  *   - DIFF V1 forward with fp8 e4m3 attention logits (per-row absmax scaling).
  *
@@ -326,6 +327,24 @@ size_t diffattn_v1_decode_workspace_size(const diffattn_v1_decode_args *args);
 
 /* DIFF V2 prefill forward. Returns DIFFATTN_OK or a negative status. */
 int diffattn_v2_fwd(const diffattn_v2_fwd_args *args, void *stream);
+
+/*
+ * Block-sparse DIFF V2 prefill forward: one key-block selection per even/odd
+ * head pair [V2 page, practical considerations: DIFF V2 works with sparse
+ * attention frameworks by selecting blocks per head pair inside a GQA group;
+ * the glossary's sparse-attention entry: a fixed subset of token pairs is
+ * scored and every other weight is zero].  args as for diffattn_v2_fwd
+ * without training saves.  block_cnt: device int32 [B, Hq/2, ceil(S / 128)];
+ * block_idx: device int32 [B, Hq/2, ceil(S / 128), max_blocks].  For query
+ * tile t (rows 128 t .. 128 t + 127) of pair p, the first block_cnt entries
+ * of its block_idx row list the 64-key tiles (keys 64 i .. 64 i + 63) the
+ * pair attends, ascending; entries out of range, past the query tile (causal)
+ * or not above the previous accepted entry are ignored.  Each head's softmax
+ * runs over the listed keys (causal mask applied inside them); a row that
+ * sees no key is zero.  1 <= max_blocks <= 1024.
+ */
+int diffattn_v2_fwd_sparse(const diffattn_v2_fwd_args *args, const int32_t *block_idx, const int32_t *block_cnt,
+                           int32_t max_blocks, void *stream);
 
 /* DIFF V2 prefill backward. Returns DIFFATTN_OK or a negative status. */
 int diffattn_v2_bwd(const diffattn_v2_bwd_args *args, void *stream);

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -197,6 +197,16 @@ def _v2_args(**kw):
     for k, v in kw.items():
         setattr(a, k, v)
     return a
+
+
+@host_only
+@pytest.mark.parametrize("blk,cnt,maxb,code", [(None, FAKE, 4, -1), (FAKE, None, 4, -1), (FAKE, FAKE, 0, -1),
+                                               (FAKE, FAKE, 1025, -1)])
+def test_v2_fwd_sparse_rejects(blk, cnt, maxb, code):
+    a = _v2_args()
+    assert B.lib().diffattn_v2_fwd_sparse(ctypes.byref(a), blk, cnt, maxb, None) == code
+    a = _v2_args(lse=FAKE, a_even=FAKE, a_odd=FAKE)
+    assert B.lib().diffattn_v2_fwd_sparse(ctypes.byref(a), FAKE, FAKE, 4, None) == -2
 
 
 def test_v2_fwd_empty_problem_is_ok():

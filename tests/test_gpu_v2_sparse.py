@@ -1,0 +1,142 @@
+"""GPU parity of diffattn_v2_fwd_sparse (the DIFF V2 prefill forward over key
+blocks selected per even/odd head pair, through the C ABI) against the float64
+oracle: ragged causal and full-attention cases over several 128-row query and
+64-key tiles, a group of four query heads per KV head, query tiles whose
+selection is empty or leaves rows without keys, lists with entries the kernel
+ignores, the full selection against the dense kernel, and sampled rows of the
+full 4 x 4096-token workload under its seeded selection."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differential_attention_02_amd import binding as B
+from differential_attention_02_amd import workloads
+from tests.parity import as_f64, assert_bf16_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _inputs(seed, **kw):
+    return workloads.make_v2_prefill_inputs("v2_prefill_4k", seed=seed, **kw)
+
+
+def _run(inp, mask, causal=True):
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    idx, cnt = B.v2_block_lists(mask.cuda())
+    out = B.v2_fwd_sparse(q, k, v, lam, idx, cnt, causal=causal)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(inp, mask, causal=True, rows=None):
+    out = oracle.v2_prefill_fwd_block_sparse(as_f64(inp["q"]), as_f64(inp["k"]), as_f64(inp["v"]),
+                                             as_f64(inp["lam"]), mask.numpy(), causal=causal)
+    return out if rows is None else out[:, rows]
+
+
+def _mask(inp, seed, **kw):
+    Bn, S, Hq, _ = inp["q"].shape
+    return workloads.make_block_selection(Bn, Hq // 2, S, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("S,budget", [(1, 2), (65, 2), (300, 3), (700, 5), (1100, 6)])
+def test_ragged_causal(S, budget):
+    _note(f"v2 sparse causal S={S} budget={budget}")
+    inp = _inputs(S, batch=2, seqlen=S, q_heads=8, kv_heads=4)
+    m = _mask(inp, S, budget=budget, local=2)
+    assert_bf16_rows(_run(inp, m), _ref(inp, m), f"v2 sparse causal S={S}")
+
+
+@pytest.mark.parametrize("S", [200, 650])
+def test_full_attention(S):
+    _note(f"v2 sparse non-causal S={S}")
+    inp = _inputs(200 + S, batch=2, seqlen=S, q_heads=4, kv_heads=2)
+    m = _mask(inp, S, budget=4, local=1, causal=False)
+    assert_bf16_rows(_run(inp, m, causal=False), _ref(inp, m, causal=False), f"v2 sparse non-causal S={S}")
+
+
+def test_group_of_four():
+    """Two pairs per KV head, each with its own selection."""
+    _note("v2 sparse group 4")
+    inp = _inputs(7, batch=1, seqlen=520, q_heads=8, kv_heads=2)
+    m = _mask(inp, 7, budget=4, local=2)
+    assert_bf16_rows(_run(inp, m), _ref(inp, m), "v2 sparse group 4")
+
+
+def test_empty_selections_and_dead_rows():
+    """A query tile with no block gives zeros; a causal query tile that keeps
+    only its second diagonal key block leaves its first 64 rows without keys
+    (zeros) and its last 64 rows on that block alone."""
+    _note("v2 sparse empty and dead rows")
+    inp = _inputs(11, batch=1, seqlen=384, q_heads=4, kv_heads=2)
+    m = _mask(inp, 11, budget=3, local=1)
+    m[0, 0, 1] = False
+    m[0, 1, 2] = False
+    m[0, 1, 2, 5] = True
+    out = _run(inp, m)
+    ref = _ref(inp, m)
+    assert torch.all(out[0, 128:256, 0] == 0)
+    assert torch.all(out[0, 256:320, 1] == 0)
+    assert_bf16_rows(out, ref, "v2 sparse empty and dead rows")
+
+
+def test_ignored_entries():
+    """Entries out of range, past the query tile, repeated or out of order are
+    skipped: the result is that of the accepted entries' selection."""
+    _note("v2 sparse ignored entries")
+    inp = _inputs(12, batch=1, seqlen=300, q_heads=2, kv_heads=1)
+    n_qt, n_kb = 3, 5
+    idx = torch.full((1, 1, n_qt, 6), -1, dtype=torch.int32)
+    cnt = torch.zeros((1, 1, n_qt), dtype=torch.int32)
+    lists = [[0, 1, 1, 3, 9],          # tile 0: 3 is past the causal limit (tiles 0-1), 9 out of range
+             [-2, 2, 0, 3, 3],         # tile 1: -2 skipped, 0 below 2 skipped, repeated 3 skipped
+             [0, 4, 2, 1000, 7, 4]]    # tile 2: 2 below 4 skipped; 1000 and 7 out of range
+    accepted = [[0, 1], [2, 3], [0, 4]]
+    for t, lst in enumerate(lists):
+        idx[0, 0, t, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        cnt[0, 0, t] = len(lst)
+    cnt[0, 0, 2] = 8                   # counts above max_blocks are clamped to it
+    m = torch.zeros((1, 1, n_qt, n_kb), dtype=torch.bool)
+    for t, acc in enumerate(accepted):
+        m[0, 0, t, acc] = True
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    out = B.v2_fwd_sparse(q, k, v, lam, idx.cuda(), cnt.cuda())
+    torch.cuda.synchronize()
+    assert_bf16_rows(out, _ref(inp, m), "v2 sparse ignored entries")
+
+
+def test_full_selection_matches_dense_kernel():
+    """Selecting every key block reproduces the dense V2 forward."""
+    _note("v2 sparse full selection")
+    inp = _inputs(13, batch=2, seqlen=777, q_heads=4, kv_heads=2)
+    Bn, S, Hq, _ = inp["q"].shape
+    m = torch.ones((Bn, Hq // 2, (S + 127) // 128, (S + 63) // 64), dtype=torch.bool)
+    out = _run(inp, m)
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    dense = B.v2_fwd(q, k, v, lam)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(out, dense, rtol=0, atol=0)
+    assert_bf16_rows(out, oracle.v2_prefill_fwd(*(as_f64(inp[n]) for n in ("q", "k", "v", "lam"))),
+                     "v2 sparse full selection")
+
+
+def test_full_workload_sampled_rows():
+    """The 4 x 4096-token, 24-query-head workload under its seeded selection
+    (16 key blocks of 64 per query tile: the first block, the four ending at
+    the tile's last row, the rest drawn at random from the earlier ones)."""
+    _note("v2 sparse full workload")
+    cfg = workloads.CONFIGS["v2_prefill_4k"]
+    inp = _inputs(14)
+    m = workloads.make_block_selection(cfg.batch, cfg.q_heads // 2, cfg.seqlen, seed=14)
+    out = _run(inp, m)
+    rows = np.array([0, 1, 127, 128, 1000, 2047, 3001, 4095])
+    bsl = [3]                          # one batch element: the oracle forms whole 4096 x 4096 maps
+    sub = {n: inp[n][bsl] for n in ("q", "k", "v", "lam")}
+    ref = _ref(sub, m[bsl], rows=rows)
+    assert_bf16_rows(out[bsl][:, torch.as_tensor(rows, device=out.device)], ref, "v2 sparse full workload sampled")
+    assert torch.isfinite(out.float()).all()
