@@ -106,6 +106,27 @@ def test_fused_large_logits():
     assert_bf16_rows(y, ref[0], "large logits")
 
 
+def test_fused_late_dominant_key():
+    """One late key per head whose logit with every later query is about 100
+    (natural log; 144 in log2 units) while the first keys' logits are near 0:
+    pass 1's running sum overflows its reference range there and takes the
+    max-tracking update; map 2's dominant key sits in another tile."""
+    _note("late dominant key")
+    inp = workloads.make_attn_inputs("prefill_4k", seed=21, batch=1, seqlen=700, heads=2)
+    gen = torch.Generator().manual_seed(22)
+    for qn, kn, j in (("q1", "k1", 540), ("q2", "k2", 333)):
+        u = torch.randn((2, 64), generator=gen)
+        u = u / u.norm(dim=-1, keepdim=True)
+        q, k = inp[qn].float(), inp[kn].float()
+        q[0, j:] += 8.0 * u
+        k[0, j] = 100.0 * u
+        inp[qn], inp[kn] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    ref, _ = _oracle_fwd(inp, layer=12, causal=True, norm=True, eps=1e-8, aux=True)
+    assert ref[1]["lse1"][0, :, 600].max() > 90.0
+    y, _ = _gpu_fwd(inp, layer=12, causal=True, norm=True, eps=1e-8)
+    assert_bf16_rows(y, ref[0], "late dominant key")
+
+
 def test_fused_strided_views():
     """q1/q2 and k1/k2 as halves of one [B, S, H, 2, 64] projection tensor."""
     inp = workloads.make_attn_inputs("prefill_4k", seed=11, batch=2, seqlen=200, heads=3)

@@ -66,6 +66,25 @@ def test_peaked_maps():
     assert_bf16_rows(_run(inp), _ref(inp), "v2 prefill peaked")
 
 
+def test_late_dominant_key():
+    """A late key whose logit with every later query of its pair is about 100
+    (144 in log2 units) while the first keys' logits are near 0: pass 1's
+    running sum leaves its reference range there and takes the max-tracking
+    update."""
+    _note("v2 prefill late dominant key")
+    inp = _inputs(23, batch=1, seqlen=520, q_heads=4, kv_heads=2)
+    gen = torch.Generator().manual_seed(24)
+    u = torch.randn((2, 128), generator=gen)
+    u = u / u.norm(dim=-1, keepdim=True)
+    q, k = inp["q"].float(), inp["k"].float()
+    q[0, 400:, 0] += 8.0 * u[0]          # even head of pair 0 (KV head 0)
+    q[0, 300:, 3] += 8.0 * u[1]          # odd head of pair 1 (KV head 1)
+    k[0, 400, 0] = 141.0 * u[0]
+    k[0, 300, 1] = 141.0 * u[1]
+    inp["q"], inp["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    assert_bf16_rows(_run(inp), _ref(inp), "v2 prefill late dominant key")
+
+
 def test_broadcast_lambda_shapes():
     _note("v2 prefill lambda shapes")
     inp = _inputs(9, batch=2, seqlen=190, q_heads=4, kv_heads=2)
