@@ -584,7 +584,8 @@ def main(argv=None) -> int:
                                "four ending at the tile's last row, 11 random earlier ones; seed 0)",
                    "density": v2s["density"]},
         "roofline": {"bound": "mfma", "achieved": v2s["event_tflops"], "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": v2s["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": v2s["event_tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": _traffic_from_profile("fwd_v2_sparse_v2_sparse_4k_pmc.md", V2P_SOURCES),
                      "note": "1024 flop per selected (query, key, pair) triple"},
         "median_ms": v2s["median_ms"], "min_ms": v2s["min_ms"],
     }

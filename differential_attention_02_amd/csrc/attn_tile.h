@@ -35,35 +35,6 @@ __device__ __forceinline__ void lse_update(const f32x16 &s, float c, float &m, f
   m = mn;
 }
 
-// Sum of 2^(c s - m) over one lane's 16 scores added to l against the row's
-// current reference m, without a new maximum: the sum is exact for any
-// reference.  Returns false if the new sum left [0, 2^100) (a score far above
-// the reference, or no reference yet: m = -inf gives inf or NaN); the caller
-// then redoes the sub-tile with lse_update, which raises the reference.
-__device__ __forceinline__ bool lse_try_ref(const f32x16 &s, float c, float m, float l, float &l_new) {
-  float a[4] = {l, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int r = 0; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -m));
-  l_new = (a[0] + a[1]) + (a[2] + a[3]);
-  return l_new < 0x1p100f;
-}
-
-// Both maps' pass-1 update of one sub-tile: the reference path when every lane
-// of the wave stays in range (the common case once a row has seen a few keys),
-// else the max-tracking update for the whole wave (a uniform branch).
-__device__ __forceinline__ void lse_update_pair(const f32x16 &s1, const f32x16 &s2, float c1, float c2, float &m1,
-                                                float &l1, float &m2, float &l2) {
-  float n1, n2;
-  const bool ok = lse_try_ref(s1, c1, m1, l1, n1) & lse_try_ref(s2, c2, m2, l2, n2);
-  if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
-    l1 = n1;
-    l2 = n2;
-  } else {
-    lse_update(s1, c1, m1, l1);
-    lse_update(s2, c2, m2, l2);
-  }
-}
-
 // Full-row top score M and log2 partition function L from the two
 // half-waves' (m, l).
 __device__ __forceinline__ void lse_finish(float m, float l, float &M, float &L) {

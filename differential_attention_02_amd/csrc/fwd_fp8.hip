@@ -197,8 +197,10 @@ __device__ __forceinline__ void pass1_tile(const SmemF &sm, int kbase, int krow,
     f32x16 s1a, s2a, s1b, s2b;
     scores_f(sm, 0, krow, h, qf1, qf2, s1a, s2a);
     scores_f(sm, 1, krow, h, qf1, qf2, s1b, s2b);
-    lse_update_pair(s1a, s2a, c1, c2, m1, l1, m2, l2);
-    lse_update_pair(s1b, s2b, c1, c2, m1, l1, m2, l2);
+    lse_update(s1a, c1, m1, l1);
+    lse_update(s2a, c2, m2, l2);
+    lse_update(s1b, c1, m1, l1);
+    lse_update(s2b, c2, m2, l2);
   } else {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -312,9 +314,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
   float M1, L1, M2, L2;
   lse_finish(m1, l1, M1, L1);
   lse_finish(m2, l2, M2, L2);
-  // |W| <= 1 + |lambda| (pass 1 tracks each row's sum against a reference, not
-  // its exact maximum); weights down to 2^-27 stay normal in fp16.
-  const float sg = row_scale_log2(1.f + fabsf(lam));
+  const float sg = row_scale_log2(fast_exp2(M1 - L1) + fabsf(lam) * fast_exp2(M2 - L2));
   const float L1s = L1 - sg, L2s = L2 - sg;
 
   // ---------------- pass 2: O = (P1 / l1 - lambda P2 / l2) V ----------------

@@ -23,14 +23,11 @@
 // amplified by 1 / (1 - lambda).  W and V enter the PV product as fp16 (V is
 // converted exactly from bf16 on its way into LDS), because bf16's 8-bit
 // significand alone would spend most of the error budget.  Each row's W is
-// scaled by a power of two 2^sigma that keeps its largest possible value just
-// under 2^15: from 1 + |lambda| in inference, or, in training mode, from pass
-// 1's exact row maxima (the largest weight is at most 2^(M1 - L1) + |lambda|
-// 2^(M2 - L2), M the row's top score), so even 64K-key rows of ~1/65536
-// weights stay well inside fp16's normal range; sigma folds into L for free
-// and the epilogue removes it exactly.  In inference pass 1 adds each sub-tile
-// against the row's current reference and only recomputes the maximum when a
-// sum leaves [0, 2^100), which saves the per-score max.  Matrix-core work per (query, key) pair is 4 QK^T products of
+// scaled by a power of two 2^sigma chosen from pass 1 (the largest weight is
+// at most 2^(M1 - L1) + |lambda| 2^(M2 - L2), M the row's top score), so it
+// sits just under 2^15 and even 64K-key rows of ~1/65536 weights stay in
+// fp16's normal range; sigma folds into L for free and the epilogue removes
+// it exactly.  Matrix-core work per (query, key) pair is 4 QK^T products of
 // width 64 plus one PV product of width 128: 768 flop, the same as a one-pass
 // form with two PV products.
 //
@@ -163,9 +160,7 @@ __device__ __forceinline__ void pv_step(const Smem &sm, int sub, int lane, const
 // is visible to every query of the workgroup; both sub-tiles' score products
 // are issued before any softmax arithmetic so the exponentials of the first
 // overlap the matrix work of the second.
-// REF: sums against each row's reference without tracking the exact maximum
-// (the inference forward, whose weight scale needs no maximum).
-template <bool MASKED, bool REF>
+template <bool MASKED>
 __device__ __forceinline__ void pass1_tile(const Smem &sm, int kbase, int krow, int h, const bf16x8 *qf1,
                                            const bf16x8 *qf2, float c, float &m1, float &l1, float &m2,
                                            float &l2, int S, bool causal, int qw, int my_q) {
@@ -173,15 +168,10 @@ __device__ __forceinline__ void pass1_tile(const Smem &sm, int kbase, int krow, 
     f32x16 s1a, s2a, s1b, s2b;
     scores(sm, 0, krow, h, qf1, qf2, s1a, s2a);
     scores(sm, 1, krow, h, qf1, qf2, s1b, s2b);
-    if constexpr (REF) {
-      lse_update_pair(s1a, s2a, c, c, m1, l1, m2, l2);
-      lse_update_pair(s1b, s2b, c, c, m1, l1, m2, l2);
-    } else {
-      lse_update(s1a, c, m1, l1);
-      lse_update(s2a, c, m2, l2);
-      lse_update(s1b, c, m1, l1);
-      lse_update(s2b, c, m2, l2);
-    }
+    lse_update(s1a, c, m1, l1);
+    lse_update(s2a, c, m2, l2);
+    lse_update(s1b, c, m1, l1);
+    lse_update(s2b, c, m2, l2);
   } else {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -306,25 +296,21 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
   // Interior tiles first (straight-line, no masks), then the diagonal / tail.
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
-    pass1_tile<false, !SAVE>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
+    pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);
-    pass1_tile<true, !SAVE>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
+    pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   float M1, L1, M2, L2;
   lse_finish(m1, l1, M1, L1);
   lse_finish(m2, l2, M2, L2);
-  // Row scale 2^sg for the fp16 weights (and 2^sg2 for the saved second map):
-  // |W| <= 2^(M1 - L1) + |lambda| 2^(M2 - L2) with the exact maxima (training),
-  // else the bound 1 + |lambda|, which still leaves weights of 2^-27 normal in
-  // fp16 (a 2^20-key row of equal weights sits near 2^-6).
-  const float sg = SAVE ? row_scale_log2(fast_exp2(M1 - L1) + fabsf(lam) * fast_exp2(M2 - L2))
-                        : row_scale_log2(1.f + fabsf(lam));
+  // Row scale 2^sg for the fp16 weights (and 2^sg2 for the saved second map).
+  const float sg = row_scale_log2(fast_exp2(M1 - L1) + fabsf(lam) * fast_exp2(M2 - L2));
   const float L1s = L1 - sg, L2s = L2 - sg;
   const float sg2 = SAVE ? row_scale_log2(fast_exp2(M2 - L2)) : 0.f;
   const float L2s2 = L2 - sg2;

@@ -20,9 +20,8 @@
 // loads, one barrier per tile), as in the V1 forward: pass 1 computes each
 // map's log2 partition function per row; pass 2 recomputes the scores, forms
 // the combined weight W = 2^(s_e c - L_e) - sigmoid(lambda) 2^(s_o c - L_o) in
-// float32, scales it by a power of two per row (largest possible weight,
-// 1 + sigmoid(lambda) or in training mode the exact bound from pass 1's
-// maxima, just under 2^15), rounds it once to fp16 and accumulates W V with fp16 V.  Rounding the
+// float32, scales it by a power of two per row (largest weight just under
+// 2^15), rounds it once to fp16 and accumulates W V with fp16 V.  Rounding the
 // combined weight keeps the error proportional to the combined map when
 // sigmoid(lambda) is near 1 and the two heads nearly cancel.  Scores are
 // computed transposed (S^T = K Q^T, lane = query); K rows are read in the
@@ -104,9 +103,7 @@ __device__ __forceinline__ void scores2(const SmemV2 &sm, int sub, int krow, int
   }
 }
 
-// REF: sums against each row's reference without tracking the exact maximum
-// (inference, whose weight scale needs no maximum).
-template <bool MASKED, bool REF>
+template <bool MASKED>
 __device__ __forceinline__ void pass1_tile(const SmemV2 &sm, int kbase, int krow, int h, const bf16x8 *qe,
                                            const bf16x8 *qo, float c, float &me, float &le, float &mo, float &lo,
                                            int S, bool causal, int qw, int my_q) {
@@ -117,12 +114,8 @@ __device__ __forceinline__ void pass1_tile(const SmemV2 &sm, int kbase, int krow
     f32x16 se, so;
     scores2(sm, sub, krow, h, qe, qo, se, so);
     if (MASKED && ((causal && sb + 31 > qw) || sb + 32 > S)) mask_scores(se, so, sb, h, S, causal, my_q);
-    if constexpr (REF) {
-      lse_update_pair(se, so, c, c, me, le, mo, lo);
-    } else {
-      lse_update(se, c, me, le);
-      lse_update(so, c, mo, lo);
-    }
+    lse_update(se, c, me, le);
+    lse_update(so, c, mo, lo);
   }
 }
 
@@ -213,22 +206,20 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
-    pass1_tile<false, !SAVE>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);
-    pass1_tile<true, !SAVE>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   float Me, Le, Mo, Lo;
   lse_finish(me, le, Me, Le);
   lse_finish(mo, lo, Mo, Lo);
-  // |W| <= 2^(Me - Le) + sigma 2^(Mo - Lo) with the exact maxima (training),
-  // else the bound 1 + sigma.
-  const float sg = SAVE ? row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo)) : row_scale_log2(1.f + sig);
+  const float sg = row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo));
   const float Les = Le - sg, Los = Lo - sg;
   // Each head's own weights just under 2^15 for A_even and A_odd.
   const float sge = SAVE ? row_scale_log2(fast_exp2(Me - Le)) : 0.f;
@@ -372,7 +363,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
     const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
     ld.load(nk * BN, false, nxt);
-    pass1_tile<true, true>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    pass1_tile<true>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     store_tile(sm[(n + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
@@ -380,7 +371,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   lse_finish(me, le, Me, Le);
   lse_finish(mo, lo, Mo, Lo);
   const bool live = Le != kNegInf;  // the row saw at least one key (both heads see the same keys)
-  const float sg = live ? row_scale_log2(1.f + sig) : 0.f;  // |W| <= 1 + sigma
+  const float sg = live ? row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo)) : 0.f;
   const float Les = live ? Le - sg : __builtin_inff(), Los = live ? Lo - sg : __builtin_inff();
 
   // ---------------- pass 2 ----------------

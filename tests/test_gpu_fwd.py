@@ -109,8 +109,9 @@ def test_fused_large_logits():
 def test_fused_late_dominant_key():
     """One late key per head whose logit with every later query is about 100
     (natural log; 144 in log2 units) while the first keys' logits are near 0:
-    pass 1's running sum overflows its reference range there and takes the
-    max-tracking update; map 2's dominant key sits in another tile."""
+    the running maximum jumps far past the range of a float's exponent at that
+    key (the earlier sum is rescaled to zero); map 2's dominant key sits in
+    another tile."""
     _note("late dominant key")
     inp = workloads.make_attn_inputs("prefill_4k", seed=21, batch=1, seqlen=700, heads=2)
     gen = torch.Generator().manual_seed(22)

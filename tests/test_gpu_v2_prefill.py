@@ -68,9 +68,8 @@ def test_peaked_maps():
 
 def test_late_dominant_key():
     """A late key whose logit with every later query of its pair is about 100
-    (144 in log2 units) while the first keys' logits are near 0: pass 1's
-    running sum leaves its reference range there and takes the max-tracking
-    update."""
+    (144 in log2 units) while the first keys' logits are near 0: the running
+    maximum jumps far past the range of a float's exponent at that key."""
     _note("v2 prefill late dominant key")
     inp = _inputs(23, batch=1, seqlen=520, q_heads=4, kv_heads=2)
     gen = torch.Generator().manual_seed(24)
