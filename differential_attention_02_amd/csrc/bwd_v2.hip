@@ -236,22 +236,36 @@ struct SmemQ {
   f16 v[KT * GST];
 };
 
-__device__ __forceinline__ void stage_kv(SmemQ &sm, const bf16 *kg, const bf16 *vg, int64_t kvs, int kbase, int S,
-                                         int tid) {
-  for (int i = tid; i < KT * (D / 8); i += NT) {
-    const int r = i >> 4, col = (i & 15) * 8, key = kbase + r;
-    u32x4 a = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
+// One thread's share of a K/V tile in flight: 16 bytes of K and of V for four
+// (key, column-chunk) slots.
+struct KVRegs {
+  u32x4 k[KT * (D / 8) / NT], v[KT * (D / 8) / NT];
+};
+
+__device__ __forceinline__ void load_kv(KVRegs &r, const bf16 *kg, const bf16 *vg, int64_t kvs, int kbase, int S,
+                                        int tid) {
+#pragma unroll
+  for (int i = 0; i < KT * (D / 8) / NT; ++i) {
+    const int idx = tid + i * NT, row = idx >> 4, col = (idx & 15) * 8, key = kbase + row;
+    r.k[i] = r.v[i] = u32x4{0, 0, 0, 0};
     if (key < S) {
-      a = *(const u32x4 *)(kg + (int64_t)key * kvs + col);
-      bb = *(const u32x4 *)(vg + (int64_t)key * kvs + col);
+      r.k[i] = *(const u32x4 *)(kg + (int64_t)key * kvs + col);
+      r.v[i] = *(const u32x4 *)(vg + (int64_t)key * kvs + col);
     }
-    *(f16x8 *)(sm.k + r * QST + col) = to_f16x8(a);
-    *(f16x8 *)(sm.v + r * GST + col) = to_f16x8(bb);
+  }
+}
+
+__device__ __forceinline__ void store_kv(SmemQ &sm, const KVRegs &r, int tid) {
+#pragma unroll
+  for (int i = 0; i < KT * (D / 8) / NT; ++i) {
+    const int idx = tid + i * NT, row = idx >> 4, col = (idx & 15) * 8;
+    *(f16x8 *)(sm.k + row * QST + col) = to_f16x8(r.k[i]);
+    *(f16x8 *)(sm.v + row * GST + col) = to_f16x8(r.v[i]);
   }
 }
 
 __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
-  __shared__ SmemQ sm;
+  __shared__ SmemQ smb[2];  // double-buffered: tile kt + 1 is loaded while tile kt is in use
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
@@ -299,10 +313,13 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   f32x16 dqe[D / 32], dqo[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dqe[dt] = dqo[dt] = f32x16{};
+  KVRegs nx;
+  load_kv(nx, kg, vg, p.kvs_s, 0, S, tid);
+  store_kv(smb[0], nx, tid);
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    stage_kv(sm, kg, vg, p.kvs_s, kt * KT, S, tid);
-    __syncthreads();
+    const SmemQ &sm = smb[kt & 1];
+    if (kt + 1 < n_kt) load_kv(nx, kg, vg, p.kvs_s, (kt + 1) * KT, S, tid);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int sb = kt * KT + sub * 32;
@@ -342,6 +359,8 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
         }
       }
     }
+    if (kt + 1 < n_kt) store_kv(smb[(kt + 1) & 1], nx, tid);  // the buffer tile kt - 1 used
+    __syncthreads();
   }
   if (qok) {
     const float fq = p.scale * fast_exp2(-(kap + sg));
