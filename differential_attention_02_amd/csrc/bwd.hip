@@ -43,6 +43,8 @@
 // Matrix-core operands are fp16 (bf16 inputs convert exactly) with float32
 // accumulation: bf16 rounding of g, W and dS alone would spend most of the
 // bf16 error budget.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
