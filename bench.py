@@ -369,6 +369,32 @@ def _cpu_baseline_fwd(inp, budget_s=12.0):
                       f"{dt:.1f} s of oracle time"}
 
 
+def _cpu_baseline_64k(inp, heads=2):
+    """The float64 oracle on a stratified sample of the 64K workload: 1024
+    query rows (512 evenly spaced and the last 512) of each of the first
+    `heads` heads, each row against all of its causal keys.  Reports the rate
+    on the sample and the full forward's oracle time extrapolated from it."""
+    import numpy as np
+    import oracle
+    cfg = inp["cfg"]
+    S = cfg.seqlen
+    rows = np.unique(np.concatenate([np.linspace(0, S - 513, 512).astype(np.int64), np.arange(S - 512, S)]))
+    li = oracle.lambda_init(cfg.layer)
+    lam = oracle.lambda_value(*[t.double().numpy() for t in inp["lambda_vecs"]], li)
+    dt = 0.0
+    for h in range(heads):
+        x = [inp[k][:, :, h:h + 1].double().numpy() for k in ("q1", "k1", "q2", "k2", "v")]
+        t0 = time.perf_counter()
+        oracle.diff_attn_fwd(*x, lam, li, causal=True, norm=True, eps=cfg.eps, rows=rows)
+        dt += time.perf_counter() - t0
+    flops = heads * int((rows + 1).sum()) * FLOP_PER_PAIR_FWD
+    full = cfg.batch * cfg.heads * cfg.pairs * FLOP_PER_PAIR_FWD
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"prefill_64k: {len(rows)} query rows (512 evenly spaced + the last 512) of {heads} of "
+                      f"{cfg.batch * cfg.heads} heads, all causal keys; {dt:.1f} s of oracle time",
+            "extrapolated_full_forward_s": full / (flops / dt)}
+
+
 def _cpu_baseline_train(inp):
     """The float64 oracle's forward and backward on one (batch, head) slice of
     the 8K training workload (all 8192 causal rows), same inputs as the GPU."""
@@ -630,6 +656,7 @@ def main(argv=None) -> int:
         extra["v2_train_4k"]["cpu_baseline"] = _cpu_baseline_v2_prefill(v2t["inputs"], with_bwd=True)
         extra["v1_decode"]["cpu_baseline"] = _cpu_baseline_v1_decode()
         extra["v2_sparse_4k"]["cpu_baseline"] = _cpu_baseline_v2_sparse(v2s["inputs"], v2s["mask"])
+        extra["prefill_64k"]["cpu_baseline"] = _cpu_baseline_64k(r64["inputs"])
     line = {
         "metric": METRIC,
         "value": main_r["tflops"],
