@@ -111,7 +111,7 @@ def _time_launches(launch, steps, warmup, per_launch=None):
 
 
 def _device_info():
-    """CU count and peak clock read on the box (hipDeviceAttributeClockRate is
+    """CU count and peak clock read from the device (hipDeviceAttributeClockRate is
     5 in hip_runtime_api.h's enum)."""
     import ctypes
     import torch
@@ -511,7 +511,7 @@ def main(argv=None) -> int:
                     help="first copy a device buffer of this many MiB (reference kernel for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         return 2
     import torch
