@@ -140,3 +140,33 @@ def test_full_workload_sampled_rows():
     ref = _ref(sub, m[bsl], rows=rows)
     assert_bf16_rows(out[bsl][:, torch.as_tensor(rows, device=out.device)], ref, "v2 sparse full workload sampled")
     assert torch.isfinite(out.float()).all()
+
+
+def test_longest_lists_match_dense_kernel():
+    """65536 tokens: the last query tiles list all 1024 key tiles (the most a
+    list may hold); selecting every tile reproduces the dense kernel, and a
+    list that repeats every entry twice gives the same result."""
+    _note("v2 sparse 64K full lists")
+    inp = _inputs(15, batch=1, seqlen=65536, q_heads=2, kv_heads=1)
+    S = 65536
+    q, k, v, lam = (inp[n].cuda() for n in ("q", "k", "v", "lam"))
+    m = torch.ones((1, 1, S // 128, S // 64), dtype=torch.bool, device="cuda")
+    idx, cnt = B.v2_block_lists(m)
+    assert idx.shape[-1] == 1024
+    out = B.v2_fwd_sparse(q, k, v, lam, idx, cnt)
+    dense = B.v2_fwd(q, k, v, lam)
+    torch.cuda.synchronize()
+    assert_bf16_rows(out, dense, "v2 sparse 64K full selection vs dense")
+    # Entries that do not rise above the previous accepted one are skipped: a
+    # list 0,0,1,1,2,2,... (cut at 1024 entries) keeps tiles 0..511 only.
+    dup = torch.repeat_interleave(torch.arange(512, dtype=torch.int32, device="cuda"), 2)
+    idx2 = dup.expand(1, 1, S // 128, 1024).contiguous()
+    cnt2 = torch.full((1, 1, S // 128), 1024, dtype=torch.int32, device="cuda")
+    out2 = B.v2_fwd_sparse(q, k, v, lam, idx2, cnt2)
+    m2 = torch.zeros_like(m)
+    m2[..., :512] = True
+    idx3, cnt3 = B.v2_block_lists(m2)
+    out3 = B.v2_fwd_sparse(q, k, v, lam, idx3, cnt3)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out3)
+    assert torch.isfinite(out2.float()).all()
