@@ -572,7 +572,8 @@ def main(argv=None) -> int:
                             "ms_per_step": r64["wall_s"] / max(3, args.steps // 10) * 1e3,
                             "roofline": {"bound": "mfma", "achieved": r64["event_tflops"], "peak": PEAK_BF16_TFLOPS,
                                          "unit": "TFLOP/s", "frac": r64["event_tflops"] / PEAK_BF16_TFLOPS,
-                                         "traffic": None}}
+                                         "traffic": _traffic_from_profile("fwd_mfma_prefill_64k_pmc.md",
+                                                                          FWD_SOURCES)}}
     tr = _gpu_train(max(3, args.steps // 10), 1)
     extra["train_8k"] = {"metric": "fwd+bwd TFLOP/s", "value": tr["tflops"], "unit": "TFLOP/s",
                          "ms_per_step": tr["ms_per_step"], "frac_of_bf16_peak": tr["tflops"] / PEAK_BF16_TFLOPS,
