@@ -43,8 +43,6 @@
 // Matrix-core operands are fp16 (bf16 inputs convert exactly) with float32
 // accumulation: bf16 rounding of g, W and dS alone would spend most of the
 // bf16 error budget.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -370,53 +368,46 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
       const int qs = q0 + sub * 32;
       if (qs >= S) continue;
       if (p.causal && qs + 31 < kw) continue;  // every query of this sub-chunk precedes my keys
-      const bool need_mask = (p.causal && qs < kw + 31) || kw + 32 > S || qs + 32 > S;
-      // Two straight-line copies, with and without the mask, so the element
-      // loop has no branch and its arithmetic interleaves with the products.
-      auto body = [&](auto masked) {
-        // S1, S2 = Q K^T and dP' = g' V^T; lane = key, registers = queries.
-        f32x16 s1 = {}, s2 = {}, dp = {};
-        const f16 *qa1 = sm.q1 + (sub * 32 + prow) * QST + 8 * h;
-        const f16 *qa2 = sm.q2 + (sub * 32 + prow) * QST + 8 * h;
-        const f16 *ga = sm.g + (sub * 32 + prow) * GST + 8 * h;
+      // S1, S2 = Q K^T and dP' = g' V^T; lane = key, registers = queries.
+      f32x16 s1 = {}, s2 = {}, dp = {};
+      const f16 *qa1 = sm.q1 + (sub * 32 + prow) * QST + 8 * h;
+      const f16 *qa2 = sm.q2 + (sub * 32 + prow) * QST + 8 * h;
+      const f16 *ga = sm.g + (sub * 32 + prow) * GST + 8 * h;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          s1 = mfma32(*(const f16x8 *)(qa1 + kc * 16), kf1[kc], s1);
-          s2 = mfma32(*(const f16x8 *)(qa2 + kc * 16), kf2[kc], s2);
+      for (int kc = 0; kc < 4; ++kc) {
+        s1 = mfma32(*(const f16x8 *)(qa1 + kc * 16), kf1[kc], s1);
+        s2 = mfma32(*(const f16x8 *)(qa2 + kc * 16), kf2[kc], s2);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
+      float wv[16], ds1[16], ds2[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = sub * 32 + row_of_reg(r, h);
+        float p1 = fast_exp2(fmaf(s1[r], c, -sm.lse1[qi]));
+        float p2 = fast_exp2(fmaf(s2[r], c, -sm.lse2[qi]));
+        // Masked pairs as selects, not branches: a uniform test per score
+        // split the loop into blocks the scheduler could not interleave.
+        const int q = q0 + qi;
+        const bool dead = (my_key >= S) | (q >= S) | ((p.causal != 0) & (my_key > q));
+        p1 = dead ? 0.f : p1;
+        p2 = dead ? 0.f : p2;
+        wv[r] = (p1 - lam * p2) * fW;
+        ds1[r] = p1 * (dp[r] - sm.e1[qi]) * fdS;
+        ds2[r] = -lam * p2 * (dp[r] - sm.e2[qi]) * fdS;
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const f16x8 wb = pack8h(wv + 8 * kc2), b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
+        const int r0 = sub * 32 + kc2 * 16;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) dv[ct] = mfma32(tr_operand(sm.g, GST, r0, ct * 32, lane), wb, dv[ct]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          dk1[dt] = mfma32(tr_operand(sm.q1, QST, r0, dt * 32, lane), b1, dk1[dt]);
+          dk2[dt] = mfma32(tr_operand(sm.q2, QST, r0, dt * 32, lane), b2, dk2[dt]);
         }
-#pragma unroll
-        for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
-        float wv[16], ds1[16], ds2[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = sub * 32 + row_of_reg(r, h);
-          float p1 = fast_exp2(fmaf(s1[r], c, -sm.lse1[qi]));
-          float p2 = fast_exp2(fmaf(s2[r], c, -sm.lse2[qi]));
-          if constexpr (decltype(masked)::value) {
-            const int q = q0 + qi;
-            if (my_key >= S || q >= S || (p.causal && my_key > q)) p1 = p2 = 0.f;
-          }
-          wv[r] = (p1 - lam * p2) * fW;
-          ds1[r] = p1 * (dp[r] - sm.e1[qi]) * fdS;
-          ds2[r] = -lam * p2 * (dp[r] - sm.e2[qi]) * fdS;
-        }
-#pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) {
-          const f16x8 wb = pack8h(wv + 8 * kc2), b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
-          const int r0 = sub * 32 + kc2 * 16;
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) dv[ct] = mfma32(tr_operand(sm.g, GST, r0, ct * 32, lane), wb, dv[ct]);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            dk1[dt] = mfma32(tr_operand(sm.q1, QST, r0, dt * 32, lane), b1, dk1[dt]);
-            dk2[dt] = mfma32(tr_operand(sm.q2, QST, r0, dt * 32, lane), b2, dk2[dt]);
-          }
-        }
-      };
-      if (need_mask)
-        body(std::true_type{});
-      else
-        body(std::false_type{});
+      }
     }
     if (more) store_chunk(smb[(it + 1) & 1], nxt, tid);
     __syncthreads();
@@ -560,16 +551,15 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
       if (sb >= S || (p.causal && sb > q_last)) continue;
       f32x16 s1, s2, dp;
       dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
-      const bool need_mask = (p.causal && sb + 31 > qw) || sb + 32 > S;
       float ds1[16], ds2[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p1 = fast_exp2(fmaf(s1[r], c, -L1));
         float p2 = fast_exp2(fmaf(s2[r], c, -L2));
-        if (need_mask) {
-          const int key = sb + row_of_reg(r, h);
-          if (key >= S || (p.causal && key > my_q)) p1 = p2 = 0.f;
-        }
+        const int key = sb + row_of_reg(r, h);  // masked pairs as selects (see bwd_dkdv)
+        const bool dead = (key >= S) | ((p.causal != 0) & (key > my_q));
+        p1 = dead ? 0.f : p1;
+        p2 = dead ? 0.f : p2;
         ds1[r] = p1 * (dp[r] - e1) * fdS;
         ds2[r] = -lam * p2 * (dp[r] - e2) * fdS;
       }

@@ -334,16 +334,17 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
         s_o = mfma32(a, qo[kc], s_o);
         dp = mfma32(*(const f16x8 *)(va + kc * 16), gf[kc], dp);
       }
-      const bool need_mask = (causal && sb + 31 > qw) || sb + 32 > S;
       float dse[16], dso[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pe = fast_exp2(fmaf(s_e[r], c, -Le));
         float po = fast_exp2(fmaf(s_o[r], c, -Lo));
-        if (need_mask) {
-          const int key = sb + row_of_reg(r, h);
-          if (key >= S || (causal && key > my_q)) pe = po = 0.f;
-        }
+        // Masked pairs as selects: a uniform test per score split the loop
+        // into blocks the scheduler could not interleave.
+        const int key = sb + row_of_reg(r, h);
+        const bool dead = (key >= S) | (causal & (key > my_q));
+        pe = dead ? 0.f : pe;
+        po = dead ? 0.f : po;
         dse[r] = pe * (dp[r] - ee) * fdS;
         dso[r] = -sig * po * (dp[r] - eo) * fdS;
       }
