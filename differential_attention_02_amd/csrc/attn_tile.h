@@ -28,9 +28,13 @@ __device__ __forceinline__ void lse_update(const f32x16 &s, float c, float &m, f
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
   const float mn = fmaxf(m, mx * c);
   const float ms = mn == kNegInf ? 0.f : mn;
-  float a[4] = {l * fast_exp2(m - ms), 0.f, 0.f, 0.f};
+  // Four partial sums, each started from its first term (no additions of 0).
+  float a[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -ms));
+  for (int r = 0; r < 4; ++r) a[r] = fast_exp2(fmaf(s[r], c, -ms));
+  a[0] = fmaf(l, fast_exp2(m - ms), a[0]);
+#pragma unroll
+  for (int r = 4; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -ms));
   l = (a[0] + a[1]) + (a[2] + a[3]);
   m = mn;
 }
@@ -81,6 +85,12 @@ __device__ __forceinline__ void pv_step_tile(const f16 *vt, int sub, int lane, c
     }
   }
 }
+
+// Scheduling fence for the double-buffered key loops: keeps the next tile's
+// global loads above the current tile's compute and its LDS stores below it,
+// so the load latency hides behind the compute (left to itself the compiler
+// moved the stores, and the wait for the loads, ahead of the softmax work).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Masks the scores of keys past the sequence end or (causal) past the query.
 __device__ __forceinline__ void mask_scores(f32x16 &s1, f32x16 &s2, int sb, int h, int S, bool causal, int my_q) {

@@ -301,13 +301,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
+    sched_fence();
     pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c1, c2, m1, l1, m2, l2, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);
+    sched_fence();
     pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c1, c2, m1, l1, m2, l2, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
@@ -326,13 +330,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
+    sched_fence();
     pass2_tile<false>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c1, c2, lam, L1s, L2s, o, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
+    sched_fence();
     pass2_tile<true>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c1, c2, lam, L1s, L2s, o, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }

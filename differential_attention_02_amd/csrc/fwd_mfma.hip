@@ -296,13 +296,17 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
   // Interior tiles first (straight-line, no masks), then the diagonal / tail.
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
+    sched_fence();
     pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);
+    sched_fence();
     pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
@@ -328,15 +332,19 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
+    if constexpr (!SAVE) sched_fence();
     pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c, lam, L1s, L2s, L2s2, o, o2, S, causal,
                             qw, my_q);
+    if constexpr (!SAVE) sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
+    if constexpr (!SAVE) sched_fence();
     pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c, lam, L1s, L2s, L2s2, o, o2, S, causal,
                            qw, my_q);
+    if constexpr (!SAVE) sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }

@@ -206,13 +206,17 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
+    sched_fence();
     pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);
+    sched_fence();
     pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
@@ -237,15 +241,19 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
+    if constexpr (!SAVE) sched_fence();
     pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
                             my_q);
+    if constexpr (!SAVE) sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
+    if constexpr (!SAVE) sched_fence();
     pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
                            my_q);
+    if constexpr (!SAVE) sched_fence();
     store_tile(sm[(kt + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
@@ -363,7 +371,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
     const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
     ld.load(nk * BN, false, nxt);
+    sched_fence();
     pass1_tile<true>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(n + 1) & 1], nxt, tid, false);
     __syncthreads();
   }
@@ -385,8 +395,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
     const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
     ld.load(nk * BN, true, nxt);
+    sched_fence();
     pass2_tile<true, false>(sm[n & 1], cur * BN, krow, lane, qe, qo, c, sig, Les, Los, 1.f, 1.f, o, dummy, dummy, S,
                             causal, qw, my_q);
+    sched_fence();
     store_tile(sm[(n + 1) & 1], nxt, tid, true);
     __syncthreads();
   }
