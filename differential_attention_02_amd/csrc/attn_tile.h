@@ -21,26 +21,39 @@ __device__ __forceinline__ int k_row_perm(int i) {
 // half h.
 __device__ __forceinline__ int key_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
 
-// Online log2-domain max/sum update of one lane's share of a map's row.
+// Online log2-domain sum of one lane's share of a map's row against a lazily
+// moved reference m: the sub-tile's terms 2^(s c - m) are summed directly,
+// and only when their sum leaves [0, 2^64] (a score more than 64 above the
+// reference, or no reference yet) is the reference raised to the sub-tile's
+// top score and the sum redone.  l is always relative to m; m need not be the
+// row's top score, only within 64 of it, so a map's weights 2^(s c - L) are
+// bounded by 1, not by 2^(m - L).
 __device__ __forceinline__ void lse_update(const f32x16 &s, float c, float &m, float &l) {
-  float mx = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  const float mn = fmaxf(m, mx * c);
-  const float ms = mn == kNegInf ? 0.f : mn;
-  // Four partial sums, each started from its first term (no additions of 0).
   float a[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) a[r] = fast_exp2(fmaf(s[r], c, -ms));
-  a[0] = fmaf(l, fast_exp2(m - ms), a[0]);
+  for (int r = 0; r < 4; ++r) a[r] = fast_exp2(fmaf(s[r], c, -m));
 #pragma unroll
-  for (int r = 4; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -ms));
-  l = (a[0] + a[1]) + (a[2] + a[3]);
-  m = mn;
+  for (int r = 4; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -m));
+  float t = (a[0] + a[1]) + (a[2] + a[3]);
+  if (!(t <= 0x1p64f)) {  // also taken for NaN terms (m still -inf)
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float mn = fmaxf(m, mx * c);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    l = m == kNegInf ? 0.f : l * fast_exp2(m - ms);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = fast_exp2(fmaf(s[r], c, -ms));
+#pragma unroll
+    for (int r = 4; r < 16; ++r) a[r & 3] += fast_exp2(fmaf(s[r], c, -ms));
+    t = (a[0] + a[1]) + (a[2] + a[3]);
+    m = mn;
+  }
+  l += t;
 }
 
-// Full-row top score M and log2 partition function L from the two
-// half-waves' (m, l).
+// Full-row reference M (the larger of the two half-waves' references) and log2
+// partition function L from the two half-waves' (m, l).
 __device__ __forceinline__ void lse_finish(float m, float l, float &M, float &L) {
   const float mo = other_half(m), lo = other_half(l);
   M = fmaxf(m, mo);

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
   float M1, L1, M2, L2;
   lse_finish(m1, l1, M1, L1);
   lse_finish(m2, l2, M2, L2);
-  const float sg = row_scale_log2(fast_exp2(M1 - L1) + fabsf(lam) * fast_exp2(M2 - L2));
+  const float sg = row_scale_log2(1.f + fabsf(lam));  // a map's weights are at most 1
   const float L1s = L1 - sg, L2s = L2 - sg;
 
   // ---------------- pass 2: O = (P1 / l1 - lambda P2 / l2) V ----------------

@@ -13,7 +13,8 @@
 //
 // Two passes over 64-key tiles staged through LDS:
 //   pass 1 streams K1, K2 and computes, per map and query row, the log2
-//          partition function L_m (online max and sum of 2^(s c));
+//          partition function L_m (online sum of 2^(s c) against a reference
+//          that moves only when a score tops it by more than 64);
 //   pass 2 streams K1, K2, V, recomputes the scores and forms the combined,
 //          already normalised weight W = 2^(s1 c - L1) - lambda 2^(s2 c - L2)
 //          in float32, rounds W once to fp16 and accumulates O = W V.
@@ -22,12 +23,11 @@
 // lambda is near 1 the two maps cancel and per-map rounding error would be
 // amplified by 1 / (1 - lambda).  W and V enter the PV product as fp16 (V is
 // converted exactly from bf16 on its way into LDS), because bf16's 8-bit
-// significand alone would spend most of the error budget.  Each row's W is
-// scaled by a power of two 2^sigma chosen from pass 1 (the largest weight is
-// at most 2^(M1 - L1) + |lambda| 2^(M2 - L2), M the row's top score), so it
-// sits just under 2^15 and even 64K-key rows of ~1/65536 weights stay in
-// fp16's normal range; sigma folds into L for free and the epilogue removes
-// it exactly.  Matrix-core work per (query, key) pair is 4 QK^T products of
+// significand alone would spend most of the error budget.  W is scaled by a
+// power of two 2^sigma with (1 + |lambda|) 2^sigma just under 2^15 (a map's
+// weights are at most 1, so |W| <= 1 + |lambda|); even 64K-key rows of
+// ~1/65536 weights then stay in fp16's normal range.  sigma folds into L for
+// free and the epilogue removes it exactly.  Matrix-core work per (query, key) pair is 4 QK^T products of
 // width 64 plus one PV product of width 128: 768 flop, the same as a one-pass
 // form with two PV products.
 //
@@ -313,10 +313,11 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
   float M1, L1, M2, L2;
   lse_finish(m1, l1, M1, L1);
   lse_finish(m2, l2, M2, L2);
-  // Row scale 2^sg for the fp16 weights (and 2^sg2 for the saved second map).
-  const float sg = row_scale_log2(fast_exp2(M1 - L1) + fabsf(lam) * fast_exp2(M2 - L2));
+  // Scale 2^sg for the fp16 weights (and 2^sg2 for the saved second map): a
+  // map's weights are at most 1, so |W| <= 1 + |lambda|.
+  const float sg = row_scale_log2(1.f + fabsf(lam));
   const float L1s = L1 - sg, L2s = L2 - sg;
-  const float sg2 = SAVE ? row_scale_log2(fast_exp2(M2 - L2)) : 0.f;
+  const float sg2 = SAVE ? row_scale_log2(1.f) : 0.f;
   const float L2s2 = L2 - sg2;
 
   // ---------------- pass 2: O = (P1 / l1 - lambda P2 / l2) V ----------------

@@ -20,8 +20,8 @@
 // loads, one barrier per tile), as in the V1 forward: pass 1 computes each
 // map's log2 partition function per row; pass 2 recomputes the scores, forms
 // the combined weight W = 2^(s_e c - L_e) - sigmoid(lambda) 2^(s_o c - L_o) in
-// float32, scales it by a power of two per row (largest weight just under
-// 2^15), rounds it once to fp16 and accumulates W V with fp16 V.  Rounding the
+// float32, scales it by a power of two ((1 + sigmoid(lambda)) 2^sigma just
+// under 2^15, a head's weights being at most 1), rounds it once to fp16 and accumulates W V with fp16 V.  Rounding the
 // combined weight keeps the error proportional to the combined map when
 // sigmoid(lambda) is near 1 and the two heads nearly cancel.  Scores are
 // computed transposed (S^T = K Q^T, lane = query); K rows are read in the
@@ -223,11 +223,12 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   float Me, Le, Mo, Lo;
   lse_finish(me, le, Me, Le);
   lse_finish(mo, lo, Mo, Lo);
-  const float sg = row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo));
+  // A head's weights are at most 1, so |W| <= 1 + sigma(lambda).
+  const float sg = row_scale_log2(1.f + sig);
   const float Les = Le - sg, Los = Lo - sg;
-  // Each head's own weights just under 2^15 for A_even and A_odd.
-  const float sge = SAVE ? row_scale_log2(fast_exp2(Me - Le)) : 0.f;
-  const float sgo = SAVE ? row_scale_log2(fast_exp2(Mo - Lo)) : 0.f;
+  // Each head's own weights (at most 1) scaled just under 2^15 for A_even and A_odd.
+  const float sge = SAVE ? row_scale_log2(1.f) : 0.f;
+  const float sgo = SAVE ? row_scale_log2(1.f) : 0.f;
   const float fe = fast_exp2(sge - sg), fo = fast_exp2(sgo - sg);
 
   // ---------------- pass 2: O = (P_e - sigmoid(lambda) P_o) V ----------------
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   lse_finish(me, le, Me, Le);
   lse_finish(mo, lo, Mo, Lo);
   const bool live = Le != kNegInf;  // the row saw at least one key (both heads see the same keys)
-  const float sg = live ? row_scale_log2(fast_exp2(Me - Le) + sig * fast_exp2(Mo - Lo)) : 0.f;
+  const float sg = live ? row_scale_log2(1.f + sig) : 0.f;
   const float Les = live ? Le - sg : __builtin_inff(), Los = live ? Lo - sg : __builtin_inff();
 
   // ---------------- pass 2 ----------------
