@@ -501,7 +501,9 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 200 untimed launches by default: after 20 (8 ms of work at 4K) the clock had not settled and the
+    # 4K forward read ~5 % below its steady rate.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["prefill_4k", "prefill_64k", "train_8k", "v2_decode", "v2_prefill_4k",
                                        "v2_train_4k", "v1_decode", "prefill_4k_fp8", "v2_sparse_4k"],
                     default=None,
