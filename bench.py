@@ -78,6 +78,8 @@ FWD_SOURCES = ["differential_attention_02_amd/csrc/fwd_mfma.hip", "differential_
 V2P_SOURCES = ["differential_attention_02_amd/csrc/fwd_v2.hip", "differential_attention_02_amd/csrc/attn_tile.h",
                "differential_attention_02_amd/csrc/common.h"]
 DEC_SOURCES = ["differential_attention_02_amd/csrc/decode.hip", "differential_attention_02_amd/csrc/common.h"]
+FP8_SOURCES = ["differential_attention_02_amd/csrc/fwd_fp8.hip", "differential_attention_02_amd/csrc/attn_tile.h",
+               "differential_attention_02_amd/csrc/common.h"]
 
 
 def _time_launches(launch, steps, warmup, per_launch=None):
@@ -625,8 +627,10 @@ def main(argv=None) -> int:
         "config": {"workload": "prefill_4k with Q1, K1, Q2, K2 quantised per row to fp8 e4m3 (power-of-two absmax "
                                "scale) inside every step; score products on scaled fp8 matrix instructions"},
         "roofline": {"bound": "mfma", "achieved": f8["event_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": f8["event_tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
-                     "note": "algorithmic 768 flop per pair against the bf16/fp16 peak (the PV product stays fp16)"},
+                     "frac": f8["event_tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": _traffic_from_profile("fwd_fp8_prefill_4k_pmc.md", FP8_SOURCES),
+                     "note": "algorithmic 768 flop per pair against the bf16/fp16 peak (the PV product stays fp16); "
+                             "traffic is the forward kernel's, per launch (the quantisation kernel not counted)"},
         "median_ms": f8["median_ms"], "min_ms": f8["min_ms"],
     }
     v1d = _gpu_v1_decode(args.steps, args.warmup)
