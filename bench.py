@@ -80,6 +80,8 @@ V2P_SOURCES = ["differential_attention_02_amd/csrc/fwd_v2.hip", "differential_at
 DEC_SOURCES = ["differential_attention_02_amd/csrc/decode.hip", "differential_attention_02_amd/csrc/common.h"]
 FP8_SOURCES = ["differential_attention_02_amd/csrc/fwd_fp8.hip", "differential_attention_02_amd/csrc/attn_tile.h",
                "differential_attention_02_amd/csrc/common.h"]
+BWD_SOURCES = ["differential_attention_02_amd/csrc/bwd.hip", "differential_attention_02_amd/csrc/common.h"]
+V2B_SOURCES = ["differential_attention_02_amd/csrc/bwd_v2.hip", "differential_attention_02_amd/csrc/common.h"]
 
 
 def _time_launches(launch, steps, warmup, per_launch=None):
@@ -583,7 +585,8 @@ def main(argv=None) -> int:
                          "ms_per_step": tr["ms_per_step"], "frac_of_bf16_peak": tr["tflops"] / PEAK_BF16_TFLOPS,
                          "roofline": {"bound": "mfma", "achieved": tr["event_tflops"], "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": tr["event_tflops"] / PEAK_BF16_TFLOPS,
-                                      "traffic": None},
+                                      "traffic": _traffic_from_profile("train_step_train_8k_pmc.md", BWD_SOURCES),
+                                      "note": "traffic is the dK/dV kernel's (the step's longest), per launch"},
                          "median_ms": tr["median_ms"], "min_ms": tr["min_ms"]}
     dec = _gpu_decode(args.steps, args.warmup)
     dec_traffic = _traffic_from_profile("decode_split_v2_decode_pmc.md", DEC_SOURCES)
@@ -651,7 +654,8 @@ def main(argv=None) -> int:
                                                    "saves then backward"},
                             "roofline": {"bound": "mfma", "achieved": v2t["event_tflops"], "peak": PEAK_BF16_TFLOPS,
                                          "unit": "TFLOP/s", "frac": v2t["event_tflops"] / PEAK_BF16_TFLOPS,
-                                         "traffic": None},
+                                         "traffic": _traffic_from_profile("v2_train_step_v2_train_4k_pmc.md", V2B_SOURCES),
+                                         "note": "traffic is the dK/dV kernel's (the step's longest), per launch"},
                             "median_ms": v2t["median_ms"], "min_ms": v2t["min_ms"]}
     cpu = None
     extra["v2_decode"]["median_ms"], extra["v2_decode"]["min_ms"] = dec["median_ms"], dec["min_ms"]
