@@ -106,3 +106,28 @@ def test_train_8k_full():
         ref = _ref(inp, layer=12, causal=True, norm=True, eps=1e-5, bh=bh)
         _compare(g, ref, f"train_8k b{bh[0]} h{bh[1]}", bh=bh, with_lambda=False)
     assert np.isfinite(g["dlambda"].cpu().numpy()).all()
+
+
+def test_bwd_strided_views():
+    """Q1, K1, Q2, K2, V as views into one packed per-token projection
+    [B, S, H, 4 d + dv] and the upstream gradient as a view into a wider
+    buffer: the kernels follow the strides (forward with saves, then backward)."""
+    _note("bwd strided views")
+    inp = workloads.make_attn_inputs("train_8k", seed=25, batch=2, seqlen=300, heads=3)
+    Bn, S, H, d = inp["q1"].shape
+    dv = inp["v"].shape[-1]
+    packed = torch.empty((Bn, S, H, 4 * d + dv), dtype=torch.bfloat16)
+    for i, k in enumerate(("q1", "k1", "q2", "k2")):
+        packed[..., d * i:d * (i + 1)] = inp[k]
+    packed[..., 4 * d:] = inp["v"]
+    dyw = torch.full((Bn, S, H, dv + 8), 3.0, dtype=torch.bfloat16)
+    dyw[..., 8:] = inp["dy"]
+    pc, dyc = packed.cuda(), dyw.cuda()
+    x = [pc[..., d * i:d * (i + 1)] for i in range(4)] + [pc[..., 4 * d:]]
+    assert not any(t.is_contiguous() for t in x)
+    vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    li = B.lambda_init(12)
+    _, saves = B.fwd(*x, lambda_init=li, lambda_vecs=vecs, causal=True, norm=True, eps=1e-5, save=True)
+    g = B.bwd(*x, dyc[..., 8:], saves, lambda_init=li, lambda_vecs=vecs, causal=True, norm=True)
+    torch.cuda.synchronize()
+    _compare(g, _ref(inp, layer=12, causal=True, norm=True, eps=1e-5), "bwd strided views")

@@ -155,3 +155,23 @@ def test_full_workload_slices():
     worst = np.abs(dk.sum(axis=1)).max() / (rms * np.sqrt(cfg.seqlen))
     print(f"[parity] v2 bwd sum_keys dK / (rms sqrt(S)) = {worst:.3e}", flush=True)
     assert worst < 0.05
+
+
+def test_grads_strided_views():
+    """q, k, v as views into one packed [B, S, Hq + 2 Hkv, D] projection and the
+    upstream gradient as a view into a wider buffer (forward with saves, then
+    backward, both following the strides)."""
+    _note("v2 bwd strided views")
+    inp = _inputs(53, batch=2, seqlen=170, q_heads=4, kv_heads=2)
+    d = _dout(inp, 8)
+    packed = torch.cat([inp["q"], inp["k"], inp["v"]], dim=2).cuda()
+    qv, kv, vv = packed[:, :, :4], packed[:, :, 4:6], packed[:, :, 6:8]
+    dw = torch.zeros((2, 170, 3, 128), dtype=torch.bfloat16)
+    dw[:, :, 1:] = d
+    dv_ = dw.cuda()[:, :, 1:]
+    assert not (qv.is_contiguous() or kv.is_contiguous() or dv_.is_contiguous())
+    lam = inp["lam"].cuda()
+    _, saves = B.v2_fwd(qv, kv, vv, lam, causal=True, save=True)
+    g = B.v2_bwd(qv, kv, vv, lam, dv_, saves, causal=True)
+    torch.cuda.synchronize()
+    _check_grads(g, _ref(inp, d), "v2 bwd strided views")
