@@ -80,3 +80,20 @@ def test_full_workload_sampled_rows():
     rows = np.array([0, 1, 63, 64, 127, 128, 1000, 2047, 3001, 4095])
     ref = _ref(inp, eps=1e-8, rows=rows)
     assert_bf16_rows(out[:, torch.as_tensor(rows, device=out.device)], ref, "fp8 forward full workload sampled")
+
+
+def test_forward_strided_views():
+    """Q1, K1, Q2, K2, V as views into one packed per-token projection
+    [B, S, H, 4 d + dv]: the quantisation and the forward follow the strides."""
+    _note("fp8 strided views")
+    inp = workloads.make_attn_inputs("prefill_4k", seed=9, batch=2, seqlen=333, heads=3)
+    Bn, S, H, d = inp["q1"].shape
+    packed = torch.cat([inp[k] for k in NAMES], dim=-1).cuda()
+    offs = [0, d, 2 * d, 3 * d, 4 * d, packed.shape[-1]]
+    x = [packed[..., offs[i]:offs[i + 1]] for i in range(5)]
+    assert not any(t.is_contiguous() for t in x)
+    vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    y = B.fwd_fp8(*x, lambda_init=B.lambda_init(inp["cfg"].layer), lambda_vecs=vecs, causal=True, norm=True,
+                  eps=1e-5)
+    torch.cuda.synchronize()
+    assert_bf16_rows(y, _ref(inp), "fp8 strided views")

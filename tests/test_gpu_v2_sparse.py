@@ -170,3 +170,21 @@ def test_longest_lists_match_dense_kernel():
     torch.cuda.synchronize()
     assert torch.equal(out2, out3)
     assert torch.isfinite(out2.float()).all()
+
+
+def test_strided_views():
+    """q, k, v as views into one packed [B, S, Hq + 2 Hkv, D] projection and the
+    output written into a wider buffer whose other heads stay untouched."""
+    _note("v2 sparse strided")
+    inp = _inputs(8, batch=2, seqlen=400, q_heads=4, kv_heads=2)
+    m = _mask(inp, 8, budget=3, local=1)
+    packed = torch.cat([inp["q"], inp["k"], inp["v"]], dim=2).cuda()
+    qv, kv, vv = packed[:, :, :4], packed[:, :, 4:6], packed[:, :, 6:8]
+    idx, cnt = B.v2_block_lists(m.cuda())
+    wide = torch.full((2, 400, 4, 128), 5.0, dtype=torch.bfloat16, device="cuda")
+    out = wide[:, :, 1:3]
+    B.v2_fwd_sparse(qv, kv, vv, inp["lam"].cuda(), idx, cnt, causal=True, out=out)
+    torch.cuda.synchronize()
+    assert_bf16_rows(out, _ref(inp, m), "v2 sparse strided")
+    w = wide.cpu()
+    assert torch.all(w[:, :, 0] == 5.0) and torch.all(w[:, :, 3] == 5.0)
