@@ -90,3 +90,21 @@ def test_v2_decode_full():
         ref = oracle.v2_decode(as_f64(inp["q"][sl]), as_f64(inp["k_cache"][sl]), as_f64(inp["v_cache"][sl]), lam)
         assert_bf16_rows(out[sl], ref, f"v2_decode batches {b}..{b + 7}")
     assert np.isfinite(out).all()
+
+
+def test_strided_views():
+    """Queries as a view into a wider per-token buffer and the K and V caches as
+    views into one packed [B, L, 2 Hkv, D] cache (K heads first), with ragged
+    sequence lengths; the kernels follow the strides."""
+    _note("decode strided")
+    inp = _case(5, 3, 8, 4, 128, 900, torch.bfloat16)
+    qw = torch.zeros((3, 10, 128), dtype=torch.bfloat16)
+    qw[:, 1:9] = inp["q"]
+    kv = torch.cat([inp["k_cache"], inp["v_cache"]], dim=2).cuda()
+    q, k, v = qw.cuda()[:, 1:9], kv[:, :, :4], kv[:, :, 4:]
+    assert not (k.is_contiguous() or v.is_contiguous())
+    lens = [900, 257, 33]
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = B.v2_decode(q, k, v, inp["lam"].cuda(), seqlens=sl)
+    torch.cuda.synchronize()
+    assert_bf16_rows(out, _ref(inp, lens), "decode strided")
