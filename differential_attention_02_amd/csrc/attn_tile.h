@@ -105,6 +105,16 @@ __device__ __forceinline__ void pv_step_tile(const f16 *vt, int sub, int lane, c
 // moved the stores, and the wait for the loads, ahead of the softmax work).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Masks one map's scores of keys past the sequence end or (causal) past the
+// query.
+__device__ __forceinline__ void mask_scores1(f32x16 &s, int sb, int h, int S, bool causal, int my_q) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = sb + key_of_reg(r, h);
+    if (key >= S || (causal && key > my_q)) s[r] = kNegInf;
+  }
+}
+
 // Masks the scores of keys past the sequence end or (causal) past the query.
 __device__ __forceinline__ void mask_scores(f32x16 &s1, f32x16 &s2, int sb, int h, int S, bool causal, int my_q) {
 #pragma unroll

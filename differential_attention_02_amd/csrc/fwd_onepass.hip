@@ -1,0 +1,415 @@
+// One-pass causal/non-causal inference forward of multi-head differential
+// attention on gfx950 matrix cores: bf16 storage, d = 64, dv = 128.
+//
+// The operator (glossary page "Differential Transformer", section "How
+// differential attention works"; news write-up, multi-head section):
+//   Y = RMSNorm_head((softmax(s Q1 K1^T) - lambda softmax(s Q2 K2^T)) V) (1 - lambda_init)
+//
+// One sweep over the keys with two running softmax states per query row.
+// With per-map references m1, m2 (log2 domain) and e_m = 2^(s_m c - m_m), the
+// kernel accumulates, per row,
+//   l1 = sum e1,  l2 = sum e2,  X = sum (e1 - kappa e2) V,  Y = sum e2 V,
+// and finishes with O = X / l1 + (kappa / l1 - lambda / l2) Y, which is exact
+// for any kappa.  kappa is kept within 2^-7 of lambda l1 / l2 (when it drifts,
+// X += (kappa_old - kappa_new) Y re-bases it), so the fp16-rounded weight
+// e1 - kappa e2 is l1 (p1 - lambda' p2) with lambda' ~ lambda: its rounding
+// error is proportional to the combined map rather than to each map, which
+// matters when lambda is near 1 and the two maps cancel; the Y term enters
+// only with a coefficient of at most ~2^-7 lambda / l2.  The references move
+// lazily: a reference is raised to the sub-tile's top score only when that
+// tops it by more than 2^8 (so no term exceeds 2^8), and by whole powers of
+// two when a row's merged sum passes bnd = 2^14 / (1 + |lambda|) (many keys
+// near the reference); X or Y, l and kappa are rescaled with it.  Bounding
+// l1 and l2 by bnd keeps every weight inside fp16 (e_m <= l_m and
+// |kappa e2| <~ |lambda| l1).
+// Matrix-core work per (query, key) pair: 2 QK^T products of width 64 and
+// 2 PV products of width 128 (768 flop); two exponentials.
+//
+// Work split.  One workgroup of 8 waves (two per SIMD) owns 256 query rows of
+// one (batch, head); each wave owns a 32-row block, the two waves sharing a
+// SIMD holding one early and one late block so the causal diagonal is shared
+// out evenly, and the second of them running half a sub-tile behind the
+// first (see the key loop).  Causal tiles are issued longest first and consecutive workgroup
+// ids walk the (batch, head) index (workgroups are dealt round-robin to the 8
+// XCDs, so a head's query tiles share one L2).
+//
+// Scores are computed transposed, S^T = K Q^T (keys on rows): a lane owns one
+// query column and its score registers are already the B operand of the PV
+// product O^T = V^T W^T (K rows read in the permuted order of the shared tile
+// helpers).  The two half-waves hold disjoint keys of the same rows; every
+// decision (references, kappa) is taken on merged sums, so both halves agree.
+// V is converted bf16 -> fp16 on its way into LDS (exact for magnitudes in
+// [2^-14, 65504]).
+#include "attn_tile.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int D = 64, DV = 128, BN = 64, NW = 8, NT = 64 * NW, OBM = 32 * NW;
+constexpr int NBUF = 3;  // LDS tile buffers
+constexpr int KST = D + 8;   // LDS row stride of a K tile, bf16 elements (144 B)
+constexpr int VST = DV + 32; // LDS row stride of the V tile, fp16 elements (320 B)
+
+struct Smem {
+  bf16 k1[BN * KST];
+  bf16 k2[BN * KST];
+  f16 v[BN * VST];
+};
+
+// One thread's share of a 64-key tile: KC 16-byte chunks of K1 and of K2,
+// VC of V.
+constexpr int KC = 8 * BN / NT, VC = 16 * BN / NT;
+struct Stage {
+  u32x4 k1[KC], k2[KC], v[VC];
+};
+
+// Raw buffer loads; each slice's buffer range ends at its last key row, so
+// rows past the sequence end read as zeros.
+struct Loader {
+  __amdgpu_buffer_rsrc_t rk1, rk2, rv;
+  uint32_t ko, vo;        // this thread's byte offsets inside a tile
+  uint32_t kstep, vstep;  // bytes per key row
+
+  __device__ __forceinline__ void init(const bf16 *k1, const bf16 *k2, const bf16 *v, int64_t ks, int64_t vs,
+                                       int S, int tid) {
+    const uint32_t kbytes = (uint32_t)((int64_t)(S - 1) * ks * 2 + D * 2);
+    const uint32_t vbytes = (uint32_t)((int64_t)(S - 1) * vs * 2 + DV * 2);
+    rk1 = __builtin_amdgcn_make_buffer_rsrc((void *)k1, 0, kbytes, 0x00020000);
+    rk2 = __builtin_amdgcn_make_buffer_rsrc((void *)k2, 0, kbytes, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, 0, vbytes, 0x00020000);
+    kstep = (uint32_t)(ks * 2);
+    vstep = (uint32_t)(vs * 2);
+    ko = (uint32_t)(tid >> 3) * kstep + (tid & 7) * 16;
+    vo = (uint32_t)(tid >> 4) * vstep + (tid & 15) * 16;
+  }
+
+  __device__ __forceinline__ void load(int kbase, Stage &r) const {
+    const uint32_t kb = (uint32_t)kbase * kstep, vb = (uint32_t)kbase * vstep;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int o = (int)(ko + kb + i * (NT / 8) * kstep);
+      r.k1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, o, 0, 0));
+      r.k2[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk2, o, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < VC; ++i)
+      r.v[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(vo + vb + i * (NT / 16) * vstep), 0, 0));
+  }
+};
+
+__device__ __forceinline__ void store_stage(Smem &sm, const Stage &r, int tid) {
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int row = (tid >> 3) + i * (NT / 8), col = (tid & 7) * 8;
+    *(u32x4 *)(sm.k1 + row * KST + col) = r.k1[i];
+    *(u32x4 *)(sm.k2 + row * KST + col) = r.k2[i];
+  }
+#pragma unroll
+  for (int i = 0; i < VC; ++i) {
+    const int row = (tid >> 4) + i * (NT / 16), col = (tid & 15) * 8;
+    const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]), bf16x2_to_f16x2(r.v[i][2]),
+                     bf16x2_to_f16x2(r.v[i][3])};
+    *(u32x4 *)(sm.v + row * VST + col) = h;
+  }
+}
+
+// Running state of one query row, held by both lanes of the row (the
+// references and kappa are identical in the two; l1, l2 are each lane's share).
+struct RowState {
+  float m1, m2, l1, l2, kap;
+};
+
+// e[r] = 2^(s[r] c - m); returns the lane's sum.
+__device__ __forceinline__ float exps16(const f32x16 &s, float c, float m, float *e) {
+  float a[4];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s[r], c, -m));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) a[r] = (e[r] + e[r + 4]) + (e[r + 8] + e[r + 12]);
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// S^T of one map over one 32-key sub-tile.
+__device__ __forceinline__ f32x16 score_map(const bf16 *ktile, int sub, int krow, int h, const bf16x8 *qf) {
+  const bf16 *a = ktile + (sub * 32 + krow) * KST + 8 * h;
+  f32x16 s = {};
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) s = mfma32(*(const bf16x8 *)(a + kc * 16), qf[kc], s);
+  return s;
+}
+
+// Merged (both half-waves) top scaled score of one map's sub-tile.
+__device__ __forceinline__ float top_score(const f32x16 &s, float c) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx *= c;
+  return fmaxf(mx, other_half(mx));
+}
+
+// Moves a reference to mn >= m; returns the factor for what was accumulated
+// against the old one (0 when it was -inf: nothing was).
+__device__ __forceinline__ float move_ref(float &m, float mn) {
+  const float a = m == kNegInf ? 0.f : fast_exp2(m - mn);
+  m = mn;
+  return a;
+}
+
+// Scores of both maps over one 32-key sub-tile and the softmax bookkeeping;
+// returns the fp16 B operands of the sub-tile's two PV products
+// (w = e1 - kappa e2, and e2).
+template <bool MASKED>
+__device__ __forceinline__ void sub_softmax(const Smem &sm, int sub, int sb, int krow, int lane, const bf16x8 *q1f,
+                                            const bf16x8 *q2f, float c, float lam, float bnd, RowState &st,
+                                            f32x16 *x, f32x16 *y, int S, bool causal, int my_q, f16x8 *wb,
+                                            f16x8 *eb) {
+  const int h = lane >> 5;
+  f32x16 s1 = score_map(sm.k1, sub, krow, h, q1f);
+  f32x16 s2 = score_map(sm.k2, sub, krow, h, q2f);
+  if constexpr (MASKED) {
+    mask_scores1(s1, sb, h, S, causal, my_q);
+    mask_scores1(s2, sb, h, S, causal, my_q);
+  }
+  // A reference moves only when a score tops it by more than 2^8 (or there is
+  // none yet), so no term exceeds 2^8.
+  const float mx1 = top_score(s1, c), mx2 = top_score(s2, c);
+  if (mx1 > st.m1 + 8.f || mx2 > st.m2 + 8.f) {  // rare; both lanes of a row agree
+    const float a1 = mx1 > st.m1 + 8.f ? move_ref(st.m1, mx1) : 1.f;
+    const float a2 = mx2 > st.m2 + 8.f ? move_ref(st.m2, mx2) : 1.f;
+    st.l1 *= a1;
+    st.l2 *= a2;
+    // Fold kappa Y back into X first (X becomes sum e1 V, kappa 0): scaling
+    // kappa by 1 / a2 instead could overflow when map 2's reference jumps far.
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      x[ct] = (x[ct] + st.kap * y[ct]) * a1;
+      y[ct] *= a2;
+    }
+    st.kap = 0.f;
+  }
+  float e1[16], e2[16];
+  float t1 = exps16(s1, c, st.m1 == kNegInf ? 0.f : st.m1, e1);
+  float t2 = exps16(s2, c, st.m2 == kNegInf ? 0.f : st.m2, e2);
+  float L1 = st.l1 + t1, L2 = st.l2 + t2;
+  L1 += other_half(L1);
+  L2 += other_half(L2);
+  if (L1 > bnd || L2 > bnd) {  // rare; both lanes of a row agree (merged sums)
+    // Many keys near the reference: raising it by whole powers of two (an
+    // exact rescale) brings the merged sum to at most bnd / 2.
+    if (L1 > bnd) {
+      const float k = ceilf(log2f(L1 / bnd)) + 1.f, f = fast_exp2(-k);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e1[r] *= f;
+      t1 *= f;
+      st.l1 *= f;
+      st.kap *= f;
+      st.m1 += k;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) x[ct] *= f;
+    }
+    if (L2 > bnd) {
+      const float k = ceilf(log2f(L2 / bnd)) + 1.f, f = fast_exp2(-k);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e2[r] *= f;
+      t2 *= f;
+      st.l2 *= f;
+      st.kap *= fast_exp2(k);
+      st.m2 += k;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) y[ct] *= f;
+    }
+    L1 = st.l1 + t1;
+    L2 = st.l2 + t2;
+    L1 += other_half(L1);
+    L2 += other_half(L2);
+  }
+  st.l1 += t1;
+  st.l2 += t2;
+  // kappa tracks lambda L1 / L2 (merged sums including this sub-tile).
+  const float ks = L2 > 0.f ? lam * L1 * __builtin_amdgcn_rcpf(L2) : 0.f;
+  if (fabsf(ks - st.kap) > 0x1p-7f * fabsf(ks)) {
+    const float d = st.kap - ks;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) x[ct] += d * y[ct];
+    st.kap = ks;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e1[r] = fmaf(-st.kap, e2[r], e1[r]);
+  wb[0] = pack8(e1);
+  wb[1] = pack8(e1 + 8);
+  eb[0] = pack8(e2);
+  eb[1] = pack8(e2 + 8);
+}
+
+// X^T += V^T W^T and Y^T += V^T E^T over one sub-tile.
+__device__ __forceinline__ void sub_pv(const Smem &sm, int sub, int lane, const f16x8 *wb, const f16x8 *eb,
+                                       f32x16 *x, f32x16 *y) {
+  const int h = lane >> 5, j = lane & 15, half16 = (lane >> 4) & 1;
+#pragma unroll
+  for (int kc2 = 0; kc2 < 2; ++kc2) {
+    const int key0 = sub * 32 + kc2 * 16 + 8 * h + (j >> 2);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f16 *p = sm.v + key0 * VST + ct * 32 + 16 * half16 + 4 * (j & 3);
+      const f16x4 lo = lds_read_tr16(p);
+      const f16x4 hi = lds_read_tr16(p + 4 * VST);
+      const f16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      x[ct] = mfma32(va, wb[kc2], x[ct]);
+      y[ct] = mfma32(va, eb[kc2], y[ct]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
+  __shared__ Smem sm[NBUF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 31, h = lane >> 5;
+  const int BH = p.B * p.H;
+  const int n_qt = (p.S + OBM - 1) / OBM;
+  const int bh = blockIdx.x % BH;
+  const int qt_i = blockIdx.x / BH;
+  const int qt = p.causal ? n_qt - 1 - qt_i : qt_i;
+  const int b = bh / p.H, hd = bh % p.H;
+  const int q0 = qt * OBM;
+  // Waves w and w + 4 share a SIMD: give them row blocks w and 7 - w.
+  const int blk = wave < 4 ? wave : 11 - wave;
+  const int qw = q0 + 32 * blk, my_q = qw + ln;
+  const int S = p.S;
+  const bool causal = p.causal != 0;
+
+  const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
+  if (blockIdx.x == 0 && tid == 0 && p.lambda_out) *p.lambda_out = lam;
+  const float c = p.scale * kLog2e;
+  const float bnd = 0x1p14f / (1.f + fabsf(lam));
+
+  Loader ld;
+  ld.init((const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h, (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h,
+          (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h, p.ks_s, p.vs_s, S, tid);
+
+  bf16x8 q1f[4], q2f[4];
+  {
+    const bf16 *q1 = (const bf16 *)p.q1 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
+    const bf16 *q2 = (const bf16 *)p.q2 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      q1f[kc] = my_q < S ? *(const bf16x8 *)(q1 + kc * 16) : bf16x8{};
+      q2f[kc] = my_q < S ? *(const bf16x8 *)(q2 + kc * 16) : bf16x8{};
+    }
+  }
+
+  const int kend = causal ? min(S, q0 + OBM) : S;
+  const int n_kt = (kend + BN - 1) / BN;
+  // Tiles every row of the workgroup sees in full (no mask, no tail).
+  const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
+  const int krow = k_row_perm(ln);
+
+  f32x16 x[4], y[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    x[ct] = f32x16{};
+    y[ct] = f32x16{};
+  }
+  RowState st = {kNegInf, kNegInf, 0.f, 0.f, 0.f};
+
+  // Three LDS buffers: tile kt is read from buffer kt % 3 while tile kt + 1
+  // (loaded into registers one tile ahead) is stored into buffer (kt + 1) % 3.
+  // The waves of the second group (one per SIMD) run half a sub-tile behind
+  // the first: they defer the PV products of each tile's second sub-tile to
+  // the start of the next tile (buffer (kt - 1) % 3, still intact), so that on
+  // every SIMD one wave's matrix work overlaps the other's softmax arithmetic
+  // instead of both waves reaching each phase together after the barrier.
+  const bool lag = wave >= 4;
+  bool pending = false;
+  f16x8 pw[2], pe[2];
+  int cur = 0, prv = NBUF - 1, nxb = 1;
+  Stage nxt;
+  ld.load(0, nxt);
+  store_stage(sm[0], nxt, tid);
+  __syncthreads();
+  for (int kt = 0; kt < n_full; ++kt) {
+    ld.load((kt + 1) * BN, nxt);  // past the end: the buffer range gives zeros
+    sched_fence();
+    if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);
+    {
+      f16x8 wb[2], eb[2];
+      sub_softmax<false>(sm[cur], 0, kt * BN, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
+      sub_pv(sm[cur], 0, lane, wb, eb, x, y);
+    }
+    sub_softmax<false>(sm[cur], 1, kt * BN + 32, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, pw,
+                       pe);
+    pending = lag;
+    if (!lag) sub_pv(sm[cur], 1, lane, pw, pe, x, y);
+    sched_fence();
+    store_stage(sm[nxb], nxt, tid);
+    __syncthreads();
+    prv = cur;
+    cur = nxb;
+    nxb = nxb == NBUF - 1 ? 0 : nxb + 1;
+  }
+  for (int kt = n_full; kt < n_kt; ++kt) {
+    ld.load((kt + 1) * BN, nxt);
+    sched_fence();
+    if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);
+    pending = false;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int sb = kt * BN + sub * 32;
+      if (sb >= S || (causal && sb > qw + 31)) continue;  // wave-uniform
+      f16x8 wb[2], eb[2];
+      if ((causal && sb + 31 > qw) || sb + 32 > S)
+        sub_softmax<true>(sm[cur], sub, sb, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
+      else
+        sub_softmax<false>(sm[cur], sub, sb, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
+      sub_pv(sm[cur], sub, lane, wb, eb, x, y);
+    }
+    sched_fence();
+    store_stage(sm[nxb], nxt, tid);
+    __syncthreads();
+    prv = cur;
+    cur = nxb;
+    nxb = nxb == NBUF - 1 ? 0 : nxb + 1;
+  }
+  if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);  // only when there was no masked tile
+
+  // O = X / L1 + (kappa / L1 - lambda / L2) Y; per-head RMSNorm x (1 - lambda_init).
+  const float L1 = st.l1 + other_half(st.l1);
+  const float L2 = st.l2 + other_half(st.l2);
+  const float i1 = 1.f / L1;
+  const float cy = st.kap * i1 - lam / L2;
+  float ss = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[ct][r] = fmaf(x[ct][r], i1, cy * y[ct][r]);
+      ss = fmaf(x[ct][r], x[ct][r], ss);
+    }
+  ss += other_half(ss);
+  const float rstd = p.norm ? 1.f / sqrtf(ss * (1.f / DV) + p.eps) : 1.f;
+  const float f = p.norm ? rstd * (1.f - p.lambda_init) : 1.f;
+  if (my_q < S) {
+    bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + hd * p.os_h;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = ct * 32 + 8 * g + 4 * h;
+        bf16x4 yv = {f2bf(x[ct][4 * g] * f), f2bf(x[ct][4 * g + 1] * f), f2bf(x[ct][4 * g + 2] * f),
+                     f2bf(x[ct][4 * g + 3] * f)};
+        *(bf16x4 *)(out + ch) = yv;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_onepass(const FwdParams &p, hipStream_t st) {
+  const int n_qt = (p.S + OBM - 1) / OBM;
+  dim3 grid(n_qt * p.B * p.H), block(NT);
+  hipLaunchKernelGGL(fwd_onepass_kernel, grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -108,8 +108,10 @@ struct V2BwdParams {
 
 // Reference vector-ALU forward: any supported (d, dv), f32 or bf16.
 hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipStream_t st);
-// Fused bf16 matrix-core forward, d = 64, dv = 128.
+// Fused bf16 matrix-core forward, d = 64, dv = 128: the one-pass kernel
+// without training saves, the two-pass kernel with them.
 hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st);
+hipError_t launch_fwd_onepass(const FwdParams &p, hipStream_t st);
 // The same forward with fp8 e4m3 score operands (per-row power-of-two absmax
 // scales); the workspace holds the codes and exponents.
 size_t fwd_fp8_workspace_bytes(int B, int S, int H);
