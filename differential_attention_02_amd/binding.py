@@ -125,6 +125,7 @@ SIGNATURES = {
     "diffattn_bwd_workspace_size": (c_sz, [ctypes.POINTER(BwdArgs)]),
     "diffattn_v2_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v2_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeArgs)]),
+    "diffattn_v2_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v1_decode": (ctypes.c_int, [ctypes.POINTER(V1DecodeArgs), c_vp]),
     "diffattn_v1_decode_workspace_size": (c_sz, [ctypes.POINTER(V1DecodeArgs)]),
     "diffattn_v2_fwd": (ctypes.c_int, [ctypes.POINTER(V2FwdArgs), c_vp]),
@@ -425,6 +426,15 @@ def decode_workspace_size(args: DecodeArgs) -> int:
 
 def decode_launch(args: DecodeArgs) -> None:
     _check(lib().diffattn_v2_decode(ctypes.byref(args), _stream()), "diffattn_v2_decode")
+
+
+DECODE_SCRATCH_BYTES = 32 << 20   # DIFFATTN_DECODE_SCRATCH_BYTES
+
+
+def decode_noalloc_launch(args: DecodeArgs) -> None:
+    """diffattn_v2_decode_noalloc: the split partials go to the library's fixed
+    per-GPU scratch (args.workspace is ignored)."""
+    _check(lib().diffattn_v2_decode_noalloc(ctypes.byref(args), _stream()), "diffattn_v2_decode_noalloc")
 
 
 def v2_decode(q, k_cache, v_cache, lam, *, seqlens=None, softmax_scale: float = 0.0,

@@ -546,18 +546,10 @@ size_t diffattn_v2_decode_workspace_size(const diffattn_v2_decode_args *a) {
   return diffattn::decode_workspace_bytes(a->batch, a->q_heads, a->head_dim, splits);
 }
 
-int diffattn_v2_decode(const diffattn_v2_decode_args *a, void *stream) {
-  g_last_error.clear();
-  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->batch < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0");
-  if (a->batch == 0) return DIFFATTN_OK;
-  int splits = 0;
-  int rc = check_decode(a, &splits);
-  if (rc) return rc;
-  const size_t need = diffattn::decode_workspace_bytes(a->batch, a->q_heads, a->head_dim, splits);
-  if (!a->workspace || a->workspace_bytes < need)
-    return fail(DIFFATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
-  if (!aligned16(a->workspace)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+static_assert(diffattn::kDecodeScratchBytes == DIFFATTN_DECODE_SCRATCH_BYTES, "scratch size and its header constant");
+
+// Launches a validated decode with its partials in `ws` (need bytes).
+static int run_decode(const diffattn_v2_decode_args *a, int splits, void *ws, void *stream) {
   diffattn::DecodeParams p{};
   p.q = a->q; p.k = a->k_cache; p.v = a->v_cache;
   p.qs_b = a->q_stride[0]; p.qs_h = a->q_stride[1];
@@ -570,9 +562,43 @@ int diffattn_v2_decode(const diffattn_v2_decode_args *a, void *stream) {
   p.chunk = (a->kv_len + splits - 1) / splits;
   if (p.chunk < 1) p.chunk = 1;
   p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
-  p.part_o = static_cast<float *>(a->workspace);
+  p.part_o = static_cast<float *>(ws);
   p.part_ml = p.part_o + (size_t)a->batch * a->q_heads * splits * a->head_dim;
   return hip_status(diffattn::launch_decode(p, a->dtype, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+int diffattn_v2_decode(const diffattn_v2_decode_args *a, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0");
+  if (a->batch == 0) return DIFFATTN_OK;
+  int splits = 0;
+  int rc = check_decode(a, &splits);
+  if (rc) return rc;
+  const size_t need = diffattn::decode_workspace_bytes(a->batch, a->q_heads, a->head_dim, splits);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(DIFFATTN_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
+  if (!aligned16(a->workspace)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  return run_decode(a, splits, a->workspace, stream);
+}
+
+int diffattn_v2_decode_noalloc(const diffattn_v2_decode_args *a, void *stream) {
+  g_last_error.clear();
+  if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "need batch >= 0");
+  if (a->batch == 0) return DIFFATTN_OK;
+  int splits = 0;
+  int rc = check_decode(a, &splits);
+  if (rc) return rc;
+  const size_t need = diffattn::decode_workspace_bytes(a->batch, a->q_heads, a->head_dim, splits);
+  if (need > diffattn::kDecodeScratchBytes)
+    return fail(DIFFATTN_ERR_WORKSPACE,
+                "decode needs %zu scratch bytes; the fixed scratch holds %zu (use diffattn_v2_decode with a "
+                "workspace, or fewer splits)", need, diffattn::kDecodeScratchBytes);
+  hipError_t e = hipSuccess;
+  void *ws = diffattn::decode_scratch(&e);
+  if (!ws) return fail(DIFFATTN_ERR_HIP, "decode scratch lookup failed: %s", hipGetErrorString(e));
+  return run_decode(a, splits, ws, stream);
 }
 
 }  // extern "C"

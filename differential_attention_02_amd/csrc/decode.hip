@@ -30,6 +30,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace diffattn {
 namespace {
 
@@ -495,6 +497,38 @@ int decode_max_chunk() { return MAX_CHUNK; }
 hipError_t launch_decode(const DecodeParams &p, int dtype, hipStream_t st) {
   if (dtype == 0) return p.D == 64 ? launch_typed<float, 64>(p, st) : launch_typed<float, 128>(p, st);
   return p.D == 64 ? launch_typed<bf16, 64>(p, st) : launch_typed<bf16, 128>(p, st);
+}
+
+// Fixed scratch of the allocation-free decode entry point (for callers that
+// cannot allocate device memory): the split kernel's partial outputs and
+// (max, sum) pairs.  Every GPU the library runs on holds its own copy until
+// the process ends.  Host code uses the per-device address from
+// hipGetSymbolAddress, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+void *decode_scratch(hipError_t *err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  *err = hipSuccess;
+  return addr[dev];
 }
 
 }  // namespace diffattn

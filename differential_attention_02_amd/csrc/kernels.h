@@ -130,5 +130,9 @@ hipError_t launch_v1_decode(const V1DecodeParams &p, int dtype, hipStream_t st);
 int decode_max_chunk();
 int decode_auto_splits(int B, int Hkv, int L);
 hipError_t launch_decode(const DecodeParams &p, int dtype, hipStream_t st);
+// Fixed device scratch of the allocation-free V2 decode: its size, and its
+// address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+void *decode_scratch(hipError_t *err);
 
 }  // namespace diffattn

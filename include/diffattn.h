@@ -319,6 +319,23 @@ int diffattn_v2_decode(const diffattn_v2_decode_args *args, void *stream);
 /* Workspace bytes diffattn_v2_decode needs for these arguments (0 if invalid). */
 size_t diffattn_v2_decode_workspace_size(const diffattn_v2_decode_args *args);
 
+/*
+ * DIFF V2 decode step that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid it).  Same arguments and results as
+ * diffattn_v2_decode except that workspace and workspace_bytes are ignored:
+ * the split partials go to a fixed scratch array the library holds on each
+ * GPU it runs on (DIFFATTN_DECODE_SCRATCH_BYTES, kept until the process ends;
+ * the array's address is looked up once per device).  A call whose partials
+ * need more than that (diffattn_v2_decode_workspace_size > the limit) returns
+ * DIFFATTN_ERR_WORKSPACE without launching.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (different streams,
+ * different threads) race and must be serialised by the caller.  The scratch
+ * needs no clearing (the split kernel writes every partial it reads).
+ */
+#define DIFFATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int diffattn_v2_decode_noalloc(const diffattn_v2_decode_args *args, void *stream);
+
 /* DIFF V1 decode step. Returns DIFFATTN_OK or a negative status. */
 int diffattn_v1_decode(const diffattn_v1_decode_args *args, void *stream);
 

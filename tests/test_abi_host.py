@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
@@ -160,6 +160,20 @@ def test_decode_workspace_and_empty_call():
 
 
 @host_only
+def test_decode_noalloc_empty_and_oversized():
+    """The allocation-free decode: an empty batch is OK, and a call whose split
+    partials exceed the fixed scratch is rejected on the host (no launch)."""
+    a = _dec_args(batch=0)
+    assert B.lib().diffattn_v2_decode_noalloc(ctypes.byref(a), None) == 0
+    a = _dec_args(batch=4, q_heads=4, kv_heads=2, kv_len=20000, num_splits=20000)
+    a.q_stride = (ctypes.c_int64 * 2)(4 * 128, 128)
+    a.kv_stride = (ctypes.c_int64 * 3)(20000 * 2 * 128, 2 * 128, 128)
+    a.o_stride = (ctypes.c_int64 * 2)(2 * 128, 128)
+    assert B.lib().diffattn_v2_decode_workspace_size(ctypes.byref(a)) > B.DECODE_SCRATCH_BYTES
+    assert B.lib().diffattn_v2_decode_noalloc(ctypes.byref(a), None) == -3
+    assert b"scratch" in B.lib().diffattn_last_error()
+
+
 def test_decode_rejects_small_workspace():
     lib = B.lib()
     a = _dec_args(batch=64)
