@@ -43,7 +43,8 @@ def test_worked_example_printed_values():
 
 
 def test_worked_example_draw_matches_global_seed():
-    """The seeded generator gives the same draw as torch.manual_seed(0)."""
+    """The seeded generator gives the same first draw as torch's global
+    generator seeded with 0 (which the page seeds)."""
     torch.manual_seed(0)
     ref = torch.randn(4, 6, 8)
     q1, k1, q2, k2, _ = workloads.worked_example_inputs()
@@ -137,6 +138,20 @@ def test_lambda_init_schedule():
     assert vals[-1] == pytest.approx(0.8, abs=1e-12)
     with pytest.raises(ValueError):
         lambda_init(0)
+
+
+def test_lambda_init_values_at_the_workload_layers():
+    """lambda_init at layers 1, 2, 12 and 24 equals the pages' printed schedule
+    evaluated in 40-digit decimal arithmetic (tests/golden/lambda_init.json,
+    cited there), and the gaps to 0.8 shrink by exactly exp(-0.3) per layer,
+    which fixes the decay rate (a 0.3 -> 0.03 slip gives a ratio of 0.97)."""
+    rec = json.load(open(os.path.join(GOLDEN, "lambda_init.json")))
+    for layer, val in rec["lambda_init"].items():
+        assert lambda_init(int(layer)) == pytest.approx(float(val), abs=2e-16), layer
+    q = float(rec["gap_ratio_exp_minus_0.3"])
+    for layer in range(1, 24):   # deeper, 0.8 - lambda_init loses digits to cancellation
+        ratio = (0.8 - lambda_init(layer + 1)) / (0.8 - lambda_init(layer))
+        assert ratio == pytest.approx(q, rel=1e-10), layer
 
 
 def test_lambda_value_special_cases():
