@@ -10,6 +10,7 @@ from .diffattn_oracle import (  # noqa: F401
     diff_weights,
     diff_attn_fwd,
     diff_attn_bwd,
+    diff_attn_lambda_grad,
     v2_decode,
     v2_prefill_fwd,
     v2_prefill_bwd,

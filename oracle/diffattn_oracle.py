@@ -257,6 +257,55 @@ def diff_attn_bwd(q1, k1, q2, k2, v, dy, *, lam_init: float,
     return out
 
 
+def diff_attn_lambda_grad(q1, k1, q2, k2, v, dy, *, lam_init: float,
+                          lam_vectors=None, lam_fixed: float | None = None,
+                          causal: bool = True, norm: bool = True, eps: float = 1e-5,
+                          scale: float | None = None) -> dict:
+    """The lambda part of diff_attn_bwd on its own (same chain rule, same
+    steps, without dQ, dK, dV), for sizes where the full backward is too slow:
+    per (b, h), O = A1 - lam A2 with A_m = P_m V, g = dL/dO through the
+    per-head RMSNorm, dlam += -sum(g * A2); then the four vector gradients
+    from lam = e^al - e^be + lam_init.  Returns dlambda, lambda and, with
+    lam_vectors, dlq1, dlk1, dlq2, dlk2."""
+    q1, k1, q2, k2, v, dy = map(_f64, (q1, k1, q2, k2, v, dy))
+    B, S, H, d = q1.shape
+    dv_w = v.shape[-1]
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if lam_vectors is not None:
+        lq1, lk1, lq2, lk2 = map(_f64, lam_vectors)
+        lam = lambda_value(lq1, lk1, lq2, lk2, lam_init)
+    else:
+        if lam_fixed is None:
+            raise ValueError("need lam_vectors or lam_fixed")
+        lam = float(lam_fixed)
+    rows = np.arange(S)
+    a = 1.0 - lam_init
+    dlam = 0.0
+    for b in range(B):
+        for h in range(H):
+            V = v[b, :, h]
+            dY = dy[b, :, h]
+            A1 = _softmax_rows(_scores(q1[b, :, h], k1[b, :, h], s, causal, rows)) @ V
+            A2 = _softmax_rows(_scores(q2[b, :, h], k2[b, :, h], s, causal, rows)) @ V
+            O = A1 - lam * A2
+            if norm:
+                r = 1.0 / np.sqrt(np.mean(O * O, axis=-1) + eps)
+                dot = np.sum(dY * O, axis=-1)
+                g = a * r[:, None] * dY - a * (r ** 3 * dot)[:, None] * O / dv_w
+            else:
+                g = dY
+            dlam += -float(np.sum(g * A2))
+    out = {"dlambda": dlam, "lambda": lam}
+    if lam_vectors is not None:
+        ea = math.exp(float(np.dot(lq1, lk1)))
+        eb = math.exp(float(np.dot(lq2, lk2)))
+        out["dlq1"] = dlam * ea * lk1
+        out["dlk1"] = dlam * ea * lq1
+        out["dlq2"] = -dlam * eb * lk2
+        out["dlk2"] = -dlam * eb * lq2
+    return out
+
+
 def v2_decode(q, k_cache, v_cache, lam, seqlens=None, scale: float | None = None):
     """DIFF V2 decode step with grouped-query attention ([V2] items 1, 2, 5 and
     "GQA compatibility").
@@ -413,7 +462,7 @@ def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lam_init: float, 
 
 
 def v2_prefill_fwd_block_sparse(q, k, v, lam, block_mask, *, q_block: int = 128, k_block: int = 64,
-                                causal: bool = True, scale: float | None = None):
+                                causal: bool = True, scale: float | None = None, rows=None):
     """DIFF V2 forward restricted to selected key blocks, one selection per
     even/odd head pair ([V2] "practical considerations": DIFF V2 works with
     sparse attention frameworks by selecting blocks per head pair inside a GQA
@@ -424,7 +473,8 @@ def v2_prefill_fwd_block_sparse(q, k, v, lam, block_mask, *, q_block: int = 128,
     of pair p may attend key j iff block_mask[b, p, i // q_block, j // k_block]
     (and j <= i when causal).  Both heads of the pair use the pair's
     selection; each head's softmax runs over its allowed keys only.  A row
-    with no allowed key gives zeros.  Returns [B, S, Hq/2, D].
+    with no allowed key gives zeros.  rows: optional query positions to
+    evaluate (default all).  Returns [B, R, Hq/2, D].
     """
     q, k, v = map(_f64, (q, k, v))
     B, S, Hq, D = q.shape
@@ -435,23 +485,24 @@ def v2_prefill_fwd_block_sparse(q, k, v, lam, block_mask, *, q_block: int = 128,
     s = 1.0 / math.sqrt(D) if scale is None else float(scale)
     lam = np.broadcast_to(_f64(lam), (B, S, Hq // 2))
     block_mask = np.asarray(block_mask, dtype=bool)
-    rows = np.arange(S)
-    out = np.zeros((B, S, Hq // 2, D))
+    keys = np.arange(S)
+    rows = keys if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, rows.shape[0], Hq // 2, D))
     for b in range(B):
         for p in range(Hq // 2):
-            allowed = block_mask[b, p][rows[:, None] // q_block, rows[None, :] // k_block]
+            allowed = block_mask[b, p][rows[:, None] // q_block, keys[None, :] // k_block]
             if causal:
-                allowed &= rows[None, :] <= rows[:, None]
+                allowed &= keys[None, :] <= rows[:, None]
             live = allowed.any(axis=1)
             attn = []
             for t in (2 * p, 2 * p + 1):
                 j = t // group
-                sc = np.where(allowed, (q[b, :, t] @ k[b, :, j].T) * s, -np.inf)
+                sc = np.where(allowed, (q[b, rows, t] @ k[b, :, j].T) * s, -np.inf)
                 m = np.where(live, sc.max(axis=1), 0.0)
                 e = np.where(allowed, np.exp(sc - m[:, None]), 0.0)
                 den = np.where(live, e.sum(axis=1), 1.0)
                 attn.append((e / den[:, None]) @ v[b, :, j])
-            out[b, :, p] = attn[0] - sigmoid(lam[b, :, p])[:, None] * attn[1]
+            out[b, :, p] = attn[0] - sigmoid(lam[b, rows, p])[:, None] * attn[1]
     return out
 
 

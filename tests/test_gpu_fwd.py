@@ -157,6 +157,28 @@ def test_generic_bf16_path():
     assert_bf16_rows(y, ref, "generic bf16 d32")
 
 
+@pytest.mark.parametrize("dims", [(8, 16), (16, 32), (32, 64), (64, 128), (128, 256)], ids=lambda d: "d%d_dv%d" % d)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_generic_every_advertised_head_size(dims, dtype):
+    """Every (d, dv) the header lists for the reference vector kernel (f32;
+    bf16 too where the fused kernel does not take it), with a ragged tail of
+    keys and lambda from vectors: f32 within max-abs 1e-5, bf16 within the
+    bf16 bar.  (bf16 d 64 dv 128 runs the fused kernel.)"""
+    d, dv = dims
+    _note(f"generic {dtype} d={d} dv={dv}")
+    cfg = workloads.AttnConfig("g", 2, 77, 2, d, dv, dtype, True, 5, d ** -0.5, lambda_vec_dim=16)
+    inp = workloads.make_attn_inputs(cfg, seed=30 + d)
+    for causal in (True, False):
+        y, lam = _gpu_fwd(inp, layer=5, causal=causal, norm=True, eps=1e-6)
+        ref, lam_ref = _oracle_fwd(inp, layer=5, causal=causal, norm=True, eps=1e-6)
+        assert lam == pytest.approx(lam_ref, rel=1e-6)
+        what = f"generic {dtype} d={d} dv={dv} causal={causal}"
+        if dtype == torch.float32:
+            assert_f32(y, ref, what)
+        else:
+            assert_bf16_rows(y, ref, what)
+
+
 def test_training_saves():
     """lse1, lse2, rstd, the pre-norm output and A2 = map2 V saved for the
     backward match the oracle's."""
@@ -200,14 +222,15 @@ def test_prefill_4k_full(eps):
     assert np.isfinite(y.float().cpu().numpy()).all()
 
 
-def test_prefill_64k_full():
+@pytest.mark.parametrize("eps", [1e-5, 1e-8])
+def test_prefill_64k_full(eps):
     """Long-context forward: 65536 causal tokens, 16 heads, lambda_init at
-    layer 24; oracle on sampled rows, including the last rows that see every
-    key."""
-    _note("prefill_64k full")
+    layer 24, both RMSNorm eps values; oracle on sampled rows, including the
+    last rows that see every key."""
+    _note(f"prefill_64k full eps={eps}")
     inp = workloads.make_attn_inputs("prefill_64k")
-    y, lam = _gpu_fwd(inp, layer=24, causal=True, norm=True, eps=1e-5)
+    y, lam = _gpu_fwd(inp, layer=24, causal=True, norm=True, eps=eps)
     rows = _sample_rows(65536, 32)
-    ref, lam_ref = _oracle_fwd(inp, layer=24, causal=True, norm=True, eps=1e-5, rows=rows)
+    ref, lam_ref = _oracle_fwd(inp, layer=24, causal=True, norm=True, eps=eps, rows=rows)
     assert lam == pytest.approx(lam_ref, rel=1e-6)
-    assert_bf16_rows(y.float().cpu().numpy()[:, rows], ref, "prefill_64k")
+    assert_bf16_rows(y.float().cpu().numpy()[:, rows], ref, f"prefill_64k eps={eps}")

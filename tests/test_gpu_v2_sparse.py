@@ -157,6 +157,15 @@ def test_longest_lists_match_dense_kernel():
     dense = B.v2_fwd(q, k, v, lam)
     torch.cuda.synchronize()
     assert_bf16_rows(out, dense, "v2 sparse 64K full selection vs dense")
+    # Both kernels against the oracle on sampled rows: the last 64 (every key
+    # visible) and a seeded spread.
+    rng = np.random.default_rng(15)
+    rows = np.unique(np.concatenate([np.arange(S - 64, S), rng.choice(S - 64, 64, replace=False)]))
+    x64 = [as_f64(inp[n]) for n in ("q", "k", "v", "lam")]
+    ref = oracle.v2_prefill_fwd(*x64, causal=True, rows=rows)
+    ri = torch.as_tensor(rows, device=out.device)
+    assert_bf16_rows(dense[:, ri], ref, "v2 dense 64K sampled rows vs oracle")
+    assert_bf16_rows(out[:, ri], ref, "v2 sparse 64K full selection sampled rows vs oracle")
     # Entries that do not rise above the previous accepted one are skipped: a
     # list 0,0,1,1,2,2,... (cut at 1024 entries) keeps tiles 0..511 only.
     dup = torch.repeat_interleave(torch.arange(512, dtype=torch.int32, device="cuda"), 2)
@@ -170,6 +179,8 @@ def test_longest_lists_match_dense_kernel():
     torch.cuda.synchronize()
     assert torch.equal(out2, out3)
     assert torch.isfinite(out2.float()).all()
+    ref2 = oracle.v2_prefill_fwd_block_sparse(*x64, m2.cpu().numpy(), causal=True, rows=rows)
+    assert_bf16_rows(out2[:, ri], ref2, "v2 sparse 64K half selection sampled rows vs oracle")
 
 
 def test_strided_views():

@@ -7,7 +7,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import diff_attn_bwd, diff_attn_fwd, lambda_init, lambda_value
+from oracle import diff_attn_bwd, diff_attn_fwd, diff_attn_lambda_grad, lambda_init, lambda_value
 
 H_STEP = 1e-6
 TOL = 1e-6
@@ -99,3 +99,31 @@ def test_lambda_vector_gradients_share_one_scalar():
     np.testing.assert_allclose(g["dlk1"] / vecs[0], c1[0], rtol=1e-10)
     np.testing.assert_allclose(g["dlk2"] / vecs[2], c2[0], rtol=1e-10)
     assert c1[0] / c2[0] == pytest.approx(-math.exp(np.dot(vecs[0], vecs[1])) / math.exp(np.dot(vecs[2], vecs[3])), rel=1e-10)
+
+
+@pytest.mark.parametrize("causal,norm", [(True, True), (False, True), (True, False)])
+def test_lambda_only_gradient_matches_finite_differences(causal, norm):
+    """diff_attn_lambda_grad (the lambda part of the backward on its own, used
+    where the full backward is too slow): dL/dlambda by central differences
+    in lambda, the vector gradients along a random direction of each vector,
+    and agreement with the full backward."""
+    li, eps = lambda_init(12), 1e-5
+    x, vecs, dy = _setup(7, B=2, S=20, H=2, d=16, dv=32)
+    X = (x["q1"], x["k1"], x["q2"], x["k2"], x["v"])
+    lam = lambda_value(*vecs, li)
+    gf = diff_attn_lambda_grad(*X, dy, lam_init=li, lam_fixed=lam, causal=causal, norm=norm, eps=eps)
+    f = lambda t: _loss(x, vecs, dy, li, causal, norm, eps, lam_fixed=float(t))  # noqa: E731
+    assert _rel((f(lam + H_STEP) - f(lam - H_STEP)) / (2 * H_STEP), gf["dlambda"]) < TOL
+    gv = diff_attn_lambda_grad(*X, dy, lam_init=li, lam_vectors=vecs, causal=causal, norm=norm, eps=eps)
+    rng = np.random.default_rng(8)
+    for i, name in enumerate(("dlq1", "dlk1", "dlq2", "dlk2")):
+        u = rng.standard_normal(64)
+        def fv(t, i=i, u=u):
+            vv = list(vecs)
+            vv[i] = vecs[i] + t * u
+            return _loss(x, vv, dy, li, causal, norm, eps)
+        fd = (fv(H_STEP) - fv(-H_STEP)) / (2 * H_STEP)
+        assert _rel(fd, float(np.dot(gv[name], u))) < TOL, name
+    full = diff_attn_bwd(*X, dy, lam_init=li, lam_vectors=vecs, causal=causal, norm=norm, eps=eps)
+    for name in ("dlambda", "dlq1", "dlk1", "dlq2", "dlk2"):
+        np.testing.assert_allclose(gv[name], full[name], rtol=1e-12, atol=0)

@@ -49,3 +49,16 @@ def test_empty_rows_are_zero():
     mask[0, 0, 1, 4] = True   # pair 0, query block 1 (rows 16..31) sees only keys 32..39: all in its future
     out = v2_prefill_fwd_block_sparse(q, k, v, lam, mask, q_block=16, k_block=8)
     assert np.all(out == 0.0)
+
+
+def test_row_selection_matches_full_evaluation():
+    """rows= evaluates the chosen query rows only; they equal those rows of
+    the full evaluation (used at 65,536 tokens, where the full maps do not fit)."""
+    q, k, v, lam = _case(3)
+    rng = np.random.default_rng(9)
+    mask = rng.random((1, 2, 3, 5)) < 0.6
+    rows = np.array([0, 5, 16, 31, 39])
+    for causal in (True, False):
+        full = v2_prefill_fwd_block_sparse(q, k, v, lam, mask, q_block=16, k_block=8, causal=causal)
+        part = v2_prefill_fwd_block_sparse(q, k, v, lam, mask, q_block=16, k_block=8, causal=causal, rows=rows)
+        np.testing.assert_array_equal(part, full[:, rows])
