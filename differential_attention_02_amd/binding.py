@@ -34,6 +34,7 @@ class FwdArgs(ctypes.Structure):
         ("softmax_scale", c_f32), ("eps", c_f32),
         ("out", c_vp), ("lambda_out", c_fp),
         ("lse1", c_fp), ("lse2", c_fp), ("rstd", c_fp), ("o_pre", c_fp), ("a2", c_fp),
+        ("workspace", c_vp), ("workspace_bytes", c_sz),
     ]
 
 
@@ -96,6 +97,7 @@ class V2FwdArgs(ctypes.Structure):
         ("softmax_scale", c_f32),
         ("out", c_vp), ("o_stride", c_i64 * 3),
         ("lse", c_fp), ("a_even", c_fp), ("a_odd", c_fp),
+        ("workspace", c_vp), ("workspace_bytes", c_sz),
     ]
 
 
@@ -122,6 +124,8 @@ SIGNATURES = {
     "diffattn_bwd": (ctypes.c_int, [ctypes.POINTER(BwdArgs), c_vp]),
     "diffattn_fwd_fp8": (ctypes.c_int, [ctypes.POINTER(FwdArgs), c_vp, c_sz, c_vp]),
     "diffattn_fwd_fp8_workspace_size": (c_sz, [ctypes.POINTER(FwdArgs)]),
+    "diffattn_fwd_workspace_size": (c_sz, [ctypes.POINTER(FwdArgs)]),
+    "diffattn_v2_fwd_workspace_size": (c_sz, [ctypes.POINTER(V2FwdArgs)]),
     "diffattn_bwd_workspace_size": (c_sz, [ctypes.POINTER(BwdArgs)]),
     "diffattn_v2_decode": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), c_vp]),
     "diffattn_v2_decode_workspace_size": (c_sz, [ctypes.POINTER(DecodeArgs)]),
@@ -219,6 +223,17 @@ def _check_attn(q1, k1, q2, k2, v, out, lambda_vecs):
                    device=q1.device)
 
 
+def _attach_workspace(a, size_fn, device):
+    """Allocates the workspace size_fn(args) asks for (if any) and attaches it;
+    the tensor is kept on the args object so it lives as long as they do."""
+    nbytes = int(size_fn(ctypes.byref(a)))
+    if nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        a.workspace, a.workspace_bytes = _ptr(ws), nbytes
+        a._workspace = ws
+    return a
+
+
 def lambda_init(layer: int) -> float:
     """lambda_init for layer l >= 1 as the library computes it."""
     return float(lib().diffattn_lambda_init(int(layer)))
@@ -271,6 +286,7 @@ def fwd(q1, k1, q2, k2, v, *, lambda_init: float, lambda_vecs=None, lambda_fixed
                  "rstd": torch.empty((B, H, S), **f32), "o_pre": torch.empty((B, S, H, dv), **f32),
                  "a2": torch.empty((B, S, H, dv), **f32), "lambda": lam}
         a.lse1, a.lse2, a.rstd, a.o_pre, a.a2 = (_ptr(saves[k]) for k in ("lse1", "lse2", "rstd", "o_pre", "a2"))
+    _attach_workspace(a, lib().diffattn_fwd_workspace_size, v.device)
     _check(lib().diffattn_fwd(ctypes.byref(a), _stream()), "diffattn_fwd")
     return (out, saves) if save else out
 
@@ -298,7 +314,7 @@ def fwd_args(q1, k1, q2, k2, v, out, *, lambda_init, lambda_vecs=None, lambda_fi
             _require(tuple(t.shape) == shape and t.is_contiguous(), f"saved {k} must be contiguous {shape}")
             _check_dev(((k, t),), dtype=torch.float32, device=q1.device)
         a.lse1, a.lse2, a.rstd, a.o_pre, a.a2 = (_ptr(saves[k]) for k in ("lse1", "lse2", "rstd", "o_pre", "a2"))
-    return a
+    return _attach_workspace(a, lib().diffattn_fwd_workspace_size, q1.device)
 
 
 def fwd_launch(args: FwdArgs) -> None:
@@ -487,7 +503,7 @@ def v2_fwd_args(q, k, v, lam, out, *, causal=True, softmax_scale=0.0, saves=None
             _require(t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shape
                      and t.device == q.device, f"{name}: contiguous float32 {shape} on q's GPU")
         a.lse, a.a_even, a.a_odd = _ptr(saves["lse"]), _ptr(saves["a_even"]), _ptr(saves["a_odd"])
-    return a
+    return _attach_workspace(a, lib().diffattn_v2_fwd_workspace_size, q.device)
 
 
 def v2_fwd_launch(args: V2FwdArgs) -> None:

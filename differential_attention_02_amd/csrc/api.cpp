@@ -129,6 +129,10 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
     const int64_t span = (int64_t)a->seqlen * (a->k_stride[1] > a->v_stride[1] ? a->k_stride[1] : a->v_stride[1]) * 2;
     if (span >= ((int64_t)1 << 31))
       return fail(DIFFATTN_ERR_UNSUPPORTED, "bf16 fused path needs seqlen x key-row stride below 2^30 elements");
+    const size_t need = diffattn::fwd_mfma_workspace_bytes(a->batch, a->seqlen, a->heads, nsave != 0);
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(DIFFATTN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   }
 
   diffattn::FwdParams p{};
@@ -147,8 +151,15 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
   p.lambda_out = a->lambda_out;
   p.lse1 = a->lse1; p.lse2 = a->lse2; p.rstd = a->rstd; p.o_pre = a->o_pre; p.a2 = a->a2;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fused) return hip_status(diffattn::launch_fwd_mfma(p, st), "fused forward launch");
+  if (fused) return hip_status(diffattn::launch_fwd_mfma(p, a->workspace, st), "fused forward launch");
   return hip_status(diffattn::launch_fwd_generic(p, a->dtype, a->head_dim, a->v_dim, st), "forward launch");
+}
+
+size_t diffattn_fwd_workspace_size(const diffattn_fwd_args *a) {
+  if (!a || a->batch <= 0 || a->seqlen <= 0 || a->heads < 1) return 0;
+  const bool fused = a->dtype == DIFFATTN_BF16 && a->head_dim == 64 && a->v_dim == 128;
+  const bool training = a->lse1 || a->lse2 || a->rstd || a->o_pre || a->a2;
+  return fused ? diffattn::fwd_mfma_workspace_bytes(a->batch, a->seqlen, a->heads, training) : 0;
 }
 
 static int check_fwd_fp8(const diffattn_fwd_args *a) {
@@ -304,6 +315,19 @@ static int check_v2_common(int B, int S, int Hq, int Hkv, int D, int dtype, cons
   return DIFFATTN_OK;
 }
 
+static int check_v2_workspace(const diffattn_v2_fwd_args *a) {
+  const size_t need = diffattn::vrange_bytes(a->batch, a->seqlen, a->kv_heads);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(DIFFATTN_ERR_WORKSPACE, "V2 prefill needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
+  if (!aligned16(a->workspace)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  return DIFFATTN_OK;
+}
+
+size_t diffattn_v2_fwd_workspace_size(const diffattn_v2_fwd_args *a) {
+  if (!a || a->batch <= 0 || a->seqlen <= 0 || a->kv_heads < 1) return 0;
+  return diffattn::vrange_bytes(a->batch, a->seqlen, a->kv_heads);
+}
+
 int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
   g_last_error.clear();
   if (!a) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "args is NULL");
@@ -324,6 +348,7 @@ int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
     if (!fused_layout_ok(ptrs, 6, str, 3))
       return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs 16-byte aligned pointers and strides that are multiples of 8");
   }
+  if ((rc = check_v2_workspace(a))) return rc;
   diffattn::V2FwdParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
@@ -335,6 +360,7 @@ int diffattn_v2_fwd(const diffattn_v2_fwd_args *a, void *stream) {
   p.causal = a->causal != 0;
   p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
   p.lse = a->lse; p.a_even = a->a_even; p.a_odd = a->a_odd;
+  p.vpart = static_cast<const unsigned *>(a->workspace);
   return hip_status(diffattn::launch_fwd_v2(p, static_cast<hipStream_t>(stream)), "V2 prefill launch");
 }
 
@@ -361,6 +387,7 @@ int diffattn_v2_fwd_sparse(const diffattn_v2_fwd_args *a, const int32_t *block_i
     if (!fused_layout_ok(ptrs, 4, str, 3))
       return fail(DIFFATTN_ERR_UNSUPPORTED, "V2 prefill needs 16-byte aligned pointers and strides that are multiples of 8");
   }
+  if ((rc = check_v2_workspace(a))) return rc;
   diffattn::V2FwdParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v;
   p.qs_b = a->q_stride[0]; p.qs_s = a->q_stride[1]; p.qs_h = a->q_stride[2];
@@ -372,6 +399,7 @@ int diffattn_v2_fwd_sparse(const diffattn_v2_fwd_args *a, const int32_t *block_i
   p.causal = a->causal != 0;
   p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.f / std::sqrt((float)a->head_dim);
   p.blk_idx = block_idx; p.blk_cnt = block_cnt; p.max_blocks = max_blocks;
+  p.vpart = static_cast<const unsigned *>(a->workspace);
   return hip_status(diffattn::launch_fwd_v2(p, static_cast<hipStream_t>(stream)), "block-sparse V2 prefill launch");
 }
 

@@ -40,11 +40,15 @@
 //              accumulating dQ with atomics keeps every result deterministic;
 //   bwd_lambda one workgroup: dL/dlambda = sum of the row shares in a fixed
 //              order, then the chain rule into the four lambda vectors.
-// Matrix-core operands are fp16 (bf16 inputs convert exactly) with float32
-// accumulation: bf16 rounding of g, W and dS alone would spend most of the
-// bf16 error budget.
+// Matrix-core operands are fp16 with float32 accumulation: bf16 rounding of g,
+// W and dS alone would spend most of the bf16 error budget.  Q, K and V enter
+// fp16 times powers of two 2^kq, 2^kk, 2^kv chosen per (batch, head) from
+// their largest magnitudes (bwd_pre, bwd_scales; vrange.h), so any finite bf16
+// inputs convert without saturating or losing precision, and every result is
+// unscaled exactly.
 #include "common.h"
 #include "kernels.h"
+#include "vrange.h"
 
 namespace diffattn {
 namespace {
@@ -59,7 +63,8 @@ struct Ws {
   f16 *qh;         // [B, H, S, 2 D] fp16: Q1 (channels 0..63) and Q2 (64..127)
   float *e1, *e2;  // [B, H, S]  E_m = sum_j P_m dP (unscaled)
   float *gnorm, *vnorm, *dlam_row;  // [B, H, S]
-  float *scales;   // [B*H][4]: sg, kappa, omega, unused (exponents of 2)
+  float *amax;     // [B, H, S][4]: the row's largest |Q1|,|Q2|; |K1|,|K2|; |V|; unused
+  float *scales;   // [B*H][8]: sg, kappa, omega, kq, kk, kv, unused x2 (exponents of 2)
   float *dlam_bh;  // [B*H] per-(batch, head) sums of dlam_row
 };
 
@@ -77,7 +82,8 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
   w.gnorm = (float *)p; p += align256(rows * 4);
   w.vnorm = (float *)p; p += align256(rows * 4);
   w.dlam_row = (float *)p; p += align256(rows * 4);
-  w.scales = (float *)p; p += align256((size_t)B * H * 16);
+  w.amax = (float *)p; p += align256(rows * 16);
+  w.scales = (float *)p; p += align256((size_t)B * H * 32);
   w.dlam_bh = (float *)p; p += align256((size_t)B * H * 4);
   return w;
 }
@@ -85,7 +91,7 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
 __host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
   const size_t rows = (size_t)B * H * S;
   return align256(rows * DV * 4) + align256(rows * DV * 2) + align256(rows * 2 * D * 2) + 5 * align256(rows * 4) +
-         align256((size_t)B * H * 16) + align256((size_t)B * H * 4);
+         align256(rows * 16) + align256((size_t)B * H * 32) + align256((size_t)B * H * 4);
 }
 
 __device__ __forceinline__ float exp2i(float e) { return fast_exp2(e); }  // e integral: exact power of 2
@@ -120,51 +126,76 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   const float gn = wave_sum(g0 * g0 + g1 * g1);
   const float vn = wave_sum(v0 * v0 + v1 * v1);
   const float ga = wave_sum(g0 * a2.x + g1 * a2.y);
+  // Largest magnitudes of the row's Q1 | Q2 and K1 | K2 (lanes 0..31 the
+  // first, 32..63 the second, two channels each) and V: their fp16 copies
+  // are scaled by powers of two chosen from these (vrange.h).
+  const int qc = 2 * (lane & 31);
+  const bf16 *qp = (const bf16 *)(lane < 32 ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s + h * p.qs_h + qc;
+  const bf16 *kp = (const bf16 *)(lane < 32 ? p.k1 : p.k2) + b * p.ks_b + (int64_t)s * p.ks_s + h * p.ks_h + qc;
+  const float qm = wave_max(fmaxf(fabsf(bf2f(qp[0])), fabsf(bf2f(qp[1]))));
+  const float km = wave_max(fmaxf(fabsf(bf2f(kp[0])), fabsf(bf2f(kp[1]))));
+  const float vm = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
   *(float2 *)(w.g + row * DV + c) = make_float2(g0, g1);
   if (lane == 0) {
     w.gnorm[row] = sqrtf(gn);
     w.vnorm[row] = sqrtf(vn);
     w.dlam_row[row] = -ga;
+    *(f32x4 *)(w.amax + row * 4) = f32x4{qm, km, vm, 0.f};
   }
 }
 
 // ---------------------------------------------------------------------------
 // bwd_scales: one workgroup per (b, h).
 __global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
-  __shared__ float red[3][NT / 64];
+  __shared__ float red[6][NT / 64];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int64_t base = (int64_t)bh * p.S;
   float gm = 0.f, vm = 0.f, dl = 0.f;
+  f32x4 am = {0.f, 0.f, 0.f, 0.f};
   for (int s = tid; s < p.S; s += NT) {
     gm = fmaxf(gm, w.gnorm[base + s]);
     vm = fmaxf(vm, w.vnorm[base + s]);
     dl += w.dlam_row[base + s];
+    const f32x4 a = *(const f32x4 *)(w.amax + (base + s) * 4);
+    am = f32x4{fmaxf(am[0], a[0]), fmaxf(am[1], a[1]), fmaxf(am[2], a[2]), 0.f};
   }
   for (int o = 32; o > 0; o >>= 1) {
     gm = fmaxf(gm, __shfl_xor(gm, o));
     vm = fmaxf(vm, __shfl_xor(vm, o));
     dl += __shfl_xor(dl, o);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) am[i] = fmaxf(am[i], __shfl_xor(am[i], o));
   }
   if (lane == 0) {
     red[0][wave] = gm;
     red[1][wave] = vm;
     red[2][wave] = dl;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) red[3 + i][wave] = am[i];
   }
   __syncthreads();
   if (tid == 0) {
     gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     vm = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    float ks[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      ks[i] = (float)v_shift_of_max(__float_as_uint(fmaxf(fmaxf(red[3 + i][0], red[3 + i][1]),
+                                                          fmaxf(red[3 + i][2], red[3 + i][3]))) >> 16);
     w.dlam_bh[bh] = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
     const float al = fmaxf(1.f, fabsf(lam));
     const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
     const float x = 2.f * al * gm * vm;  // bound on |dS| before scaling by 2^sg
-    const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) : 0.f;
+    // dP' = g' V' carries 2^(sg + kv): dS is scaled by 2^kappa on top of it.
+    const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) - ks[2] : 0.f;
     const float om = floorf(13.f - log2f(1.f + fabsf(lam)));
-    w.scales[bh * 4 + 0] = sg;
-    w.scales[bh * 4 + 1] = kap;
-    w.scales[bh * 4 + 2] = om;
-    w.scales[bh * 4 + 3] = 0.f;
+    w.scales[bh * 8 + 0] = sg;
+    w.scales[bh * 8 + 1] = kap;
+    w.scales[bh * 8 + 2] = om;
+    w.scales[bh * 8 + 3] = ks[0];  // Q1, Q2
+    w.scales[bh * 8 + 4] = ks[1];  // K1, K2
+    w.scales[bh * 8 + 5] = ks[2];  // V
   }
 }
 
@@ -184,7 +215,7 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
   const int bh = row / p.S;
   const int b = bh / p.H, h = bh % p.H;
   const int c = 2 * lane;
-  const float sg = w.scales[bh * 4 + 0], f = exp2i(sg);
+  const float sg = w.scales[bh * 8 + 0], f = exp2i(sg);
   const float2 g = *(const float2 *)(w.g + row * DV + c);
   const f16x2 gh = {(f16)(g.x * f), (f16)(g.y * f)};
   *(f16x2 *)(w.gh + row * DV + c) = gh;
@@ -202,9 +233,8 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_qconv: Q1 | Q2 rows to fp16 (bf16 converts exactly within fp16's range),
-// 8 channels per thread, into [B, H, S, 2 D] for the key-outer kernel's
-// staging.
+// bwd_qconv: Q1 | Q2 rows to fp16 times 2^kq (exact), 8 channels per thread,
+// into [B, H, S, 2 D] for the key-outer kernel's staging.
 __global__ __launch_bounds__(NT) void bwd_qconv_kernel(BwdParams p, Ws w) {
   const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8
   const int64_t n = (int64_t)p.B * p.H * p.S * (2 * D / 8);
@@ -214,9 +244,8 @@ __global__ __launch_bounds__(NT) void bwd_qconv_kernel(BwdParams p, Ws w) {
   const int s = row % p.S, bh = row / p.S, b = bh / p.H, hd = bh % p.H;
   const bf16 *q = (const bf16 *)(ch < D ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s + hd * p.qs_h + (ch & (D - 1));
   const u32x4 raw = *(const u32x4 *)q;
-  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
-                   bf16x2_to_f16x2(raw[3])};
-  *(u32x4 *)(w.qh + i * 8) = h;
+  const VScale sq((int)w.scales[bh * 8 + 3]);
+  *(u32x4 *)(w.qh + i * 8) = sq.on ? bf16x8_to_f16x8<true>(raw, sq) : bf16x8_to_f16x8<false>(raw, sq);
 }
 
 // Permutation of rows 0..31 used for the A operand of score-like products so
@@ -224,10 +253,9 @@ __global__ __launch_bounds__(NT) void bwd_qconv_kernel(BwdParams p, Ws w) {
 __device__ __forceinline__ int row_perm(int i) { return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1); }
 __device__ __forceinline__ int row_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
 
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const u32x4 &raw) {
-  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
-                   bf16x2_to_f16x2(raw[3])};
-  return __builtin_bit_cast(f16x8, h);
+// Eight bf16 values to fp16 times 2^k (the fp16 copies' range shift).
+__device__ __forceinline__ f16x8 to_f16x8(const u32x4 &raw, const VScale &sc) {
+  return __builtin_bit_cast(f16x8, bf16x8_to_f16x8_scaled(raw, sc));
 }
 
 __device__ __forceinline__ f16x8 pack8h(const float *w) {
@@ -321,9 +349,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   const int bh = blockIdx.x % BH, b = bh / p.H, hd = bh % p.H;
   const int S = p.S;
   const int kb = (blockIdx.x / BH) * KVB, kw = kb + wave * 32, my_key = kw + ln;
-  const float sg = w.scales[bh * 4 + 0], kap = w.scales[bh * 4 + 1], om = w.scales[bh * 4 + 2];
-  const float c = p.scale * kLog2e;
-  const float fdS = exp2i(kap), fW = exp2i(om), fE = exp2i(sg);
+  const float sg = w.scales[bh * 8 + 0], kap = w.scales[bh * 8 + 1], om = w.scales[bh * 8 + 2];
+  const float kq = w.scales[bh * 8 + 3], kk = w.scales[bh * 8 + 4], kv = w.scales[bh * 8 + 5];
+  const VScale sck((int)kk), scv((int)kv);
+  // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
+  const float c = p.scale * kLog2e * exp2i(-(kq + kk));
+  const float fdS = exp2i(kap), fW = exp2i(om), fE = exp2i(sg + kv);
 
   // K1, K2 (B operand of S = Q K^T) and V (B operand of dP = g V^T) for my key, fp16.
   f16x8 kf1[4], kf2[4], vf[8];
@@ -334,11 +365,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
     const bf16 *vv = (const bf16 *)p.v + b * p.vs_b + (int64_t)my_key * p.vs_s + hd * p.vs_h + 8 * h;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      kf1[kc] = ok ? bf16x8_to_f16x8(*(const u32x4 *)(k1 + kc * 16)) : f16x8{};
-      kf2[kc] = ok ? bf16x8_to_f16x8(*(const u32x4 *)(k2 + kc * 16)) : f16x8{};
+      kf1[kc] = ok ? to_f16x8(*(const u32x4 *)(k1 + kc * 16), sck) : f16x8{};
+      kf2[kc] = ok ? to_f16x8(*(const u32x4 *)(k2 + kc * 16), sck) : f16x8{};
     }
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) vf[kc] = ok ? bf16x8_to_f16x8(*(const u32x4 *)(vv + kc * 16)) : f16x8{};
+    for (int kc = 0; kc < 8; ++kc) vf[kc] = ok ? to_f16x8(*(const u32x4 *)(vv + kc * 16), scv) : f16x8{};
   }
 
   f32x16 dv[4], dk1[2], dk2[2];
@@ -416,7 +447,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
   if (my_key < S) {
     const float fv = exp2i(-(om + sg));
-    const float fk = p.scale * exp2i(-(kap + sg));
+    const float fk = p.scale * exp2i(-(kap + sg + kv + kq));
     bf16 *dvp = (bf16 *)p.dv + b * p.dvs_b + (int64_t)my_key * p.dvs_s + hd * p.dvs_h;
     bf16 *dk1p = (bf16 *)p.dk1 + b * p.dks_b + (int64_t)my_key * p.dks_s + hd * p.dks_h;
     bf16 *dk2p = (bf16 *)p.dk2 + b * p.dks_b + (int64_t)my_key * p.dks_s + hd * p.dks_h;
@@ -453,7 +484,8 @@ struct SmemB {
 };
 
 __device__ __forceinline__ void stage_kv(SmemB &sm, const bf16 *k1g, const bf16 *k2g, const bf16 *vg,
-                                         int64_t ks, int64_t vs, int kbase, int S, int tid) {
+                                         int64_t ks, int64_t vs, int kbase, int S, int tid, const VScale &sck,
+                                         const VScale &scv) {
   for (int i = tid; i < KT * 8; i += NT) {
     const int r = i >> 3, col = (i & 7) * 8, key = kbase + r;
     u32x4 a = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
@@ -461,14 +493,14 @@ __device__ __forceinline__ void stage_kv(SmemB &sm, const bf16 *k1g, const bf16 
       a = *(const u32x4 *)(k1g + (int64_t)key * ks + col);
       bb = *(const u32x4 *)(k2g + (int64_t)key * ks + col);
     }
-    *(f16x8 *)(sm.k1 + r * QST + col) = bf16x8_to_f16x8(a);
-    *(f16x8 *)(sm.k2 + r * QST + col) = bf16x8_to_f16x8(bb);
+    *(f16x8 *)(sm.k1 + r * QST + col) = to_f16x8(a, sck);
+    *(f16x8 *)(sm.k2 + r * QST + col) = to_f16x8(bb, sck);
   }
   for (int i = tid; i < KT * 16; i += NT) {
     const int r = i >> 4, col = (i & 15) * 8, key = kbase + r;
     u32x4 a = {0, 0, 0, 0};
     if (key < S) a = *(const u32x4 *)(vg + (int64_t)key * vs + col);
-    *(f16x8 *)(sm.v + r * GST + col) = bf16x8_to_f16x8(a);
+    *(f16x8 *)(sm.v + r * GST + col) = to_f16x8(a, scv);
   }
 }
 
@@ -502,8 +534,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const int b = bh / p.H, hd = bh % p.H;
   const int S = p.S;
   const int q0 = qt * QB, qw = q0 + wave * 32, my_q = qw + ln;
-  const float sg = w.scales[bh * 4 + 0], kap = w.scales[bh * 4 + 1];
-  const float c = p.scale * kLog2e;
+  const float sg = w.scales[bh * 8 + 0], kap = w.scales[bh * 8 + 1];
+  const float kq = w.scales[bh * 8 + 3], kk = w.scales[bh * 8 + 4], kv = w.scales[bh * 8 + 5];
+  const VScale scq((int)kq), sck((int)kk), scv((int)kv);
+  // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
+  const float c = p.scale * kLog2e * exp2i(-(kq + kk));
   const float fdS = exp2i(kap);
   const int64_t statb = (int64_t)bh * S;
   const bool qok = my_q < S;
@@ -515,8 +550,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
     const bf16 *q2 = (const bf16 *)p.q2 + b * p.qs_b + (int64_t)my_q * p.qs_s + hd * p.qs_h + 8 * h;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      qf1[kc] = qok ? bf16x8_to_f16x8(*(const u32x4 *)(q1 + kc * 16)) : f16x8{};
-      qf2[kc] = qok ? bf16x8_to_f16x8(*(const u32x4 *)(q2 + kc * 16)) : f16x8{};
+      qf1[kc] = qok ? to_f16x8(*(const u32x4 *)(q1 + kc * 16), scq) : f16x8{};
+      qf2[kc] = qok ? to_f16x8(*(const u32x4 *)(q2 + kc * 16), scq) : f16x8{};
     }
     const f16 *gp = w.gh + (statb + my_q) * DV + 8 * h;
 #pragma unroll
@@ -534,7 +569,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const bf16 *vg = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
 
   // E_m' = g' . A_m for this query (scaled like dP').
-  const float fE = exp2i(sg);
+  const float fE = exp2i(sg + kv);
   const float e1 = qok ? w.e1[statb + my_q] * fE : 0.f;
   const float e2 = qok ? w.e2[statb + my_q] * fE : 0.f;
 
@@ -543,7 +578,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   dq1[0] = dq1[1] = dq2[0] = dq2[1] = f32x16{};
   for (int kt = 0; kt < n_kt; ++kt) {
     __syncthreads();
-    stage_kv(sm, k1g, k2g, vg, p.ks_s, p.vs_s, kt * KT, S, tid);
+    stage_kv(sm, k1g, k2g, vg, p.ks_s, p.vs_s, kt * KT, S, tid, sck, scv);
     __syncthreads();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -576,7 +611,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
     }
   }
   if (qok) {
-    const float fq = p.scale * exp2i(-(kap + sg));
+    const float fq = p.scale * exp2i(-(kap + sg + kv + kk));
     bf16 *d1 = (bf16 *)p.dq1 + b * p.dqs_b + (int64_t)my_q * p.dqs_s + hd * p.dqs_h;
     bf16 *d2 = (bf16 *)p.dq2 + b * p.dqs_b + (int64_t)my_q * p.dqs_s + hd * p.dqs_h;
 #pragma unroll

@@ -31,10 +31,14 @@
 //   v2b_dkdv   key-outer: 128 keys of one (batch, KV head) per workgroup,
 //              every pair of the head, 64-query chunks double-buffered in
 //              LDS; dV and dK in registers.  No atomics: deterministic.
-// Matrix-core operands are fp16 (bf16 inputs convert exactly within fp16's
-// range) with float32 accumulation.
+// Matrix-core operands are fp16 with float32 accumulation; Q, K and V enter
+// fp16 times powers of two 2^kq, 2^kk, 2^kv chosen per (batch, KV head) from
+// their largest magnitudes (v2b_pre, v2b_scales; vrange.h), so any finite bf16
+// inputs convert without saturating or losing precision; results are unscaled
+// exactly.
 #include "common.h"
 #include "kernels.h"
+#include "vrange.h"
 
 namespace diffattn {
 namespace {
@@ -48,7 +52,9 @@ struct Ws2 {
   f16 *qh;               // [B, P, S, 2 D] Q_e (channels 0..127) | Q_o (128..255)
   float *ee, *eo, *gn;   // [B, P, S]  E_e, E_o (unscaled), |g|
   float *vn;             // [B, Hkv, S]  |V| rows
-  float *scales;         // [B * Hkv][4]: sg, kappa, omega, unused (exponents of 2)
+  float *qm;             // [B, P, S]  largest |Q_e|, |Q_o| of the row
+  float *kvm;            // [B, Hkv, S][2]  largest |K|, |V| of the row
+  float *scales;         // [B * Hkv][8]: sg, kappa, omega, kq, kk, kv, unused x2 (exponents of 2)
 };
 
 __host__ __device__ inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -63,14 +69,16 @@ __host__ __device__ inline Ws2 carve2(void *base, int B, int S, int P, int Hkv) 
   w.eo = (float *)c; c += al256(rows * 4);
   w.gn = (float *)c; c += al256(rows * 4);
   w.vn = (float *)c; c += al256((size_t)B * Hkv * S * 4);
-  w.scales = (float *)c; c += al256((size_t)B * Hkv * 16);
+  w.qm = (float *)c; c += al256(rows * 4);
+  w.kvm = (float *)c; c += al256((size_t)B * Hkv * S * 8);
+  w.scales = (float *)c; c += al256((size_t)B * Hkv * 32);
   return w;
 }
 
 __host__ __device__ inline size_t ws2_bytes(int B, int S, int P, int Hkv) {
   const size_t rows = (size_t)B * P * S;
   return al256(rows * D * 2) + al256(rows * 2 * D * 2) + 3 * al256(rows * 4) + al256((size_t)B * Hkv * S * 4) +
-         al256((size_t)B * Hkv * 16);
+         al256(rows * 4) + al256((size_t)B * Hkv * S * 8) + al256((size_t)B * Hkv * 32);
 }
 
 __device__ __forceinline__ float sigmoid_of(const V2BwdParams &p, int b, int s, int pr) {
@@ -94,54 +102,90 @@ __global__ __launch_bounds__(NT) void v2b_pre_kernel(V2BwdParams p, Ws2 w) {
   const float g0 = bf2f(gp[0]), g1 = bf2f(gp[1]);
   const float gg = wave_sum(g0 * g0 + g1 * g1);
   const float ga = wave_sum(g0 * ao.x + g1 * ao.y);
+  // Largest magnitudes of the row's Q_e, Q_o (and, once per KV head, K and V):
+  // their fp16 copies are scaled by powers of two chosen from these (vrange.h).
+  const bf16 *qp = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + 2 * pr * p.qs_h + c;
+  const float qmx = wave_max(fmaxf(fmaxf(fabsf(bf2f(qp[0])), fabsf(bf2f(qp[1]))),
+                                   fmaxf(fabsf(bf2f(qp[p.qs_h])), fabsf(bf2f(qp[p.qs_h + 1])))));
   if (lane == 0) {
     const float sg = sigmoid_of(p, b, s, pr);
     w.gn[row] = sqrtf(gg);
+    w.qm[row] = qmx;
     p.dlam[((int64_t)b * p.S + s) * P + pr] = -sg * (1.f - sg) * ga;
   }
   const int ppk = p.Hq / p.Hkv / 2, j = pr / ppk;
   if (pr % ppk == 0) {  // wave-uniform
     const bf16 *vr = (const bf16 *)p.v + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c;
+    const bf16 *kr = (const bf16 *)p.k + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c;
     const float v0 = bf2f(vr[0]), v1 = bf2f(vr[1]);
     const float vv = wave_sum(v0 * v0 + v1 * v1);
-    if (lane == 0) w.vn[((int64_t)b * p.Hkv + j) * p.S + s] = sqrtf(vv);
+    const float vmx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const float kmx = wave_max(fmaxf(fabsf(bf2f(kr[0])), fabsf(bf2f(kr[1]))));
+    const int64_t kr_row = ((int64_t)b * p.Hkv + j) * p.S + s;
+    if (lane == 0) {
+      w.vn[kr_row] = sqrtf(vv);
+      *(float2 *)(w.kvm + kr_row * 2) = make_float2(kmx, vmx);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // v2b_scales: one workgroup per (b, KV head j).
 __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
-  __shared__ float red[2][NT / 64];
+  __shared__ float red[5][NT / 64];
   const int bj = blockIdx.x, b = bj / p.Hkv, j = bj % p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;  // pairs per KV head
-  float gm = 0.f;
+  float gm = 0.f, qm = 0.f;
   for (int pp = 0; pp < ppk; ++pp) {
     const int64_t base = ((int64_t)b * P + j * ppk + pp) * p.S;
-    for (int s = tid; s < p.S; s += NT) gm = fmaxf(gm, w.gn[base + s]);
+    for (int s = tid; s < p.S; s += NT) {
+      gm = fmaxf(gm, w.gn[base + s]);
+      qm = fmaxf(qm, w.qm[base + s]);
+    }
   }
-  float vm = 0.f;
+  float vm = 0.f, km = 0.f, vx = 0.f;
   const float *vn = w.vn + (int64_t)bj * p.S;
-  for (int s = tid; s < p.S; s += NT) vm = fmaxf(vm, vn[s]);
+  const float *kvm = w.kvm + (int64_t)bj * p.S * 2;
+  for (int s = tid; s < p.S; s += NT) {
+    vm = fmaxf(vm, vn[s]);
+    km = fmaxf(km, kvm[2 * s]);
+    vx = fmaxf(vx, kvm[2 * s + 1]);
+  }
   for (int o = 32; o > 0; o >>= 1) {
     gm = fmaxf(gm, __shfl_xor(gm, o));
     vm = fmaxf(vm, __shfl_xor(vm, o));
+    qm = fmaxf(qm, __shfl_xor(qm, o));
+    km = fmaxf(km, __shfl_xor(km, o));
+    vx = fmaxf(vx, __shfl_xor(vx, o));
   }
   if (lane == 0) {
     red[0][wave] = gm;
     red[1][wave] = vm;
+    red[2][wave] = qm;
+    red[3][wave] = km;
+    red[4][wave] = vx;
   }
   __syncthreads();
   if (tid == 0) {
-    gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    vm = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    float mx[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) mx[i] = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
+    gm = mx[0];
+    vm = mx[1];
+    const float kq = (float)v_shift_of_max(__float_as_uint(mx[2]) >> 16);
+    const float kk = (float)v_shift_of_max(__float_as_uint(mx[3]) >> 16);
+    const float kv = (float)v_shift_of_max(__float_as_uint(mx[4]) >> 16);
     const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
     const float x = 2.f * gm * vm;  // bound on |dS| before scaling by 2^sg
-    const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) : 0.f;
-    w.scales[bj * 4 + 0] = sg;
-    w.scales[bj * 4 + 1] = kap;
-    w.scales[bj * 4 + 2] = 12.f;
-    w.scales[bj * 4 + 3] = 0.f;
+    // dP' = g' V' carries 2^(sg + kv): dS is scaled by 2^kappa on top of it.
+    const float kap = x > 0.f ? fminf(fmaxf(floorf(13.f - log2f(x) - sg), -60.f), 60.f) - kv : 0.f;
+    w.scales[bj * 8 + 0] = sg;
+    w.scales[bj * 8 + 1] = kap;
+    w.scales[bj * 8 + 2] = 12.f;
+    w.scales[bj * 8 + 3] = kq;
+    w.scales[bj * 8 + 4] = kk;
+    w.scales[bj * 8 + 5] = kv;
   }
 }
 
@@ -157,7 +201,7 @@ __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
   const int bp = row / p.S, b = bp / P, pr = bp % P;
   const int bj = b * p.Hkv + pr / ppk;
   const int c = 2 * lane;
-  const float sg = w.scales[bj * 4 + 0], f = fast_exp2(sg);
+  const float sg = w.scales[bj * 8 + 0], f = fast_exp2(sg);
   const bf16 *gp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c;
   const f16x2 gh = {(f16)(bf2f(gp[0]) * f), (f16)(bf2f(gp[1]) * f)};
   *(f16x2 *)(w.gh + row * D + c) = gh;
@@ -175,7 +219,8 @@ __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
 }
 
 // ---------------------------------------------------------------------------
-// v2b_qconv: Q_e | Q_o rows to fp16, 8 channels per thread, into [B, P, S, 2 D].
+// v2b_qconv: Q_e | Q_o rows to fp16 times 2^kq, 8 channels per thread, into
+// [B, P, S, 2 D].
 __global__ __launch_bounds__(NT) void v2b_qconv_kernel(V2BwdParams p, Ws2 w) {
   const int P = p.Hq / 2;
   const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8 channels
@@ -187,9 +232,8 @@ __global__ __launch_bounds__(NT) void v2b_qconv_kernel(V2BwdParams p, Ws2 w) {
   const int t = 2 * pr + (ch >= D);
   const bf16 *q = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + t * p.qs_h + (ch & (D - 1));
   const u32x4 raw = *(const u32x4 *)q;
-  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
-                   bf16x2_to_f16x2(raw[3])};
-  *(u32x4 *)(w.qh + i * 8) = h;
+  const VScale sq((int)w.scales[(b * p.Hkv + pr / (p.Hq / p.Hkv / 2)) * 8 + 3]);
+  *(u32x4 *)(w.qh + i * 8) = bf16x8_to_f16x8_scaled(raw, sq);
 }
 
 // Permutation of rows 0..31 used for the A operand of score-like products so
@@ -197,10 +241,9 @@ __global__ __launch_bounds__(NT) void v2b_qconv_kernel(V2BwdParams p, Ws2 w) {
 __device__ __forceinline__ int row_perm(int i) { return (i & 0x13) | ((i & 4) << 1) | ((i & 8) >> 1); }
 __device__ __forceinline__ int row_of_reg(int r, int h) { return ((r & 8) << 1) + 8 * h + (r & 7); }
 
-__device__ __forceinline__ f16x8 to_f16x8(const u32x4 &raw) {
-  const u32x4 h = {bf16x2_to_f16x2(raw[0]), bf16x2_to_f16x2(raw[1]), bf16x2_to_f16x2(raw[2]),
-                   bf16x2_to_f16x2(raw[3])};
-  return __builtin_bit_cast(f16x8, h);
+// Eight bf16 values to fp16 times 2^k (the fp16 copies' range shift).
+__device__ __forceinline__ f16x8 to_f16x8(const u32x4 &raw, const VScale &sc) {
+  return __builtin_bit_cast(f16x8, bf16x8_to_f16x8_scaled(raw, sc));
 }
 
 __device__ __forceinline__ f16x8 pack8h(const float *v) {
@@ -255,12 +298,13 @@ __device__ __forceinline__ void load_kv(KVRegs &r, const bf16 *kg, const bf16 *v
   }
 }
 
-__device__ __forceinline__ void store_kv(SmemQ &sm, const KVRegs &r, int tid) {
+__device__ __forceinline__ void store_kv(SmemQ &sm, const KVRegs &r, int tid, const VScale &sck,
+                                         const VScale &scv) {
 #pragma unroll
   for (int i = 0; i < KT * (D / 8) / NT; ++i) {
     const int idx = tid + i * NT, row = idx >> 4, col = (idx & 15) * 8;
-    *(f16x8 *)(sm.k + row * QST + col) = to_f16x8(r.k[i]);
-    *(f16x8 *)(sm.v + row * GST + col) = to_f16x8(r.v[i]);
+    *(f16x8 *)(sm.k + row * QST + col) = to_f16x8(r.k[i], sck);
+    *(f16x8 *)(sm.v + row * GST + col) = to_f16x8(r.v[i], scv);
   }
 }
 
@@ -277,8 +321,11 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   const int S = p.S;
   const bool causal = p.causal != 0;
   const int q0 = qt * QB, qw = q0 + wave * 32, my_q = qw + ln;
-  const float sg = w.scales[bj * 4 + 0], kap = w.scales[bj * 4 + 1];
-  const float c = p.scale * kLog2e;
+  const float sg = w.scales[bj * 8 + 0], kap = w.scales[bj * 8 + 1];
+  const float kq = w.scales[bj * 8 + 3], kk = w.scales[bj * 8 + 4], kv = w.scales[bj * 8 + 5];
+  const VScale scq((int)kq), sck((int)kk), scv((int)kv);
+  // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
+  const float c = p.scale * kLog2e * fast_exp2(-(kq + kk));
   const float fdS = fast_exp2(kap);
   const int64_t rowb = (int64_t)bp * S;  // row base in [B, P, S]
   const bool qok = my_q < S;
@@ -290,15 +337,15 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
     const f16 *gp = w.gh + (rowb + my_q) * D + 8 * h;
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      qe[kc] = qok ? to_f16x8(*(const u32x4 *)(qp + kc * 16)) : f16x8{};
-      qo[kc] = qok ? to_f16x8(*(const u32x4 *)(qp + p.qs_h + kc * 16)) : f16x8{};
+      qe[kc] = qok ? to_f16x8(*(const u32x4 *)(qp + kc * 16), scq) : f16x8{};
+      qo[kc] = qok ? to_f16x8(*(const u32x4 *)(qp + p.qs_h + kc * 16), scq) : f16x8{};
       gf[kc] = qok ? *(const f16x8 *)(gp + kc * 16) : f16x8{};
     }
   }
   const int64_t lr = ((int64_t)b * p.Hq + 2 * pr) * S + my_q;
   const float Le = qok ? p.lse[lr] * kLog2e : __builtin_inff();
   const float Lo = qok ? p.lse[lr + S] * kLog2e : __builtin_inff();
-  const float fE = fast_exp2(sg);
+  const float fE = fast_exp2(sg + kv);
   const float ee = qok ? w.ee[rowb + my_q] * fE : 0.f;
   const float eo = qok ? w.eo[rowb + my_q] * fE : 0.f;
   const float sig = qok ? sigmoid_of(p, b, my_q, pr) : 0.f;
@@ -315,7 +362,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   for (int dt = 0; dt < D / 32; ++dt) dqe[dt] = dqo[dt] = f32x16{};
   KVRegs nx;
   load_kv(nx, kg, vg, p.kvs_s, 0, S, tid);
-  store_kv(smb[0], nx, tid);
+  store_kv(smb[0], nx, tid, sck, scv);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const SmemQ &sm = smb[kt & 1];
@@ -360,11 +407,11 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
         }
       }
     }
-    if (kt + 1 < n_kt) store_kv(smb[(kt + 1) & 1], nx, tid);  // the buffer tile kt - 1 used
+    if (kt + 1 < n_kt) store_kv(smb[(kt + 1) & 1], nx, tid, sck, scv);  // the buffer tile kt - 1 used
     __syncthreads();
   }
   if (qok) {
-    const float fq = p.scale * fast_exp2(-(kap + sg));
+    const float fq = p.scale * fast_exp2(-(kap + sg + kv + kk));
     bf16 *de = (bf16 *)p.dq + b * p.dqs_b + (int64_t)my_q * p.dqs_s + 2 * pr * p.dqs_h;
     bf16 *dO = de + p.dqs_h;
 #pragma unroll
@@ -458,9 +505,12 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
   const int S = p.S;
   const bool causal = p.causal != 0;
   const int kb = (blockIdx.x / BJ) * KVB, kw = kb + wave * 32, my_key = kw + ln;
-  const float sg = w.scales[bj * 4 + 0], kap = w.scales[bj * 4 + 1], om = w.scales[bj * 4 + 2];
-  const float c = p.scale * kLog2e;
-  const float fdS = fast_exp2(kap), fW = fast_exp2(om), fE = fast_exp2(sg);
+  const float sg = w.scales[bj * 8 + 0], kap = w.scales[bj * 8 + 1], om = w.scales[bj * 8 + 2];
+  const float kq = w.scales[bj * 8 + 3], kk = w.scales[bj * 8 + 4], kv = w.scales[bj * 8 + 5];
+  const VScale sck((int)kk), scv((int)kv);
+  // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
+  const float c = p.scale * kLog2e * fast_exp2(-(kq + kk));
+  const float fdS = fast_exp2(kap), fW = fast_exp2(om), fE = fast_exp2(sg + kv);
 
   // K (B operand of S = Q K^T) and V (B operand of dP' = g' V^T) for my key, fp16.
   f16x8 kf[D / 16], vf[D / 16];
@@ -470,8 +520,8 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
     const bf16 *vp = (const bf16 *)p.v + b * p.kvs_b + (int64_t)my_key * p.kvs_s + j * p.kvs_h + 8 * h;
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      kf[kc] = ok ? to_f16x8(*(const u32x4 *)(kp + kc * 16)) : f16x8{};
-      vf[kc] = ok ? to_f16x8(*(const u32x4 *)(vp + kc * 16)) : f16x8{};
+      kf[kc] = ok ? to_f16x8(*(const u32x4 *)(kp + kc * 16), sck) : f16x8{};
+      vf[kc] = ok ? to_f16x8(*(const u32x4 *)(vp + kc * 16), scv) : f16x8{};
     }
   }
 
@@ -552,7 +602,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
   if (my_key < S) {
     const float fv = fast_exp2(-(om + sg));
-    const float fk = p.scale * fast_exp2(-(kap + sg));
+    const float fk = p.scale * fast_exp2(-(kap + sg + kv + kq));
     bf16 *dvp = (bf16 *)p.dv + b * p.dkvs_b + (int64_t)my_key * p.dkvs_s + j * p.dkvs_h;
     bf16 *dkp = (bf16 *)p.dk + b * p.dkvs_b + (int64_t)my_key * p.dkvs_s + j * p.dkvs_h;
 #pragma unroll

@@ -22,6 +22,7 @@
 // different 16-byte bank groups), their exponents, and the fp16 V tile.
 #include "attn_tile.h"
 #include "kernels.h"
+#include "vrange.h"
 
 namespace diffattn {
 namespace {
@@ -148,7 +149,8 @@ struct LoaderF {
   }
 };
 
-__device__ __forceinline__ void store_tile(SmemF &sm, const TileRegsF &r, int tid, bool with_v) {
+__device__ __forceinline__ void store_tile(SmemF &sm, const TileRegsF &r, int tid, bool with_v,
+                                           const VScale &vsc) {
   const int row = tid >> 2, col = (tid & 3) * 16;
   *(u32x4 *)(sm.k1 + row * KST8 + col) = r.k1;
   *(u32x4 *)(sm.k2 + row * KST8 + col) = r.k2;
@@ -158,8 +160,7 @@ __device__ __forceinline__ void store_tile(SmemF &sm, const TileRegsF &r, int ti
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vr = (tid >> 4) + 16 * i, vc = (tid & 15) * 8;
-      const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]), bf16x2_to_f16x2(r.v[i][2]),
-                       bf16x2_to_f16x2(r.v[i][3])};
+      const u32x4 h = bf16x8_to_f16x8_scaled(r.v[i], vsc);
       *(u32x4 *)(sm.v + vr * VST + vc) = h;
     }
   }
@@ -292,19 +293,22 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
   const int n_kt = (kend + BN - 1) / BN;
   const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
   const int krow = k_row_perm(ln);
+  // fp16 V is V 2^vk (range of bf16; see vrange.h); the epilogue removes it.
+  const int vk = v_shift(p.vpart + (int64_t)bh * vrange_chunks(S), vrange_chunks(kend));
+  const VScale vsc(vk);
 
   // ---------------- pass 1: per-map log2 partition functions ----------------
   float m1 = kNegInf, l1 = 0.f, m2 = kNegInf, l2 = 0.f;
   TileRegsF nxt;
   ld.load(0, false, nxt);
-  store_tile(sm[0], nxt, tid, false);
+  store_tile(sm[0], nxt, tid, false, vsc);
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
     sched_fence();
     pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c1, c2, m1, l1, m2, l2, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
     sched_fence();
     pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c1, c2, m1, l1, m2, l2, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   float M1, L1, M2, L2;
@@ -326,14 +330,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
   ld.load(0, true, nxt);
-  store_tile(sm[0], nxt, tid, true);
+  store_tile(sm[0], nxt, tid, true, vsc);
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
     sched_fence();
     pass2_tile<false>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c1, c2, lam, L1s, L2s, o, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
@@ -341,12 +345,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
     sched_fence();
     pass2_tile<true>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c1, c2, lam, L1s, L2s, o, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
 
   // ---------------- epilogue: per-head RMSNorm x (1 - lambda_init) ----------------
-  const float unscale = fast_exp2(-sg);
+  const float unscale = __builtin_ldexpf(1.f, -vk) * fast_exp2(-sg);
   float ss = 0.f;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
@@ -374,14 +378,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_fp8_kernel(FwdParams p, Fp8Ws w) {
 
 size_t fwd_fp8_workspace_bytes(int B, int S, int H) {
   const size_t rows = (size_t)B * H * S;
-  return al256f(4 * rows * D) + al256f(4 * rows * 4);
+  return al256f(4 * rows * D) + al256f(4 * rows * 4) + vrange_bytes(B, S, H);
 }
 
-hipError_t launch_fwd_fp8(const FwdParams &p, void *workspace, hipStream_t st) {
-  Fp8Ws w = carve_fp8(workspace, p.B, p.S, p.H);
-  const int64_t rows = (int64_t)p.B * p.H * p.S;
+hipError_t launch_fwd_fp8(const FwdParams &p0, void *workspace, hipStream_t st) {
+  Fp8Ws w = carve_fp8(workspace, p0.B, p0.S, p0.H);
+  const int64_t rows = (int64_t)p0.B * p0.H * p0.S;
+  FwdParams p = p0;
+  p.vpart = reinterpret_cast<const unsigned *>(static_cast<char *>(workspace) + al256f(4 * rows * D) +
+                                               al256f(4 * rows * 4));
+  VRangeParams vr{p.v, p.vs_b, p.vs_s, p.vs_h, p.B, p.S, p.H, const_cast<unsigned *>(p.vpart)};
+  hipError_t e = launch_vrange(vr, DV, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fp8q_kernel, dim3((4 * rows + NT / 8 - 1) / (NT / 8)), dim3(NT), 0, st, p, w);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (p.S + BM - 1) / BM;
   hipLaunchKernelGGL(fwd_fp8_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);

@@ -41,8 +41,8 @@
 // 8 h + 0..7 and 16 + 8 h + 0..7 (h = lane / 32), exactly the k-slots of two
 // 32x32x16 PV steps.  V^T operands come from the row-major V tile through LDS
 // transpose reads.  The epilogue (RMSNorm over the head's 128 channels) reduces
-// inside the lane and across the two half-waves.  V entries beyond the fp16
-// range (|v| > 65504) saturate.
+// inside the lane and across the two half-waves.  V enters fp16 times a
+// power of two chosen per workgroup so bf16's whole range converts (vrange.h).
 #include "attn_tile.h"
 #include "kernels.h"
 #include "v1_stage.h"
@@ -213,6 +213,9 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
 
   const int kend = causal ? min(S, q0 + BM) : S;
   const int n_kt = (kend + BN - 1) / BN;
+  // fp16 V is V 2^vk (range of bf16; see vrange.h); the epilogue removes it.
+  const int vk = v_shift(p.vpart + (int64_t)bh * vrange_chunks(S), vrange_chunks(kend));
+  const VScale vsc(vk);
   // Tiles every query of the workgroup sees in full (no mask, no tail).
   const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
   const int krow = k_row_perm(ln);
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
   float m1 = kNegInf, l1 = 0.f, m2 = kNegInf, l2 = 0.f;
   TileRegs nxt;
   ld.load(0, false, nxt);
-  store_tile(sm[0], nxt, tid, false);
+  store_tile(sm[0], nxt, tid, false, vsc);
   __syncthreads();
   // Interior tiles first (straight-line, no masks), then the diagonal / tail.
   for (int kt = 0; kt < n_full; ++kt) {
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
     sched_fence();
     pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
     sched_fence();
     pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qf1, qf2, c, m1, l1, m2, l2, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   float M1, L1, M2, L2;
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
     for (int ct = 0; ct < 4; ++ct) o2[ct] = f32x16{};
   }
   ld.load(0, true, nxt);
-  store_tile(sm[0], nxt, tid, true);
+  store_tile(sm[0], nxt, tid, true, vsc);
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
     pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c, lam, L1s, L2s, L2s2, o, o2, S, causal,
                             qw, my_q);
     if constexpr (!SAVE) sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
@@ -279,13 +282,13 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
     pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qf1, qf2, c, lam, L1s, L2s, L2s2, o, o2, S, causal,
                            qw, my_q);
     if constexpr (!SAVE) sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
 
   // ---------------- epilogue: per-head RMSNorm x (1 - lambda_init) ----------------
-  // o holds 2^sg O; unscale exactly by powers of two.
-  const float unscale = fast_exp2(-sg);
+  // o holds 2^(sg + vk) O; unscale exactly by powers of two.
+  const float unscale = __builtin_ldexpf(1.f, -vk) * fast_exp2(-sg);
   float ss = 0.f;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
       const int64_t row = ((int64_t)b * S + my_q) * p.H + hd;
       float *op = p.o_pre + row * DV;
       float *ap = p.a2 + row * DV;
-      const float un2 = fast_exp2(-sg2);
+      const float un2 = __builtin_ldexpf(1.f, -vk) * fast_exp2(-sg2);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -331,8 +334,26 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_mfma_kernel(FwdParams p)
 
 }  // namespace
 
-hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st) {
-  if (!p.lse1) return launch_fwd_onepass(p, st);
+size_t fwd_mfma_workspace_bytes(int B, int S, int H, bool training) {
+  return training ? vrange_bytes(B, S, H) : vconv_bytes(B, S, H);
+}
+
+hipError_t launch_fwd_mfma(const FwdParams &p0, void *workspace, hipStream_t st) {
+  FwdParams p = p0;
+  if (!p.lse1) {  // inference: the one-pass kernel reads a converted fp16 copy of V
+    VConvParams vc{p.v, p.vs_b, p.vs_s, p.vs_h, p.B, p.S, p.H, static_cast<f16 *>(workspace), nullptr};
+    vc.kexp = reinterpret_cast<int *>(static_cast<char *>(workspace) +
+                                      (((size_t)p.B * p.H * p.S * DV * 2 + 255) & ~(size_t)255));
+    hipError_t e = launch_vconv(vc, st);
+    if (e != hipSuccess) return e;
+    p.v16 = vc.v16;
+    p.vexp = vc.kexp;
+    return launch_fwd_onepass(p, st);
+  }
+  p.vpart = static_cast<const unsigned *>(workspace);
+  VRangeParams vr{p.v, p.vs_b, p.vs_s, p.vs_h, p.B, p.S, p.H, static_cast<unsigned *>(workspace)};
+  hipError_t e = launch_vrange(vr, DV, st);
+  if (e != hipSuccess) return e;
   const int n_qt = (p.S + BM - 1) / BM;
   dim3 grid(n_qt * p.B * p.H), block(NT);
   hipLaunchKernelGGL(fwd_mfma_kernel<true>, grid, block, 0, st, p);

@@ -38,10 +38,12 @@
 // product O^T = V^T W^T (K rows read in the permuted order of the shared tile
 // helpers).  The two half-waves hold disjoint keys of the same rows; every
 // decision (references, kappa) is taken on merged sums, so both halves agree.
-// V is converted bf16 -> fp16 on its way into LDS (exact for magnitudes in
-// [2^-14, 65504]).
+// V comes from an fp16 copy written by a pass over V (vrange.hip) with one
+// power-of-two shift per 256-row chunk, so V may take any finite bf16
+// magnitude.
 #include "attn_tile.h"
 #include "kernels.h"
+#include "vrange.h"
 
 namespace diffattn {
 namespace {
@@ -64,14 +66,14 @@ struct Stage {
   u32x4 k1[KC], k2[KC], v[VC];
 };
 
-// Raw buffer loads; each slice's buffer range ends at its last key row, so
-// rows past the sequence end read as zeros.
+// Raw buffer loads (K1, K2 bf16; V from its fp16 copy); each slice's buffer
+// range ends at its last key row, so rows past the sequence end read as zeros.
 struct Loader {
   __amdgpu_buffer_rsrc_t rk1, rk2, rv;
   uint32_t ko, vo;        // this thread's byte offsets inside a tile
   uint32_t kstep, vstep;  // bytes per key row
 
-  __device__ __forceinline__ void init(const bf16 *k1, const bf16 *k2, const bf16 *v, int64_t ks, int64_t vs,
+  __device__ __forceinline__ void init(const bf16 *k1, const bf16 *k2, const f16 *v, int64_t ks, int64_t vs,
                                        int S, int tid) {
     const uint32_t kbytes = (uint32_t)((int64_t)(S - 1) * ks * 2 + D * 2);
     const uint32_t vbytes = (uint32_t)((int64_t)(S - 1) * vs * 2 + DV * 2);
@@ -109,9 +111,7 @@ __device__ __forceinline__ void store_stage(Smem &sm, const Stage &r, int tid) {
 #pragma unroll
   for (int i = 0; i < VC; ++i) {
     const int row = (tid >> 4) + i * (NT / 16), col = (tid & 15) * 8;
-    const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]), bf16x2_to_f16x2(r.v[i][2]),
-                     bf16x2_to_f16x2(r.v[i][3])};
-    *(u32x4 *)(sm.v + row * VST + col) = h;
+    *(u32x4 *)(sm.v + row * VST + col) = r.v[i];
   }
 }
 
@@ -262,6 +262,17 @@ __device__ __forceinline__ void sub_pv(const Smem &sm, int sub, int lane, const 
   }
 }
 
+// Moves the accumulators from V 2^vk products to V 2^(vk + dk) products.
+__device__ __forceinline__ void rescale_acc(f32x16 *x, f32x16 *y, int dk, int &vk) {
+  const float f = __builtin_ldexpf(1.f, dk);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    x[ct] *= f;
+    y[ct] *= f;
+  }
+  vk += dk;
+}
+
 __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   __shared__ Smem sm[NBUF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -286,7 +297,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
 
   Loader ld;
   ld.init((const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h, (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h,
-          (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h, p.ks_s, p.vs_s, S, tid);
+          p.v16 + (int64_t)bh * S * DV, p.ks_s, DV, S, tid);
 
   bf16x8 q1f[4], q2f[4];
   {
@@ -301,6 +312,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
 
   const int kend = causal ? min(S, q0 + OBM) : S;
   const int n_kt = (kend + BN - 1) / BN;
+  // The fp16 copy of V holds each 256-row chunk c times 2^vexp[c]; the
+  // accumulators hold sums against the current tile's shift, rescaled (rarely)
+  // when a tile's chunk has another one.  Each tile's shift is read one tile
+  // ahead.
+  const int *vexp = p.vexp + (int64_t)bh * vrange_chunks(S);
   // Tiles every row of the workgroup sees in full (no mask, no tail).
   const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
   const int krow = k_row_perm(ln);
@@ -328,10 +344,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   ld.load(0, nxt);
   store_stage(sm[0], nxt, tid);
   __syncthreads();
+  int vk = __builtin_amdgcn_readfirstlane(vexp[0]);
+  int ktile = vk;  // shift of the tile about to be computed
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, nxt);  // past the end: the buffer range gives zeros
     sched_fence();
     if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);
+    if (ktile != vk) rescale_acc(x, y, ktile - vk, vk);
+    ktile = __builtin_amdgcn_readfirstlane(vexp[min((kt + 1) * BN, kend - 1) / kVRangeRows]);
     {
       f16x8 wb[2], eb[2];
       sub_softmax<false>(sm[cur], 0, kt * BN, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
@@ -353,6 +373,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
     sched_fence();
     if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);
     pending = false;
+    if (ktile != vk) rescale_acc(x, y, ktile - vk, vk);
+    ktile = __builtin_amdgcn_readfirstlane(vexp[min((kt + 1) * BN, kend - 1) / kVRangeRows]);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int sb = kt * BN + sub * 32;
@@ -376,8 +398,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   // O = X / L1 + (kappa / L1 - lambda / L2) Y; per-head RMSNorm x (1 - lambda_init).
   const float L1 = st.l1 + other_half(st.l1);
   const float L2 = st.l2 + other_half(st.l2);
-  const float i1 = 1.f / L1;
-  const float cy = st.kap * i1 - lam / L2;
+  const float unv = __builtin_ldexpf(1.f, -vk);  // the accumulators hold V 2^vk products
+  const float i1 = unv / L1;
+  const float cy = (st.kap / L1 - lam / L2) * unv;
   float ss = 0.f;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)

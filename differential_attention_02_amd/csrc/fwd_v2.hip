@@ -29,6 +29,7 @@
 // the k-slots of the PV step; V^T comes through LDS transpose reads.
 #include "attn_tile.h"
 #include "kernels.h"
+#include "vrange.h"
 
 namespace diffattn {
 namespace {
@@ -75,14 +76,14 @@ struct LoaderV2 {
   }
 };
 
-__device__ __forceinline__ void store_tile(SmemV2 &sm, const TileRegsV2 &r, int tid, bool with_v) {
+__device__ __forceinline__ void store_tile(SmemV2 &sm, const TileRegsV2 &r, int tid, bool with_v,
+                                           const VScale &vsc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (tid >> 4) + 16 * i, col = (tid & 15) * 8;
     *(u32x4 *)(sm.k + row * KST + col) = r.k[i];
     if (with_v) {
-      const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]), bf16x2_to_f16x2(r.v[i][2]),
-                       bf16x2_to_f16x2(r.v[i][3])};
+      const u32x4 h = bf16x8_to_f16x8_scaled(r.v[i], vsc);
       *(u32x4 *)(sm.v + row * VST + col) = h;
     }
   }
@@ -197,19 +198,23 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   const int n_kt = (kend + BN - 1) / BN;
   const int n_full = min(causal ? (q0 + 1) / BN : n_kt, S / BN);
   const int krow = k_row_perm(ln);
+  // fp16 V is V 2^vk (range of bf16; see vrange.h); the epilogue removes it.
+  const int vk = v_shift(p.vpart + ((int64_t)b * p.Hkv + j) * vrange_chunks(S), vrange_chunks(kend));
+  const VScale vsc(vk);
+  const float unv = __builtin_ldexpf(1.f, -vk);
 
   // ---------------- pass 1: per-head log2 partition functions ----------------
   float me = kNegInf, le = 0.f, mo = kNegInf, lo = 0.f;
   TileRegsV2 nxt;
   ld.load(0, false, nxt);
-  store_tile(sm[0], nxt, tid, false);
+  store_tile(sm[0], nxt, tid, false, vsc);
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, false, nxt);  // past the end: the buffer range gives zeros
     sched_fence();
     pass1_tile<false>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
     sched_fence();
     pass1_tile<true>(sm[kt & 1], kt * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, false);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   float Me, Le, Mo, Lo;
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
 #pragma unroll
   for (int ct = 0; ct < (SAVE ? D / 32 : 1); ++ct) ae[ct] = ao[ct] = f32x16{};
   ld.load(0, true, nxt);
-  store_tile(sm[0], nxt, tid, true);
+  store_tile(sm[0], nxt, tid, true, vsc);
   __syncthreads();
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
     pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
                             my_q);
     if constexpr (!SAVE) sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
@@ -255,13 +260,13 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
     pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
                            my_q);
     if constexpr (!SAVE) sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true);
+    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
 
   // ---------------- epilogue: unscale, store bf16 (and the training saves) ----------------
   if (qok) {
-    const float f = fast_exp2(-sg);
+    const float f = fast_exp2(-sg) * unv;
     bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + pr * p.os_h;
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct)
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
         p.lse[lr] = Le * kLn2;
         p.lse[lr + S] = Lo * kLn2;
       }
-      const float fa = fast_exp2(-sge), fb = fast_exp2(-sgo);
+      const float fa = fast_exp2(-sge) * unv, fb = fast_exp2(-sgo) * unv;
       const int64_t srow = (((int64_t)b * S + my_q) * npair + pr) * D;
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct)
@@ -361,12 +366,15 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   }
   __syncthreads();
   const int n_valid = __builtin_amdgcn_readfirstlane(n_tiles);
+  // fp16 V is V 2^vk over every key row the list may name (see vrange.h).
+  const int vk = v_shift(p.vpart + ((int64_t)b * p.Hkv + j) * vrange_chunks(S), vrange_chunks(min(S, kt_lim * BN)));
+  const VScale vsc(vk);
 
   // ---------------- pass 1 ----------------
   float me = kNegInf, le = 0.f, mo = kNegInf, lo = 0.f;
   TileRegsV2 nxt;
   ld.load((n_valid > 0 ? tiles[0] : 0) * BN, false, nxt);
-  store_tile(sm[0], nxt, tid, false);
+  store_tile(sm[0], nxt, tid, false, vsc);
   __syncthreads();
   for (int n = 0; n < n_valid; ++n) {
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
     sched_fence();
     pass1_tile<true>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(n + 1) & 1], nxt, tid, false);
+    store_tile(sm[(n + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
   }
   float Me, Le, Mo, Lo;
@@ -390,7 +398,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) o[ct] = f32x16{};
   ld.load((n_valid > 0 ? tiles[0] : 0) * BN, true, nxt);
-  store_tile(sm[0], nxt, tid, true);
+  store_tile(sm[0], nxt, tid, true, vsc);
   __syncthreads();
   for (int n = 0; n < n_valid; ++n) {
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
@@ -400,12 +408,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
     pass2_tile<true, false>(sm[n & 1], cur * BN, krow, lane, qe, qo, c, sig, Les, Los, 1.f, 1.f, o, dummy, dummy, S,
                             causal, qw, my_q);
     sched_fence();
-    store_tile(sm[(n + 1) & 1], nxt, tid, true);
+    store_tile(sm[(n + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
   }
 
   if (qok) {
-    const float f = live ? fast_exp2(-sg) : 0.f;
+    const float f = live ? fast_exp2(-sg) * __builtin_ldexpf(1.f, -vk) : 0.f;
     bf16 *out = (bf16 *)p.out + b * p.os_b + (int64_t)my_q * p.os_s + pr * p.os_h;
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct)
@@ -422,6 +430,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
 }  // namespace
 
 hipError_t launch_fwd_v2(const V2FwdParams &p, hipStream_t st) {
+  VRangeParams vr{p.v, p.kvs_b, p.kvs_s, p.kvs_h, p.B, p.S, p.Hkv, const_cast<unsigned *>(p.vpart)};
+  hipError_t e = launch_vrange(vr, D, st);
+  if (e != hipSuccess) return e;
   const int n_qt = (p.S + BM - 1) / BM;
   if (p.blk_idx)
     hipLaunchKernelGGL(fwd_v2_sparse_kernel, dim3(n_qt * p.B * (p.Hq / 2)), dim3(NT), 0, st, p);

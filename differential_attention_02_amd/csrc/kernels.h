@@ -22,6 +22,9 @@ struct FwdParams {
   float eps;
   float *lambda_out;
   float *lse1, *lse2, *rstd, *o_pre, *a2;  // training saves (all or none)
+  const unsigned *vpart;  // V range partials (vrange.hip): the training forward
+  const _Float16 *v16;    // the one-pass forward's fp16 copy of V and its
+  const int *vexp;        // per-256-row-chunk shifts (vrange.hip)
 };
 
 struct BwdParams {
@@ -88,6 +91,7 @@ struct V2FwdParams {
   // tile), blk_cnt entries of blk_idx (64-key tile indices, ascending).
   const int32_t *blk_idx, *blk_cnt;
   int max_blocks;
+  const unsigned *vpart;  // V range partials per (batch, KV head) (vrange.hip)
 };
 
 // DIFF V2 prefill backward (bf16, D = 128).
@@ -106,11 +110,40 @@ struct V2BwdParams {
   void *workspace;
 };
 
+// Range pass over V (vrange.hip): per (batch, head) slice of a bf16
+// [B, S, H, C] tensor, the largest magnitude of every 256-row chunk (bf16
+// bits) into part[B * H][vrange_chunks(S)].
+struct VRangeParams {
+  const void *v;
+  int64_t vs_b, vs_s, vs_h;
+  int B, S, H;
+  unsigned *part;
+};
+constexpr int kVRangeRows = 256;
+inline __host__ __device__ int vrange_chunks(int S) { return (S + kVRangeRows - 1) / kVRangeRows; }
+inline size_t vrange_bytes(int B, int S, int H) { return ((size_t)B * H * vrange_chunks(S) * 4 + 255) & ~(size_t)255; }
+hipError_t launch_vrange(const VRangeParams &p, int channels, hipStream_t st);
+// fp16 copy of V for the one-pass forward: v16 [B * H, S, 128], each 256-row
+// chunk times 2^kexp[B * H][vrange_chunks(S)] (vrange.hip).
+struct VConvParams {
+  const void *v;
+  int64_t vs_b, vs_s, vs_h;
+  int B, S, H;
+  _Float16 *v16;
+  int *kexp;
+};
+inline size_t vconv_bytes(int B, int S, int H) {
+  return (((size_t)B * H * S * 128 * 2 + 255) & ~(size_t)255) + vrange_bytes(B, S, H);
+}
+hipError_t launch_vconv(const VConvParams &p, hipStream_t st);
+
 // Reference vector-ALU forward: any supported (d, dv), f32 or bf16.
 hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipStream_t st);
 // Fused bf16 matrix-core forward, d = 64, dv = 128: the one-pass kernel
 // without training saves, the two-pass kernel with them.
-hipError_t launch_fwd_mfma(const FwdParams &p, hipStream_t st);
+// The workspace holds the pass over V's results (vrange.hip).
+size_t fwd_mfma_workspace_bytes(int B, int S, int H, bool training);
+hipError_t launch_fwd_mfma(const FwdParams &p, void *workspace, hipStream_t st);
 hipError_t launch_fwd_onepass(const FwdParams &p, hipStream_t st);
 // The same forward with fp8 e4m3 score operands (per-row power-of-two absmax
 // scales); the workspace holds the codes and exponents.

@@ -1,10 +1,10 @@
 // Global -> LDS staging of the DIFF V1 forward's key tiles (bf16, d = 64,
 // dv = 128): 64 keys of K1, K2 and V per tile, 256 threads, V converted to
-// fp16 on its way into LDS.  Shared by the one-pass inference forward and the
-// two-pass training forward.
+// fp16 on its way into LDS.  Used by the two-pass training forward.
 #pragma once
 
 #include "common.h"
+#include "vrange.h"
 
 namespace diffattn {
 namespace v1s {
@@ -66,10 +66,9 @@ struct TileLoader {
   }
 };
 
-// Register -> LDS half of the staging.  V is converted bf16 -> fp16 (exact
-// for magnitudes in [2^-14, 65504]; larger values saturate, smaller lose
-// significand bits).
-__device__ __forceinline__ void store_tile(Smem &sm, const TileRegs &r, int tid, bool with_v) {
+// Register -> LDS half of the staging.  V is converted bf16 -> fp16 times the
+// workgroup's power-of-two range shift (vrange.h).
+__device__ __forceinline__ void store_tile(Smem &sm, const TileRegs &r, int tid, bool with_v, const VScale &vsc) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
@@ -80,8 +79,7 @@ __device__ __forceinline__ void store_tile(Smem &sm, const TileRegs &r, int tid,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + NT * i, row = c >> 4, col = (c & 15) * 8;
-      const u32x4 h = {bf16x2_to_f16x2(r.v[i][0]), bf16x2_to_f16x2(r.v[i][1]),
-                       bf16x2_to_f16x2(r.v[i][2]), bf16x2_to_f16x2(r.v[i][3])};
+      const u32x4 h = bf16x8_to_f16x8_scaled(r.v[i], vsc);
       *(u32x4 *)(sm.v + row * VST + col) = h;
     }
   }

@@ -82,6 +82,16 @@ extern "C" {
  *       root (1 when norm = 0);
  *     o_pre, a2: float32 [B, S, H, dv] contiguous - the un-normalised combine
  *       O = (map1 - lambda map2) V and the second map's output A2 = map2 V.
+ *   workspace: device memory of at least diffattn_fwd_workspace_size() bytes,
+ *     16-byte aligned (contents on entry do not matter), for the bf16
+ *     matrix-core path: a first pass over V writes there an fp16 copy of V
+ *     with one power-of-two shift per 256-row chunk (inference), or the
+ *     largest |v| of every 256-row chunk from which each workgroup picks the
+ *     shift of its own fp16 copy (training saves), so V may take any finite
+ *     bf16 magnitude (B x H x S x 256 bytes and a little more for inference,
+ *     a few bytes per 256 rows with training saves).  Not read by the
+ *     vector-kernel paths (size 0) nor by diffattn_fwd_fp8, which takes its
+ *     own workspace.
  *   batch = 0 or seqlen = 0 is an empty problem: DIFFATTN_OK, nothing read.
  */
 typedef struct diffattn_fwd_args {
@@ -102,6 +112,8 @@ typedef struct diffattn_fwd_args {
   float *lambda_out;
   float *lse1, *lse2, *rstd;
   float *o_pre, *a2;
+  void *workspace; /* bf16 matrix-core path; see diffattn_fwd_workspace_size */
+  size_t workspace_bytes;
 } diffattn_fwd_args;
 
 /*
@@ -191,6 +203,11 @@ typedef struct diffattn_v2_decode_args {
  *       scaled scores;
  *     a_even, a_odd [B, S, Hq/2, D]: each head's own output attn_2p and
  *       attn_2p+1.
+ *   workspace: device memory of at least diffattn_v2_fwd_workspace_size()
+ *     bytes, 16-byte aligned, contents on entry irrelevant (shared with
+ *     diffattn_v2_fwd_sparse): the largest |v| of every 256-row chunk of each
+ *     (batch, KV head) slice, from which each workgroup picks the power of two
+ *     its fp16 copy of V is scaled by, so V may take any finite bf16 magnitude.
  *   batch = 0 or seqlen = 0 is an empty problem: DIFFATTN_OK, nothing read.
  */
 typedef struct diffattn_v2_fwd_args {
@@ -207,6 +224,8 @@ typedef struct diffattn_v2_fwd_args {
   float *lse;   /* training saves, all three or none (see above) */
   float *a_even;
   float *a_odd;
+  void *workspace; /* see diffattn_v2_fwd_workspace_size */
+  size_t workspace_bytes;
 } diffattn_v2_fwd_args;
 
 /*
@@ -290,6 +309,9 @@ typedef struct diffattn_v1_decode_args {
 /* Forward pass. Returns DIFFATTN_OK or a negative status. */
 int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
 
+/* Workspace bytes diffattn_fwd needs for these arguments (0: none needed). */
+size_t diffattn_fwd_workspace_size(const diffattn_fwd_args *args);
+
 /*
  * Forward pass with fp8 attention logits: Q1, K1, Q2, K2 are quantised per row
  * (one token of one head) to fp8 e4m3 with a power-of-two absmax scale (e the
@@ -300,7 +322,7 @@ int diffattn_fwd(const diffattn_fwd_args *args, void *stream);
  * section and the news write-up].  Same arguments as diffattn_fwd without
  * training saves; supported: bf16 with head_dim 64, v_dim 128.  workspace: at
  * least diffattn_fwd_fp8_workspace_size() bytes, 256-byte aligned (it receives
- * the codes and exponents).
+ * the codes, their exponents and V's range record; args->workspace is not read).
  */
 int diffattn_fwd_fp8(const diffattn_fwd_args *args, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -344,6 +366,9 @@ size_t diffattn_v1_decode_workspace_size(const diffattn_v1_decode_args *args);
 
 /* DIFF V2 prefill forward. Returns DIFFATTN_OK or a negative status. */
 int diffattn_v2_fwd(const diffattn_v2_fwd_args *args, void *stream);
+
+/* Workspace bytes diffattn_v2_fwd and diffattn_v2_fwd_sparse need (0 if invalid). */
+size_t diffattn_v2_fwd_workspace_size(const diffattn_v2_fwd_args *args);
 
 /*
  * Block-sparse DIFF V2 prefill forward: one key-block selection per even/odd

@@ -27,15 +27,15 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = _declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(B.SIGNATURES)
 
 
 def test_struct_sizes_match_layout():
-    # int32 x8 + 5 ptr + 4 x int64[3] + 4 ptr + int32 + 4 float + 7 ptr
-    assert ctypes.sizeof(B.FwdArgs) == 32 + 40 + 96 + 32 + 20 + 4 + 56
+    # int32 x8 + 5 ptr + 4 x int64[3] + 4 ptr + int32 + 4 float + 7 ptr + workspace ptr and size
+    assert ctypes.sizeof(B.FwdArgs) == 32 + 40 + 96 + 32 + 20 + 4 + 56 + 16
     assert ctypes.sizeof(B.DecodeArgs) % 8 == 0
 
 
