@@ -73,15 +73,18 @@ def _traffic_from_profile(name, files):
     return rec.get("hbm_bytes_per_launch")
 
 
-FWD_SOURCES = ["differential_attention_02_amd/csrc/fwd_mfma.hip", "differential_attention_02_amd/csrc/attn_tile.h",
-               "differential_attention_02_amd/csrc/common.h"]
-V2P_SOURCES = ["differential_attention_02_amd/csrc/fwd_v2.hip", "differential_attention_02_amd/csrc/attn_tile.h",
-               "differential_attention_02_amd/csrc/common.h"]
-DEC_SOURCES = ["differential_attention_02_amd/csrc/decode.hip", "differential_attention_02_amd/csrc/common.h"]
-FP8_SOURCES = ["differential_attention_02_amd/csrc/fwd_fp8.hip", "differential_attention_02_amd/csrc/attn_tile.h",
-               "differential_attention_02_amd/csrc/common.h"]
-BWD_SOURCES = ["differential_attention_02_amd/csrc/bwd.hip", "differential_attention_02_amd/csrc/common.h"]
-V2B_SOURCES = ["differential_attention_02_amd/csrc/bwd_v2.hip", "differential_attention_02_amd/csrc/common.h"]
+_CSRC = "differential_attention_02_amd/csrc/"
+# Sources of each timed kernel: a counter summary counts only while their digest matches.
+FWD_SOURCES = [_CSRC + f for f in ("fwd_onepass.hip", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
+V2P_SOURCES = [_CSRC + f for f in ("fwd_v2.hip", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
+DEC_SOURCES = [_CSRC + f for f in ("decode.hip", "common.h")]
+FP8_SOURCES = [_CSRC + f for f in ("fwd_fp8.hip", "v1_stage.h", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
+BWD_SOURCES = [_CSRC + f for f in ("bwd.hip", "vrange.h", "common.h")]
+V2B_SOURCES = [_CSRC + f for f in ("bwd_v2.hip", "vrange.h", "common.h")]
+# fp8 leg: per pair, the two score products (256 flop) run at the fp8 peak and the PV products
+# (512 flop) at the fp16 peak, so the mixed peak is 768 / (256 / 5000 + 512 / 2500) TFLOP/s.
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP8_MIXED_TFLOPS = FLOP_PER_PAIR_FWD / (256 / PEAK_FP8_TFLOPS + 512 / PEAK_BF16_TFLOPS)
 
 
 def _time_launches(launch, steps, warmup, per_launch=None):
@@ -274,7 +277,7 @@ def _gpu_fp8(steps, warmup):
     wall, per = _time_launches(lambda: B.fwd_fp8_launch(args, ws), steps, warmup, each)
     flops = cfg.batch * cfg.heads * cfg.pairs * FLOP_PER_PAIR_FWD
     return {"wall_s": wall, "event_s_per_launch": per, "flop_per_step": flops,
-            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12,
+            "tflops": flops * steps / wall / 1e12, "event_tflops": flops / per / 1e12, "inputs": inp,
             "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
 
 
@@ -323,6 +326,7 @@ def _gpu_v1_decode(steps, warmup):
     inp = workloads.make_v1_decode_inputs(cfg)
     x = [inp[n].cuda() for n in ("q1", "q2", "k1_cache", "k2_cache", "v_cache")]
     vecs = [t.cuda() for t in inp["lambda_vecs"]]
+    lam_rec = _seeded_lambda({"lambda_vecs": inp["lambda_vecs"], "cfg": cfg})
     del inp
     out = torch.empty((cfg.batch, cfg.heads, cfg.v_dim), dtype=x[0].dtype, device="cuda")
     args = B.v1_decode_args(*x, out, lambda_init=B.lambda_init(cfg.layer), lambda_vecs=vecs, eps=cfg.eps)
@@ -335,7 +339,40 @@ def _gpu_v1_decode(steps, warmup):
              + 2 * cfg.batch * cfg.heads * cfg.head_dim + cfg.batch * cfg.heads * cfg.v_dim) * 2
     return {"cfg": cfg, "bytes_per_step": moved, "gbs": moved * steps / wall / 1e9,
             "event_gbs": moved / per / 1e9, "event_s_per_launch": per, "splits": args.num_splits,
-            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3}
+            "median_ms": statistics.median(each) * 1e3, "min_ms": min(each) * 1e3, "seeded_lambda": lam_rec}
+
+
+def _seeded_lambda(inp):
+    """The lambda that a V1 workload's seeded vectors give:
+    exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init(layer), for the record."""
+    import math
+    from differential_attention_02_amd import binding as B
+    lq1, lk1, lq2, lk2 = (t.double() for t in inp["lambda_vecs"])
+    li = B.lambda_init(inp["cfg"].layer)
+    return {"layer": inp["cfg"].layer, "lambda_init": li,
+            "lambda": math.exp(float(lq1 @ lk1)) - math.exp(float(lq2 @ lk2)) + li}
+
+
+def _host_info():
+    """The host CPU's model name and the BLAS thread settings the oracle ran with."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    libs = []
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [{"library": p.get("internal_api"), "threads": p.get("num_threads")} for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+    except Exception:
+        pass
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+           if k in os.environ}
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": libs, "thread_env": env}
 
 
 def _blas_threads():
@@ -371,6 +408,29 @@ def _cpu_baseline_fwd(inp, budget_s=12.0):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
             "sample": f"prefill_4k: {done} of 48 (batch, head) slices, all 4096 causal rows each; "
                       f"{dt:.1f} s of oracle time"}
+
+
+def _cpu_baseline_fp8(inp, budget_s=10.0):
+    """The float64 oracle of the fp8-logit forward (per-row e4m3 quantisation
+    of Q1, K1, Q2, K2, then the forward) on whole heads of the 4K workload,
+    one head at a time until about budget_s seconds have passed."""
+    import oracle
+    cfg = inp["cfg"]
+    li = oracle.lambda_init(cfg.layer)
+    lam = oracle.lambda_value(*[t.double().numpy() for t in inp["lambda_vecs"]], li)
+    done, dt = 0, 0.0
+    for h in range(cfg.heads):
+        x = [inp[k][0:1, :, h:h + 1].double().numpy() for k in ("q1", "k1", "q2", "k2", "v")]
+        t0 = time.perf_counter()
+        oracle.diff_attn_fwd_fp8_logits(*x, lam, li, causal=True, norm=True, eps=cfg.eps)
+        dt += time.perf_counter() - t0
+        done += 1
+        if dt >= budget_s:
+            break
+    flops = done * cfg.pairs * FLOP_PER_PAIR_FWD
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"prefill_4k_fp8: {done} of 48 (batch, head) slices (batch 0), all 4096 causal rows, "
+                      f"quantisation included; {dt:.1f} s of oracle time"}
 
 
 def _cpu_baseline_64k(inp, heads=2):
@@ -545,6 +605,7 @@ def main(argv=None) -> int:
             print(json.dumps({"workload": "train_8k", **r}))
         elif args.only == "prefill_4k_fp8":
             r = _gpu_fp8(args.steps, args.warmup)
+            r.pop("inputs", None)
             print(json.dumps({"workload": "prefill_4k_fp8", **r}))
         elif args.only == "v1_decode":
             r = _gpu_v1_decode(args.steps, args.warmup)
@@ -570,18 +631,22 @@ def main(argv=None) -> int:
     main_r = _gpu_attn("prefill_4k", args.steps, args.warmup)
     cfg = main_r["cfg"]
     achieved = main_r["flop_per_step"] / main_r["event_s_per_launch"] / 1e12
-    traffic = _traffic_from_profile("fwd_mfma_prefill_4k_pmc.md", FWD_SOURCES)
+    traffic = _traffic_from_profile("fwd_onepass_prefill_4k_pmc.md", FWD_SOURCES)
     extra = {}
     r64 = _gpu_attn("prefill_64k", max(3, args.steps // 10), 1)
     extra["prefill_64k"] = {"metric": "fwd TFLOP/s", "value": r64["tflops"], "unit": "TFLOP/s",
+                            "config": {"workload": "prefill_64k: batch 1, seq 65536 causal, 16 heads, d 64, dv 128, "
+                                                   "bf16, lambda_init at layer 24", "seeded_lambda": _seeded_lambda(r64["inputs"])},
                             "frac_of_bf16_peak": r64["event_tflops"] / PEAK_BF16_TFLOPS,
                             "ms_per_step": r64["wall_s"] / max(3, args.steps // 10) * 1e3,
                             "roofline": {"bound": "mfma", "achieved": r64["event_tflops"], "peak": PEAK_BF16_TFLOPS,
                                          "unit": "TFLOP/s", "frac": r64["event_tflops"] / PEAK_BF16_TFLOPS,
-                                         "traffic": _traffic_from_profile("fwd_mfma_prefill_64k_pmc.md",
+                                         "traffic": _traffic_from_profile("fwd_onepass_prefill_64k_pmc.md",
                                                                           FWD_SOURCES)}}
     tr = _gpu_train(max(3, args.steps // 10), 1)
     extra["train_8k"] = {"metric": "fwd+bwd TFLOP/s", "value": tr["tflops"], "unit": "TFLOP/s",
+                         "config": {"workload": "train_8k: forward with training saves then backward",
+                                    "seeded_lambda": _seeded_lambda(tr["inputs"])},
                          "ms_per_step": tr["ms_per_step"], "frac_of_bf16_peak": tr["tflops"] / PEAK_BF16_TFLOPS,
                          "roofline": {"bound": "mfma", "achieved": tr["event_tflops"], "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": tr["event_tflops"] / PEAK_BF16_TFLOPS,
@@ -628,12 +693,15 @@ def main(argv=None) -> int:
         "metric": "fwd TFLOP/s with fp8 e4m3 logits", "value": f8["tflops"], "unit": "TFLOP/s",
         "ms_per_step": f8["wall_s"] / args.steps * 1e3,
         "config": {"workload": "prefill_4k with Q1, K1, Q2, K2 quantised per row to fp8 e4m3 (power-of-two absmax "
-                               "scale) inside every step; score products on scaled fp8 matrix instructions"},
-        "roofline": {"bound": "mfma", "achieved": f8["event_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": f8["event_tflops"] / PEAK_BF16_TFLOPS,
+                               "scale) inside every step; score products on scaled fp8 matrix instructions",
+                   "seeded_lambda": _seeded_lambda(f8["inputs"])},
+        "roofline": {"bound": "mfma", "achieved": f8["event_tflops"], "peak": PEAK_FP8_MIXED_TFLOPS,
+                     "unit": "TFLOP/s", "frac": f8["event_tflops"] / PEAK_FP8_MIXED_TFLOPS,
                      "traffic": _traffic_from_profile("fwd_fp8_prefill_4k_pmc.md", FP8_SOURCES),
-                     "note": "algorithmic 768 flop per pair against the bf16/fp16 peak (the PV product stays fp16); "
-                             "traffic is the forward kernel's, per launch (the quantisation kernel not counted)"},
+                     "note": "algorithmic 768 flop per pair against the mixed peak 768 / (256 / 5000 + 512 / 2500) "
+                             "= 3000 TFLOP/s: the score products (256 flop) run on fp8 at 5.0 PFLOP/s, the PV "
+                             "products (512 flop) stay fp16 at 2.5 PFLOP/s; traffic is the forward kernel's, per "
+                             "launch (the quantisation kernel not counted)"},
         "median_ms": f8["median_ms"], "min_ms": f8["min_ms"],
     }
     v1d = _gpu_v1_decode(args.steps, args.warmup)
@@ -641,7 +709,8 @@ def main(argv=None) -> int:
         "metric": "V1 decode HBM GB/s", "value": v1d["gbs"], "unit": "GB/s",
         "ms_per_step": v1d["event_s_per_launch"] * 1e3,
         "config": {"workload": "v1_decode: B64, 16 heads, K1/K2 width 64, V width 128, KV 8192, bf16, "
-                               "lambda from 64-dim vectors, per-head RMSNorm", "num_splits": "auto"},
+                               "lambda from 64-dim vectors, per-head RMSNorm", "num_splits": "auto",
+                   "seeded_lambda": v1d["seeded_lambda"]},
         "roofline": {"bound": "hbm", "achieved": v1d["event_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": v1d["event_gbs"] / PEAK_HBM_GBS,
                      "traffic": _traffic_from_profile("v1dec_split_v1_decode_pmc.md", DEC_SOURCES)},
@@ -668,6 +737,8 @@ def main(argv=None) -> int:
         extra["v1_decode"]["cpu_baseline"] = _cpu_baseline_v1_decode()
         extra["v2_sparse_4k"]["cpu_baseline"] = _cpu_baseline_v2_sparse(v2s["inputs"], v2s["mask"])
         extra["prefill_64k"]["cpu_baseline"] = _cpu_baseline_64k(r64["inputs"])
+        extra["prefill_4k_fp8"]["cpu_baseline"] = _cpu_baseline_fp8(f8["inputs"])
+        cpu["host"] = _host_info()
     line = {
         "metric": METRIC,
         "value": main_r["tflops"],
@@ -683,9 +754,12 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": "prefill_4k: batch 4, seq 4096 causal, 12 heads, d 64, dv 128, bf16, "
                                "lambda from 64-dim vectors, lambda_init at layer 12, per-head RMSNorm",
-                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single GPU"},
+                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single GPU",
+                   "seeded_lambda": _seeded_lambda(main_r["inputs"])},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "note": "768 flop per unmasked (query, key, head) over the launch's event time, which covers "
+                             "both of its kernels: the fp16 V copy pass and the one-pass forward"},
         "cpu_baseline": cpu,
         "timing": {"median_ms": main_r["median_ms"], "min_ms": main_r["min_ms"],
                    "note": "per-launch HIP events, a second run of the same K launches"},

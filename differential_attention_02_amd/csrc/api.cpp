@@ -246,6 +246,10 @@ static int check_bwd(const diffattn_bwd_args *a) {
   const int64_t *str[] = {a->q_stride, a->k_stride, a->v_stride, a->do_stride, a->dq_stride, a->dk_stride, a->dv_stride};
   if (!fused_layout_ok(ptrs, 11, str, 7))
     return fail(DIFFATTN_ERR_UNSUPPORTED, "backward needs 16-byte aligned pointers and strides that are multiples of 8");
+  // Key tiles are addressed with 32-bit byte offsets inside one (batch, head) slice.
+  const int64_t span = (int64_t)a->seqlen * (a->k_stride[1] > a->v_stride[1] ? a->k_stride[1] : a->v_stride[1]) * 2;
+  if (span >= ((int64_t)1 << 31))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "backward needs seqlen x key-row stride below 2^30 elements");
   return DIFFATTN_OK;
 }
 

@@ -48,6 +48,7 @@
 // unscaled exactly.
 #include "common.h"
 #include "kernels.h"
+#include "v1_stage.h"
 #include "vrange.h"
 
 namespace diffattn {
@@ -294,16 +295,18 @@ struct SmemA {
 };
 
 // One thread's share of a staged query chunk: four 16-byte chunks of the
-// fp16 Q1 | Q2 rows, four of g', and (threads 0..63) one row's statistics.
+// fp16 Q1 | Q2 rows, four of g', and (threads 0..63) one row's statistics as
+// loaded.  Nothing is computed from the loaded values until store_chunk, so
+// the loads stay in flight while the previous chunk is processed.
 struct ChunkRegs {
   u32x4 q[4], g[4];
   float lse1, lse2, e1, e2;
 };
 
 // Loads the chunk of QCH query rows starting at q0 (rows past the end read as
-// zeros, their statistics as masked values).
+// zeros; their statistics are read from the last row and masked when stored).
 __device__ __forceinline__ void load_chunk(const BwdParams &p, const Ws &w, int64_t statb, int q0, int S, int tid,
-                                           float fE, ChunkRegs &r) {
+                                           ChunkRegs &r) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
@@ -312,16 +315,17 @@ __device__ __forceinline__ void load_chunk(const BwdParams &p, const Ws &w, int6
     r.g[k] = ok ? *(const u32x4 *)(w.gh + (statb + q) * DV + col) : u32x4{0, 0, 0, 0};
   }
   if (tid < QCH) {
-    const int q = q0 + tid;
-    const bool ok = q < S;
-    r.lse1 = ok ? p.lse1[statb + q] * kLog2e : __builtin_inff();
-    r.lse2 = ok ? p.lse2[statb + q] * kLog2e : __builtin_inff();
-    r.e1 = ok ? w.e1[statb + q] * fE : 0.f;
-    r.e2 = ok ? w.e2[statb + q] * fE : 0.f;
+    const int64_t q = statb + min(q0 + tid, S - 1);
+    r.lse1 = p.lse1[q];
+    r.lse2 = p.lse2[q];
+    r.e1 = w.e1[q];
+    r.e2 = w.e2[q];
   }
 }
 
-__device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int tid) {
+// Register -> LDS half of the staging; the statistics are scaled (log2 units,
+// E terms by fE) and rows past the end masked here.
+__device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int tid, int q0, int S, float fE) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8;
@@ -330,10 +334,11 @@ __device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int t
     *(u32x4 *)(sm.g + row * GST + col) = r.g[k];
   }
   if (tid < QCH) {
-    sm.lse1[tid] = r.lse1;
-    sm.lse2[tid] = r.lse2;
-    sm.e1[tid] = r.e1;
-    sm.e2[tid] = r.e2;
+    const bool ok = q0 + tid < S;
+    sm.lse1[tid] = ok ? r.lse1 * kLog2e : __builtin_inff();
+    sm.lse2[tid] = ok ? r.lse2 * kLog2e : __builtin_inff();
+    sm.e1[tid] = ok ? r.e1 * fE : 0.f;
+    sm.e2[tid] = ok ? r.e2 * fE : 0.f;
   }
 }
 
@@ -386,14 +391,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   // barrier per chunk.
   ChunkRegs nxt;
   if (q_begin < S) {
-    load_chunk(p, w, statb, q_begin, S, tid, fE, nxt);
-    store_chunk(smb[0], nxt, tid);
+    load_chunk(p, w, statb, q_begin, S, tid, nxt);
+    store_chunk(smb[0], nxt, tid, q_begin, S, fE);
   }
   __syncthreads();
   for (int q0 = q_begin, it = 0; q0 < S; q0 += QCH, ++it) {
     SmemA &sm = smb[it & 1];
     const bool more = q0 + QCH < S;
-    if (more) load_chunk(p, w, statb, q0 + QCH, S, tid, fE, nxt);
+    if (more) load_chunk(p, w, statb, q0 + QCH, S, tid, nxt);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int qs = q0 + sub * 32;
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
         }
       }
     }
-    if (more) store_chunk(smb[(it + 1) & 1], nxt, tid);
+    if (more) store_chunk(smb[(it + 1) & 1], nxt, tid, q0 + QCH, S, fE);
     __syncthreads();
   }
 
@@ -483,24 +488,25 @@ struct SmemB {
   f16 v[KT * GST];
 };
 
-__device__ __forceinline__ void stage_kv(SmemB &sm, const bf16 *k1g, const bf16 *k2g, const bf16 *vg,
-                                         int64_t ks, int64_t vs, int kbase, int S, int tid, const VScale &sck,
-                                         const VScale &scv) {
-  for (int i = tid; i < KT * 8; i += NT) {
-    const int r = i >> 3, col = (i & 7) * 8, key = kbase + r;
-    u32x4 a = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
-    if (key < S) {
-      a = *(const u32x4 *)(k1g + (int64_t)key * ks + col);
-      bb = *(const u32x4 *)(k2g + (int64_t)key * ks + col);
-    }
-    *(f16x8 *)(sm.k1 + r * QST + col) = to_f16x8(a, sck);
-    *(f16x8 *)(sm.k2 + r * QST + col) = to_f16x8(bb, sck);
+// A key tile is staged global -> registers -> LDS in two halves, each loaded
+// while one 32-key sub-tile of the previous tile is computed: K1 and K2, then
+// V (v1s::TileLoader's half-tile loads: bounded buffer loads, so keys past
+// the end read as zeros).
+// Registers -> LDS: fp16 times the slices' range shifts.
+__device__ __forceinline__ void store_k12(SmemB &sm, const u32x4 (&r)[4], int tid, const VScale &sck) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + NT * j, row = i >> 3, col = (i & 7) * 8;
+    *(f16x8 *)(sm.k1 + row * QST + col) = to_f16x8(r[j], sck);
+    *(f16x8 *)(sm.k2 + row * QST + col) = to_f16x8(r[2 + j], sck);
   }
-  for (int i = tid; i < KT * 16; i += NT) {
-    const int r = i >> 4, col = (i & 15) * 8, key = kbase + r;
-    u32x4 a = {0, 0, 0, 0};
-    if (key < S) a = *(const u32x4 *)(vg + (int64_t)key * vs + col);
-    *(f16x8 *)(sm.v + r * GST + col) = to_f16x8(a, scv);
+}
+
+__device__ __forceinline__ void store_v(SmemB &sm, const u32x4 (&r)[4], int tid, const VScale &scv) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + NT * j, row = i >> 4, col = (i & 15) * 8;
+    *(f16x8 *)(sm.v + row * GST + col) = to_f16x8(r[j], scv);
   }
 }
 
@@ -524,7 +530,7 @@ __device__ __forceinline__ void dq_products(const SmemB &sm, int sub, int krow, 
 }
 
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
-  __shared__ SmemB sm;
+  __shared__ SmemB smb[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 31, h = lane >> 5;
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int BH = p.B * p.H;
@@ -576,14 +582,29 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   // ---- dS and dQ
   f32x16 dq1[2], dq2[2];
   dq1[0] = dq1[1] = dq2[0] = dq2[1] = f32x16{};
+  // Key tiles double-buffered in LDS; tile kt + 1 is staged in two halves
+  // (K1 and K2 during sub-tile 0 of tile kt, V during sub-tile 1), so only
+  // one half is held in registers at a time; one barrier per tile.
+  v1s::TileLoader ld;
+  ld.init(k1g, k2g, vg, p.ks_s, p.vs_s, S, tid);
+  u32x4 nx[4];
+  ld.load_k12(0, nx);
+  store_k12(smb[0], nx, tid, sck);
+  ld.load_v(0, nx);
+  store_v(smb[0], nx, tid, scv);
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    stage_kv(sm, k1g, k2g, vg, p.ks_s, p.vs_s, kt * KT, S, tid, sck, scv);
-    __syncthreads();
+    const SmemB &sm = smb[kt & 1];
+    SmemB &sn = smb[(kt + 1) & 1];
+    const bool more = kt + 1 < n_kt;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      if (more) {
+        if (sub == 0) ld.load_k12((kt + 1) * KT, nx);
+        else ld.load_v((kt + 1) * KT, nx);
+      }
       const int sb = kt * KT + sub * 32;
-      if (sb >= S || (p.causal && sb > q_last)) continue;
+      if (sb < S && !(p.causal && sb > q_last)) {
       f32x16 s1, s2, dp;
       dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
       float ds1[16], ds2[16];
@@ -608,7 +629,13 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
           dq2[dt] = mfma32(tr_operand(sm.k2, QST, r0, dt * 32, lane), b2, dq2[dt]);
         }
       }
+      }
+      if (more) {
+        if (sub == 0) store_k12(sn, nx, tid, sck);
+        else store_v(sn, nx, tid, scv);
+      }
     }
+    __syncthreads();
   }
   if (qok) {
     const float fq = p.scale * exp2i(-(kap + sg + kv + kk));

@@ -285,18 +285,35 @@ struct KVRegs {
   u32x4 k[KT * (D / 8) / NT], v[KT * (D / 8) / NT];
 };
 
-__device__ __forceinline__ void load_kv(KVRegs &r, const bf16 *kg, const bf16 *vg, int64_t kvs, int kbase, int S,
-                                        int tid) {
+// Bounded buffer loads of a (batch, KV head) slice's K and V rows: the
+// resources end at the slice's last key row, so keys past the end read as
+// zeros without a branch; byte offsets are 32-bit inside the slice.
+struct KVLoader {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t off[KT * (D / 8) / NT];  // this thread's byte offsets inside a tile
+  uint32_t step;                    // bytes per key row
+
+  __device__ __forceinline__ void init(const bf16 *kg, const bf16 *vg, int64_t kvs, int S, int tid) {
+    const uint32_t bytes = (uint32_t)((int64_t)(S - 1) * kvs * 2 + D * 2);
+    rk = __builtin_amdgcn_make_buffer_rsrc((void *)kg, 0, bytes, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void *)vg, 0, bytes, 0x00020000);
+    step = (uint32_t)(kvs * 2);
 #pragma unroll
-  for (int i = 0; i < KT * (D / 8) / NT; ++i) {
-    const int idx = tid + i * NT, row = idx >> 4, col = (idx & 15) * 8, key = kbase + row;
-    r.k[i] = r.v[i] = u32x4{0, 0, 0, 0};
-    if (key < S) {
-      r.k[i] = *(const u32x4 *)(kg + (int64_t)key * kvs + col);
-      r.v[i] = *(const u32x4 *)(vg + (int64_t)key * kvs + col);
+    for (int i = 0; i < KT * (D / 8) / NT; ++i) {
+      const int idx = tid + i * NT;
+      off[i] = (uint32_t)(idx >> 4) * step + (idx & 15) * 16;
     }
   }
-}
+
+  __device__ __forceinline__ void load(KVRegs &r, int kbase) const {
+    const uint32_t kb = (uint32_t)kbase * step;
+#pragma unroll
+    for (int i = 0; i < KT * (D / 8) / NT; ++i) {
+      r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(off[i] + kb), 0, 0));
+      r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(off[i] + kb), 0, 0));
+    }
+  }
+};
 
 __device__ __forceinline__ void store_kv(SmemQ &sm, const KVRegs &r, int tid, const VScale &sck,
                                          const VScale &scv) {
@@ -360,13 +377,15 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   f32x16 dqe[D / 32], dqo[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dqe[dt] = dqo[dt] = f32x16{};
+  KVLoader ld;
+  ld.init(kg, vg, p.kvs_s, S, tid);
   KVRegs nx;
-  load_kv(nx, kg, vg, p.kvs_s, 0, S, tid);
+  ld.load(nx, 0);
   store_kv(smb[0], nx, tid, sck, scv);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const SmemQ &sm = smb[kt & 1];
-    if (kt + 1 < n_kt) load_kv(nx, kg, vg, p.kvs_s, (kt + 1) * KT, S, tid);
+    if (kt + 1 < n_kt) ld.load(nx, (kt + 1) * KT);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int sb = kt * KT + sub * 32;
@@ -441,14 +460,19 @@ struct SmemC {
 };
 
 // One thread's share of a staged query chunk: eight 16-byte chunks of the
-// fp16 Q_e | Q_o rows, four of g', and (threads 0..63) one row's statistics.
+// fp16 Q_e | Q_o rows, four of g', and (threads 0..63) one row's statistics
+// as loaded.  Nothing is computed from the loaded values until store_chunk2,
+// so the loads stay in flight while the previous chunk is processed.
 struct ChunkRegs2 {
   u32x4 q[8], g[4];
-  float le, lo, ee, eo, sig;
+  float le, lo, ee, eo, lam;
 };
 
+// Loads the chunk of QCH query rows of pair pr starting at q0 (rows past the
+// end read as zeros; their statistics are read from the last row and masked
+// when stored).
 __device__ __forceinline__ void load_chunk2(const V2BwdParams &p, const Ws2 &w, int b, int pr, int64_t rowb,
-                                            int q0, int tid, float fE, ChunkRegs2 &r) {
+                                            int q0, int tid, ChunkRegs2 &r) {
   const int S = p.S;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -461,18 +485,19 @@ __device__ __forceinline__ void load_chunk2(const V2BwdParams &p, const Ws2 &w, 
     r.g[k] = q < S ? *(const u32x4 *)(w.gh + (rowb + q) * D + col) : u32x4{0, 0, 0, 0};
   }
   if (tid < QCH) {
-    const int q = q0 + tid;
-    const bool ok = q < S;
+    const int q = min(q0 + tid, S - 1);
     const int64_t lr = ((int64_t)b * p.Hq + 2 * pr) * S + q;
-    r.le = ok ? p.lse[lr] * kLog2e : __builtin_inff();
-    r.lo = ok ? p.lse[lr + S] * kLog2e : __builtin_inff();
-    r.ee = ok ? w.ee[rowb + q] * fE : 0.f;
-    r.eo = ok ? w.eo[rowb + q] * fE : 0.f;
-    r.sig = ok ? sigmoid_of(p, b, q, pr) : 0.f;
+    r.le = p.lse[lr];
+    r.lo = p.lse[lr + S];
+    r.ee = w.ee[rowb + q];
+    r.eo = w.eo[rowb + q];
+    r.lam = p.lam[b * p.ls_b + (int64_t)q * p.ls_s + pr * p.ls_p];
   }
 }
 
-__device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int tid) {
+// Register -> LDS half of the staging; the statistics are scaled (log2 units,
+// E terms by fE), the sigmoid formed and rows past the end masked here.
+__device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int tid, int q0, int S, float fE) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int i = tid + NT * k, row = i >> 5, col = (i & 31) * 8;
@@ -485,11 +510,12 @@ __device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int
     *(u32x4 *)(sm.g + row * GST + col) = r.g[k];
   }
   if (tid < QCH) {
-    sm.le[tid] = r.le;
-    sm.lo[tid] = r.lo;
-    sm.ee[tid] = r.ee;
-    sm.eo[tid] = r.eo;
-    sm.sig[tid] = r.sig;
+    const bool ok = q0 + tid < S;
+    sm.le[tid] = ok ? r.le * kLog2e : __builtin_inff();
+    sm.lo[tid] = ok ? r.lo * kLog2e : __builtin_inff();
+    sm.ee[tid] = ok ? r.ee * fE : 0.f;
+    sm.eo[tid] = ok ? r.eo * fE : 0.f;
+    sm.sig[tid] = ok ? 1.f / (1.f + expf(-r.lam)) : 0.f;
   }
 }
 
@@ -539,8 +565,8 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
   ChunkRegs2 nxt;
   if (n_it > 0) {
     const int pr = j * ppk;
-    load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin, tid, fE, nxt);
-    store_chunk2(smb[0], nxt, tid);
+    load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin, tid, nxt);
+    store_chunk2(smb[0], nxt, tid, q_begin, S, fE);
   }
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
@@ -549,7 +575,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
     const bool more = it + 1 < n_it;
     if (more) {
       const int pr = j * ppk + (it + 1) / n_ch;
-      load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin + ((it + 1) % n_ch) * QCH, tid, fE, nxt);
+      load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin + ((it + 1) % n_ch) * QCH, tid, nxt);
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -595,7 +621,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
         }
       }
     }
-    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid);
+    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid, q_begin + ((it + 1) % n_ch) * QCH, S, fE);
     __syncthreads();
   }
 

@@ -1,6 +1,7 @@
 // Global -> LDS staging of the DIFF V1 forward's key tiles (bf16, d = 64,
-// dv = 128): 64 keys of K1, K2 and V per tile, 256 threads, V converted to
-// fp16 on its way into LDS.  Used by the two-pass training forward.
+// dv = 128): 64 keys of K1, K2 and V per tile, 256 threads.  The loader is
+// shared by the training forward (which converts V to fp16 on its way into
+// LDS) and the backward's dQ kernel (which stages K1, K2 and V as fp16).
 #pragma once
 
 #include "common.h"
@@ -48,6 +49,25 @@ struct TileLoader {
     for (int i = 0; i < 2; ++i) ko[i] = (uint32_t)(kr + 32 * i) * kstep + (tid & 7) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) vo[i] = (uint32_t)(vr + 16 * i) * vstep + (tid & 15) * 16;
+  }
+
+  // Half-tile loads into one four-chunk register set: K1 and K2 (two chunks
+  // each), or V (four chunks), in the same thread -> (row, column) layout as
+  // load.
+  __device__ __forceinline__ void load_k12(int kbase, u32x4 (&r)[4]) const {
+    const uint32_t kb = (uint32_t)kbase * kstep;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk1, (int)(ko[i] + kb), 0, 0));
+      r[2 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk2, (int)(ko[i] + kb), 0, 0));
+    }
+  }
+
+  __device__ __forceinline__ void load_v(int kbase, u32x4 (&r)[4]) const {
+    const uint32_t vb = (uint32_t)kbase * vstep;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(vo[i] + vb), 0, 0));
   }
 
   __device__ __forceinline__ void load(int kbase, bool with_v, TileRegs &r) const {
