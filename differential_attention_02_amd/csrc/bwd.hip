@@ -323,9 +323,24 @@ __device__ __forceinline__ void load_chunk(const BwdParams &p, const Ws &w, int6
   }
 }
 
-// Register -> LDS half of the staging; the statistics are scaled (log2 units,
-// E terms by fE) and rows past the end masked here.
-__device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int tid, int q0, int S, float fE) {
+// Per-workgroup constants folded into the staged row statistics, so that the
+// score loop forms P1 2^kappa, |lambda| P2 2^kappa and the dS terms with one
+// exponential and one or two operations each:
+//   lse1' = lse1 log2(e) - kappa,  lse2' = lse2 log2(e) - kappa - log2|lambda|
+//   E1' = E1 fE,  E2' = -sigma E2 fE,  sigma = -sign(lambda)
+// (lambda = 0 makes lse2' infinite, so P2 and its terms vanish).
+struct RowFold {
+  float fE, kap, l2lam, sig;
+};
+
+__device__ __forceinline__ RowFold row_fold(float lam, float fE, float kap) {
+  return RowFold{fE, kap, log2f(fabsf(lam)), lam >= 0.f ? -1.f : 1.f};
+}
+
+// Register -> LDS half of the staging; the statistics are folded as above
+// and rows past the end masked (infinite lse', so their P terms are zero).
+__device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int tid, int q0, int S,
+                                            const RowFold &f) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8;
@@ -335,10 +350,34 @@ __device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int t
   }
   if (tid < QCH) {
     const bool ok = q0 + tid < S;
-    sm.lse1[tid] = ok ? r.lse1 * kLog2e : __builtin_inff();
-    sm.lse2[tid] = ok ? r.lse2 * kLog2e : __builtin_inff();
-    sm.e1[tid] = ok ? r.e1 * fE : 0.f;
-    sm.e2[tid] = ok ? r.e2 * fE : 0.f;
+    sm.lse1[tid] = ok ? fmaf(r.lse1, kLog2e, -f.kap) : __builtin_inff();
+    sm.lse2[tid] = ok ? fmaf(r.lse2, kLog2e, -(f.kap + f.l2lam)) : __builtin_inff();
+    sm.e1[tid] = ok ? r.e1 * f.fE : 0.f;
+    sm.e2[tid] = ok ? -f.sig * r.e2 * f.fE : 0.f;
+  }
+}
+
+// Elementwise part of one 32 x 32 block of the key-outer kernel (lane = key,
+// registers = queries qb + row_of_reg(r, h)): the merged dV weight
+// (P1 - lambda P2) 2^omega and dS_m 2^kappa for both maps.  Query qb + o is
+// masked for this lane's key iff o < lo (lo = my_key - qb under the causal
+// mask, 32 for a key past the end, else below 0): one compare per score.
+// Rows past the end already have zero probabilities (infinite lse').
+__device__ __forceinline__ void dkdv_elem(const SmemA &sm, const f32x16 &s1, const f32x16 &s2, const f32x16 &dp,
+                                          int sub, int h, float c, float sig, float fW2, int lo, float *wv,
+                                          float *ds1, float *ds2) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qi = sub * 32 + row_of_reg(r, h);
+    // The mask selects the exponent (-inf for a masked pair), not the result:
+    // a select of the exponential itself was compiled into branches.
+    const bool dead = row_of_reg(r, h) < lo;
+    const float a1 = fmaf(s1[r], c, -sm.lse1[qi]), a2 = fmaf(s2[r], c, -sm.lse2[qi]);
+    const float p1 = fast_exp2(dead ? -__builtin_inff() : a1);  // P1 2^kappa
+    const float p2 = fast_exp2(dead ? -__builtin_inff() : a2);  // |lambda| P2 2^kappa
+    wv[r] = fmaf(sig, p2, p1) * fW2;
+    ds1[r] = p1 * (dp[r] - sm.e1[qi]);
+    ds2[r] = p2 * fmaf(dp[r], sig, sm.e2[qi]);
   }
 }
 
@@ -359,7 +398,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   const VScale sck((int)kk), scv((int)kv);
   // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
   const float c = p.scale * kLog2e * exp2i(-(kq + kk));
-  const float fdS = exp2i(kap), fW = exp2i(om), fE = exp2i(sg + kv);
+  const float fE = exp2i(sg + kv);
 
   // K1, K2 (B operand of S = Q K^T) and V (B operand of dP = g V^T) for my key, fp16.
   f16x8 kf1[4], kf2[4], vf[8];
@@ -389,10 +428,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   // Query chunks double-buffered in LDS: chunk n + 1 is loaded into
   // registers while chunk n is computed, then stored to the other buffer; one
   // barrier per chunk.
+  const RowFold fold = row_fold(lam, fE, kap);
+  const float fW2 = exp2i(om - kap);  // wv = (P1 + sigma |lambda| P2) 2^kappa 2^(omega - kappa)
   ChunkRegs nxt;
   if (q_begin < S) {
     load_chunk(p, w, statb, q_begin, S, tid, nxt);
-    store_chunk(smb[0], nxt, tid, q_begin, S, fE);
+    store_chunk(smb[0], nxt, tid, q_begin, S, fold);
   }
   __syncthreads();
   for (int q0 = q_begin, it = 0; q0 < S; q0 += QCH, ++it) {
@@ -417,21 +458,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
       float wv[16], ds1[16], ds2[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = sub * 32 + row_of_reg(r, h);
-        float p1 = fast_exp2(fmaf(s1[r], c, -sm.lse1[qi]));
-        float p2 = fast_exp2(fmaf(s2[r], c, -sm.lse2[qi]));
-        // Masked pairs as selects, not branches: a uniform test per score
-        // split the loop into blocks the scheduler could not interleave.
-        const int q = q0 + qi;
-        const bool dead = (my_key >= S) | (q >= S) | ((p.causal != 0) & (my_key > q));
-        p1 = dead ? 0.f : p1;
-        p2 = dead ? 0.f : p2;
-        wv[r] = (p1 - lam * p2) * fW;
-        ds1[r] = p1 * (dp[r] - sm.e1[qi]) * fdS;
-        ds2[r] = -lam * p2 * (dp[r] - sm.e2[qi]) * fdS;
-      }
+      const int lo = my_key >= S ? 32 : (p.causal ? my_key - qs : -1);
+      dkdv_elem(sm, s1, s2, dp, sub, h, c, fold.sig, fW2, lo, wv, ds1, ds2);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const f16x8 wb = pack8h(wv + 8 * kc2), b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
@@ -445,7 +473,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
         }
       }
     }
-    if (more) store_chunk(smb[(it + 1) & 1], nxt, tid, q0 + QCH, S, fE);
+    if (more) store_chunk(smb[(it + 1) & 1], nxt, tid, q0 + QCH, S, fold);
     __syncthreads();
   }
 
@@ -529,6 +557,24 @@ __device__ __forceinline__ void dq_products(const SmemB &sm, int sub, int krow, 
   for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(va + kc * 16), gf[kc], dp);
 }
 
+// Elementwise part of one 32 x 32 block of the query-outer kernel (lane =
+// query, registers = keys sb + row_of_reg(r, h)): dS_m 2^kappa for both maps
+// from the folded row terms L1, L2, E1, E2 (RowFold).  Key sb + o of this
+// lane is masked iff o > lim, lim = (last visible key) - sb: one compare per
+// score against the register's fixed offset o.
+__device__ __forceinline__ void dq_elem(const f32x16 &s1, const f32x16 &s2, const f32x16 &dp, int h, float c,
+                                        float L1, float L2, float e1, float e2, float sig, int lim, float *ds1,
+                                        float *ds2) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const bool dead = row_of_reg(r, h) > lim;  // selects the exponent, as in dkdv_elem
+    const float p1 = fast_exp2(dead ? -__builtin_inff() : fmaf(s1[r], c, -L1));
+    const float p2 = fast_exp2(dead ? -__builtin_inff() : fmaf(s2[r], c, -L2));
+    ds1[r] = p1 * (dp[r] - e1);
+    ds2[r] = p2 * fmaf(dp[r], sig, e2);
+  }
+}
+
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   __shared__ SmemB smb[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 31, h = lane >> 5;
@@ -545,7 +591,6 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const VScale scq((int)kq), sck((int)kk), scv((int)kv);
   // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
   const float c = p.scale * kLog2e * exp2i(-(kq + kk));
-  const float fdS = exp2i(kap);
   const int64_t statb = (int64_t)bh * S;
   const bool qok = my_q < S;
 
@@ -563,8 +608,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) gf[kc] = qok ? *(const f16x8 *)(gp + kc * 16) : f16x8{};
   }
-  const float L1 = qok ? p.lse1[statb + my_q] * kLog2e : __builtin_inff();
-  const float L2 = qok ? p.lse2[statb + my_q] * kLog2e : __builtin_inff();
+  // The row statistics folded as in the key-outer kernel (RowFold): the
+  // score loop forms P1 2^kappa, |lambda| P2 2^kappa and dS_m 2^kappa.
+  const RowFold fold = row_fold(lam, exp2i(sg + kv), kap);
+  const float L1 = qok ? fmaf(p.lse1[statb + my_q], kLog2e, -kap) : __builtin_inff();
+  const float L2 = qok ? fmaf(p.lse2[statb + my_q], kLog2e, -(kap + fold.l2lam)) : __builtin_inff();
 
   const int kend = p.causal ? min(S, q0 + QB) : S;
   const int n_kt = (kend + KT - 1) / KT;
@@ -574,10 +622,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const bf16 *k2g = (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h;
   const bf16 *vg = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
 
-  // E_m' = g' . A_m for this query (scaled like dP').
-  const float fE = exp2i(sg + kv);
-  const float e1 = qok ? w.e1[statb + my_q] * fE : 0.f;
-  const float e2 = qok ? w.e2[statb + my_q] * fE : 0.f;
+  // Last key this query sees (the masks as one threshold per block).
+  const int key_lim = p.causal ? min(my_q, S - 1) : S - 1;
+  // E_m' = g' . A_m for this query (scaled like dP'), E2 times -sigma.
+  const float e1 = qok ? w.e1[statb + my_q] * fold.fE : 0.f;
+  const float e2 = qok ? -fold.sig * w.e2[statb + my_q] * fold.fE : 0.f;
 
   // ---- dS and dQ
   f32x16 dq1[2], dq2[2];
@@ -608,17 +657,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
       f32x16 s1, s2, dp;
       dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
       float ds1[16], ds2[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p1 = fast_exp2(fmaf(s1[r], c, -L1));
-        float p2 = fast_exp2(fmaf(s2[r], c, -L2));
-        const int key = sb + row_of_reg(r, h);  // masked pairs as selects (see bwd_dkdv)
-        const bool dead = (key >= S) | ((p.causal != 0) & (key > my_q));
-        p1 = dead ? 0.f : p1;
-        p2 = dead ? 0.f : p2;
-        ds1[r] = p1 * (dp[r] - e1) * fdS;
-        ds2[r] = -lam * p2 * (dp[r] - e2) * fdS;
-      }
+      dq_elem(s1, s2, dp, h, c, L1, L2, e1, e2, fold.sig, key_lim - sb, ds1, ds2);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const f16x8 b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);

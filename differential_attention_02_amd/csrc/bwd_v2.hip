@@ -343,7 +343,6 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   const VScale scq((int)kq), sck((int)kk), scv((int)kv);
   // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
   const float c = p.scale * kLog2e * fast_exp2(-(kq + kk));
-  const float fdS = fast_exp2(kap);
   const int64_t rowb = (int64_t)bp * S;  // row base in [B, P, S]
   const bool qok = my_q < S;
 
@@ -360,12 +359,16 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
     }
   }
   const int64_t lr = ((int64_t)b * p.Hq + 2 * pr) * S + my_q;
-  const float Le = qok ? p.lse[lr] * kLog2e : __builtin_inff();
-  const float Lo = qok ? p.lse[lr + S] * kLog2e : __builtin_inff();
+  // Row terms folded as in the key-outer kernel (store_chunk2): the score
+  // loop forms P_e 2^kappa, sigma P_o 2^kappa and both dS terms directly.
+  const float sig = qok ? sigmoid_of(p, b, my_q, pr) : 0.f;
+  const float Le = qok ? fmaf(p.lse[lr], kLog2e, -kap) : __builtin_inff();
+  const float Lo = qok ? fmaf(p.lse[lr + S], kLog2e, -(kap + log2f(sig))) : __builtin_inff();
   const float fE = fast_exp2(sg + kv);
   const float ee = qok ? w.ee[rowb + my_q] * fE : 0.f;
   const float eo = qok ? w.eo[rowb + my_q] * fE : 0.f;
-  const float sig = qok ? sigmoid_of(p, b, my_q, pr) : 0.f;
+  // Last key this query sees (the masks as one threshold per block).
+  const int key_lim = causal ? min(my_q, S - 1) : S - 1;
 
   const int kend = causal ? min(S, q0 + QB) : S;
   const int n_kt = (kend + KT - 1) / KT;
@@ -401,18 +404,16 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
         dp = mfma32(*(const f16x8 *)(va + kc * 16), gf[kc], dp);
       }
       float dse[16], dso[16];
+      const int lim = key_lim - sb;  // key sb + o is masked iff o > lim
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pe = fast_exp2(fmaf(s_e[r], c, -Le));
-        float po = fast_exp2(fmaf(s_o[r], c, -Lo));
-        // Masked pairs as selects: a uniform test per score split the loop
-        // into blocks the scheduler could not interleave.
-        const int key = sb + row_of_reg(r, h);
-        const bool dead = (key >= S) | (causal & (key > my_q));
-        pe = dead ? 0.f : pe;
-        po = dead ? 0.f : po;
-        dse[r] = pe * (dp[r] - ee) * fdS;
-        dso[r] = -sig * po * (dp[r] - eo) * fdS;
+        // The mask selects the exponent (-inf), not the exponential (a select
+        // of the exponential was compiled into branches).
+        const bool dead = row_of_reg(r, h) > lim;
+        const float pe = fast_exp2(dead ? -__builtin_inff() : fmaf(s_e[r], c, -Le));  // P_e 2^kappa
+        const float po = fast_exp2(dead ? -__builtin_inff() : fmaf(s_o[r], c, -Lo));  // sigma P_o 2^kappa
+        dse[r] = pe * (dp[r] - ee);
+        dso[r] = po * (eo - dp[r]);
       }
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
@@ -456,7 +457,7 @@ struct SmemC {
   f16 qe[QCH * QST];
   f16 qo[QCH * QST];
   f16 g[QCH * GST];
-  float le[QCH], lo[QCH], ee[QCH], eo[QCH], sig[QCH];
+  float le[QCH], lo[QCH], ee[QCH], eo[QCH];
 };
 
 // One thread's share of a staged query chunk: eight 16-byte chunks of the
@@ -495,9 +496,15 @@ __device__ __forceinline__ void load_chunk2(const V2BwdParams &p, const Ws2 &w, 
   }
 }
 
-// Register -> LDS half of the staging; the statistics are scaled (log2 units,
-// E terms by fE), the sigmoid formed and rows past the end masked here.
-__device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int tid, int q0, int S, float fE) {
+// Register -> LDS half of the staging.  The statistics are folded so that
+// the score loop forms P_e 2^kappa, sigma P_o 2^kappa (sigma the row's
+// sigmoid weight) and both dS terms with one exponential and one or two
+// operations each:
+//   le' = lse_e log2(e) - kappa,  lo' = lse_o log2(e) - kappa - log2(sigma),
+//   E_e' = E_e fE,  E_o' = E_o fE;
+// rows past the end get infinite lse' (zero probabilities).
+__device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int tid, int q0, int S, float fE,
+                                             float kap) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int i = tid + NT * k, row = i >> 5, col = (i & 31) * 8;
@@ -511,11 +518,11 @@ __device__ __forceinline__ void store_chunk2(SmemC &sm, const ChunkRegs2 &r, int
   }
   if (tid < QCH) {
     const bool ok = q0 + tid < S;
-    sm.le[tid] = ok ? r.le * kLog2e : __builtin_inff();
-    sm.lo[tid] = ok ? r.lo * kLog2e : __builtin_inff();
+    const float sig = 1.f / (1.f + expf(-r.lam));
+    sm.le[tid] = ok ? fmaf(r.le, kLog2e, -kap) : __builtin_inff();
+    sm.lo[tid] = ok ? fmaf(r.lo, kLog2e, -(kap + log2f(sig))) : __builtin_inff();
     sm.ee[tid] = ok ? r.ee * fE : 0.f;
     sm.eo[tid] = ok ? r.eo * fE : 0.f;
-    sm.sig[tid] = ok ? 1.f / (1.f + expf(-r.lam)) : 0.f;
   }
 }
 
@@ -536,7 +543,8 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
   const VScale sck((int)kk), scv((int)kv);
   // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
   const float c = p.scale * kLog2e * fast_exp2(-(kq + kk));
-  const float fdS = fast_exp2(kap), fW = fast_exp2(om), fE = fast_exp2(sg + kv);
+  const float fE = fast_exp2(sg + kv);
+  const float fW2 = fast_exp2(om - kap);  // wv = (P_e - sigma P_o) 2^kappa 2^(omega - kappa)
 
   // K (B operand of S = Q K^T) and V (B operand of dP' = g' V^T) for my key, fp16.
   f16x8 kf[D / 16], vf[D / 16];
@@ -566,7 +574,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
   if (n_it > 0) {
     const int pr = j * ppk;
     load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin, tid, nxt);
-    store_chunk2(smb[0], nxt, tid, q_begin, S, fE);
+    store_chunk2(smb[0], nxt, tid, q_begin, S, fE, kap);
   }
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
@@ -593,21 +601,21 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
         s_o = mfma32(*(const f16x8 *)(qb + kc * 16), kf[kc], s_o);
         dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
       }
-      const bool need_mask = (causal && qs < kw + 31) || kw + 32 > S || qs + 32 > S;
+      // Query qs + o is masked for my key iff o < lo (keys past the end: all;
+      // causal: queries before the key).  The mask selects the exponent
+      // (-inf), not the exponential, which a select would turn into branches.
+      const int lo = my_key >= S ? 32 : (causal ? my_key - qs : -1);
       float wv[16], dse[16], dso[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = sub * 32 + row_of_reg(r, h);
-        float pe = fast_exp2(fmaf(s_e[r], c, -sm.le[qi]));
-        float po = fast_exp2(fmaf(s_o[r], c, -sm.lo[qi]));
-        if (need_mask) {
-          const int q = q0 + qi;
-          if (my_key >= S || q >= S || (causal && my_key > q)) pe = po = 0.f;
-        }
-        const float sq = sm.sig[qi];
-        wv[r] = (pe - sq * po) * fW;
-        dse[r] = pe * (dp[r] - sm.ee[qi]) * fdS;
-        dso[r] = -sq * po * (dp[r] - sm.eo[qi]) * fdS;
+        const bool dead = row_of_reg(r, h) < lo;
+        const float ae = fmaf(s_e[r], c, -sm.le[qi]), ao = fmaf(s_o[r], c, -sm.lo[qi]);
+        const float pe = fast_exp2(dead ? -__builtin_inff() : ae);  // P_e 2^kappa
+        const float po = fast_exp2(dead ? -__builtin_inff() : ao);  // sigma P_o 2^kappa
+        wv[r] = (pe - po) * fW2;
+        dse[r] = pe * (dp[r] - sm.ee[qi]);
+        dso[r] = po * (sm.eo[qi] - dp[r]);
       }
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
@@ -621,7 +629,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
         }
       }
     }
-    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid, q_begin + ((it + 1) % n_ch) * QCH, S, fE);
+    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid, q_begin + ((it + 1) % n_ch) * QCH, S, fE, kap);
     __syncthreads();
   }
 
