@@ -28,15 +28,11 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 
 
-# Per-source code-generation options.  fwd_mfma.hip: the training-mode forward
-# (one wave per SIMD, O and A2 accumulators in accumulation registers) keeps
-# its score products in ordinary VGPRs instead of copying them out of
-# accumulation registers (~900 fewer register moves per launch, 5 % faster).
-# fwd_onepass.hip: two waves per SIMD, all 256 registers ordinary VGPRs (the
-# default form put the score products in accumulation registers and copied
-# them back).  The other kernels were measured and are faster without it.
-EXTRA = {"fwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "fwd_onepass.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source code-generation options.  fwd_onepass.hip: two waves per SIMD,
+# all 256 registers ordinary VGPRs (the default form put the score products in
+# accumulation registers and copied them back).  The other kernels were
+# measured and are faster without it.
+EXTRA = {"fwd_onepass.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

@@ -129,7 +129,7 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
     const int64_t span = (int64_t)a->seqlen * (a->k_stride[1] > a->v_stride[1] ? a->k_stride[1] : a->v_stride[1]) * 2;
     if (span >= ((int64_t)1 << 31))
       return fail(DIFFATTN_ERR_UNSUPPORTED, "bf16 fused path needs seqlen x key-row stride below 2^30 elements");
-    const size_t need = diffattn::fwd_mfma_workspace_bytes(a->batch, a->seqlen, a->heads, nsave != 0);
+    const size_t need = diffattn::fwd_workspace_bytes(a->batch, a->seqlen, a->heads);
     if (!a->workspace || a->workspace_bytes < need)
       return fail(DIFFATTN_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, a->workspace_bytes);
     if (!aligned16(a->workspace)) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
@@ -151,15 +151,14 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
   p.lambda_out = a->lambda_out;
   p.lse1 = a->lse1; p.lse2 = a->lse2; p.rstd = a->rstd; p.o_pre = a->o_pre; p.a2 = a->a2;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fused) return hip_status(diffattn::launch_fwd_mfma(p, a->workspace, st), "fused forward launch");
+  if (fused) return hip_status(diffattn::launch_fwd(p, a->workspace, st), "fused forward launch");
   return hip_status(diffattn::launch_fwd_generic(p, a->dtype, a->head_dim, a->v_dim, st), "forward launch");
 }
 
 size_t diffattn_fwd_workspace_size(const diffattn_fwd_args *a) {
   if (!a || a->batch <= 0 || a->seqlen <= 0 || a->heads < 1) return 0;
   const bool fused = a->dtype == DIFFATTN_BF16 && a->head_dim == 64 && a->v_dim == 128;
-  const bool training = a->lse1 || a->lse2 || a->rstd || a->o_pre || a->a2;
-  return fused ? diffattn::fwd_mfma_workspace_bytes(a->batch, a->seqlen, a->heads, training) : 0;
+  return fused ? diffattn::fwd_workspace_bytes(a->batch, a->seqlen, a->heads) : 0;
 }
 
 static int check_fwd_fp8(const diffattn_fwd_args *a) {

@@ -79,6 +79,22 @@ __device__ __forceinline__ f16x8 pack8(const float *w) {
   return r;
 }
 
+// w = hi + lo with both halves in fp16: lo carries the rounding residual of
+// hi, so hi V + lo V is accurate to about 2^-22 of |w| |V|.
+__device__ __forceinline__ void pack8_hilo(const float *w, f16x8 &hi, f16x8 &lo) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 x = {w[i], w[i + 1]};
+    const f16x2 y = __builtin_convertvector(x, f16x2);
+    const f32x2 back = __builtin_convertvector(y, f32x2);
+    const f16x2 z = __builtin_convertvector(x - back, f16x2);
+    hi[i] = y[0];
+    hi[i + 1] = y[1];
+    lo[i] = z[0];
+    lo[i + 1] = z[1];
+  }
+}
+
 // O^T[ct] += V^T (channels 32 ct .. 32 ct + 31, keys of sub-tile chunk kc2)
 // W^T for NCT channel tiles, V^T from a row-major fp16 tile with row stride
 // VSTRIDE through LDS transpose reads.

@@ -159,12 +159,16 @@ __device__ __forceinline__ float move_ref(float &m, float mn) {
 
 // Scores of both maps over one 32-key sub-tile and the softmax bookkeeping;
 // returns the fp16 B operands of the sub-tile's two PV products
-// (w = e1 - kappa e2, and e2).
-template <bool MASKED>
+// (w = e1 - kappa e2, and e2).  With SAVE kappa stays 0 (X = sum e1 V) and
+// each weight is split into fp16 hi + lo halves (wb, eb the hi halves; wl, el
+// the lo halves), so X and Y, and with them the saved O and A2, are
+// accurate to about 2^-22 relative: the backward's lambda gradient sums
+// g . A2 over every row with heavy cancellation.
+template <bool MASKED, bool SAVE>
 __device__ __forceinline__ void sub_softmax(const Smem &sm, int sub, int sb, int krow, int lane, const bf16x8 *q1f,
                                             const bf16x8 *q2f, float c, float lam, float bnd, RowState &st,
                                             f32x16 *x, f32x16 *y, int S, bool causal, int my_q, f16x8 *wb,
-                                            f16x8 *eb) {
+                                            f16x8 *eb, f16x8 *wl, f16x8 *el) {
   const int h = lane >> 5;
   f32x16 s1 = score_map(sm.k1, sub, krow, h, q1f);
   f32x16 s2 = score_map(sm.k2, sub, krow, h, q2f);
@@ -227,6 +231,13 @@ __device__ __forceinline__ void sub_softmax(const Smem &sm, int sub, int sb, int
   }
   st.l1 += t1;
   st.l2 += t2;
+  if constexpr (SAVE) {
+    pack8_hilo(e1, wb[0], wl[0]);
+    pack8_hilo(e1 + 8, wb[1], wl[1]);
+    pack8_hilo(e2, eb[0], el[0]);
+    pack8_hilo(e2 + 8, eb[1], el[1]);
+    return;
+  }
   // kappa tracks lambda L1 / L2 (merged sums including this sub-tile).
   const float ks = L2 > 0.f ? lam * L1 * __builtin_amdgcn_rcpf(L2) : 0.f;
   if (fabsf(ks - st.kap) > 0x1p-7f * fabsf(ks)) {
@@ -243,9 +254,11 @@ __device__ __forceinline__ void sub_softmax(const Smem &sm, int sub, int sb, int
   eb[1] = pack8(e2 + 8);
 }
 
-// X^T += V^T W^T and Y^T += V^T E^T over one sub-tile.
+// X^T += V^T W^T and Y^T += V^T E^T over one sub-tile (with SAVE, the hi
+// and lo halves of both weights: four products per V operand).
+template <bool SAVE>
 __device__ __forceinline__ void sub_pv(const Smem &sm, int sub, int lane, const f16x8 *wb, const f16x8 *eb,
-                                       f32x16 *x, f32x16 *y) {
+                                       const f16x8 *wl, const f16x8 *el, f32x16 *x, f32x16 *y) {
   const int h = lane >> 5, j = lane & 15, half16 = (lane >> 4) & 1;
 #pragma unroll
   for (int kc2 = 0; kc2 < 2; ++kc2) {
@@ -258,6 +271,10 @@ __device__ __forceinline__ void sub_pv(const Smem &sm, int sub, int lane, const 
       const f16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       x[ct] = mfma32(va, wb[kc2], x[ct]);
       y[ct] = mfma32(va, eb[kc2], y[ct]);
+      if constexpr (SAVE) {
+        x[ct] = mfma32(va, wl[kc2], x[ct]);
+        y[ct] = mfma32(va, el[kc2], y[ct]);
+      }
     }
   }
 }
@@ -273,6 +290,10 @@ __device__ __forceinline__ void rescale_acc(f32x16 *x, f32x16 *y, int dk, int &v
   vk += dk;
 }
 
+// SAVE also writes the training saves: lse_m = (m_m + log2 L_m) ln 2, the
+// pre-norm output O, A2 = Y / L2 (the second map's attention output) and the
+// RMSNorm's rstd.
+template <bool SAVE>
 __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   __shared__ Smem sm[NBUF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -336,9 +357,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   // the start of the next tile (buffer (kt - 1) % 3, still intact), so that on
   // every SIMD one wave's matrix work overlaps the other's softmax arithmetic
   // instead of both waves reaching each phase together after the barrier.
-  const bool lag = wave >= 4;
+  // (Not with SAVE: its hi/lo weights would double the deferred registers.)
+  const bool lag = !SAVE && wave >= 4;
   bool pending = false;
-  f16x8 pw[2], pe[2];
+  f16x8 pw[2], pe[2], pwl[SAVE ? 2 : 1], pel[SAVE ? 2 : 1];
   int cur = 0, prv = NBUF - 1, nxb = 1;
   Stage nxt;
   ld.load(0, nxt);
@@ -349,18 +371,19 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   for (int kt = 0; kt < n_full; ++kt) {
     ld.load((kt + 1) * BN, nxt);  // past the end: the buffer range gives zeros
     sched_fence();
-    if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);
+    if (pending) sub_pv<SAVE>(sm[prv], 1, lane, pw, pe, pwl, pel, x, y);
     if (ktile != vk) rescale_acc(x, y, ktile - vk, vk);
     ktile = __builtin_amdgcn_readfirstlane(vexp[min((kt + 1) * BN, kend - 1) / kVRangeRows]);
     {
-      f16x8 wb[2], eb[2];
-      sub_softmax<false>(sm[cur], 0, kt * BN, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
-      sub_pv(sm[cur], 0, lane, wb, eb, x, y);
+      f16x8 wb[2], eb[2], wl[SAVE ? 2 : 1], el[SAVE ? 2 : 1];
+      sub_softmax<false, SAVE>(sm[cur], 0, kt * BN, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q,
+                               wb, eb, wl, el);
+      sub_pv<SAVE>(sm[cur], 0, lane, wb, eb, wl, el, x, y);
     }
-    sub_softmax<false>(sm[cur], 1, kt * BN + 32, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, pw,
-                       pe);
+    sub_softmax<false, SAVE>(sm[cur], 1, kt * BN + 32, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q,
+                             pw, pe, pwl, pel);
     pending = lag;
-    if (!lag) sub_pv(sm[cur], 1, lane, pw, pe, x, y);
+    if (!lag) sub_pv<SAVE>(sm[cur], 1, lane, pw, pe, pwl, pel, x, y);
     sched_fence();
     store_stage(sm[nxb], nxt, tid);
     __syncthreads();
@@ -371,7 +394,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, nxt);
     sched_fence();
-    if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);
+    if (pending) sub_pv<SAVE>(sm[prv], 1, lane, pw, pe, pwl, pel, x, y);
     pending = false;
     if (ktile != vk) rescale_acc(x, y, ktile - vk, vk);
     ktile = __builtin_amdgcn_readfirstlane(vexp[min((kt + 1) * BN, kend - 1) / kVRangeRows]);
@@ -379,12 +402,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
     for (int sub = 0; sub < 2; ++sub) {
       const int sb = kt * BN + sub * 32;
       if (sb >= S || (causal && sb > qw + 31)) continue;  // wave-uniform
-      f16x8 wb[2], eb[2];
+      f16x8 wb[2], eb[2], wl[SAVE ? 2 : 1], el[SAVE ? 2 : 1];
       if ((causal && sb + 31 > qw) || sb + 32 > S)
-        sub_softmax<true>(sm[cur], sub, sb, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
+        sub_softmax<true, SAVE>(sm[cur], sub, sb, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb,
+                                eb, wl, el);
       else
-        sub_softmax<false>(sm[cur], sub, sb, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb, eb);
-      sub_pv(sm[cur], sub, lane, wb, eb, x, y);
+        sub_softmax<false, SAVE>(sm[cur], sub, sb, krow, lane, q1f, q2f, c, lam, bnd, st, x, y, S, causal, my_q, wb,
+                                 eb, wl, el);
+      sub_pv<SAVE>(sm[cur], sub, lane, wb, eb, wl, el, x, y);
     }
     sched_fence();
     store_stage(sm[nxb], nxt, tid);
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
     cur = nxb;
     nxb = nxb == NBUF - 1 ? 0 : nxb + 1;
   }
-  if (pending) sub_pv(sm[prv], 1, lane, pw, pe, x, y);  // only when there was no masked tile
+  if (pending) sub_pv<SAVE>(sm[prv], 1, lane, pw, pe, pwl, pel, x, y);  // only when there was no masked tile
 
   // O = X / L1 + (kappa / L1 - lambda / L2) Y; per-head RMSNorm x (1 - lambda_init).
   const float L1 = st.l1 + other_half(st.l1);
@@ -423,15 +448,50 @@ __global__ __launch_bounds__(NT, 1) void fwd_onepass_kernel(FwdParams p) {
                      f2bf(x[ct][4 * g + 3] * f)};
         *(bf16x4 *)(out + ch) = yv;
       }
+    if constexpr (SAVE) {
+      const int64_t row = ((int64_t)b * S + my_q) * p.H + hd;  // saves are [B, S, H, DV]
+      float *op = p.o_pre + row * DV;
+      float *ap = p.a2 + row * DV;
+      const float i2 = unv / L2;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = ct * 32 + 8 * g + 4 * h;
+          *(f32x4 *)(op + ch) = f32x4{x[ct][4 * g], x[ct][4 * g + 1], x[ct][4 * g + 2], x[ct][4 * g + 3]};
+          *(f32x4 *)(ap + ch) = f32x4{y[ct][4 * g], y[ct][4 * g + 1], y[ct][4 * g + 2], y[ct][4 * g + 3]} * i2;
+        }
+      if (h == 0) {
+        const int64_t si = ((int64_t)b * p.H + hd) * S + my_q;  // [B, H, S]
+        p.lse1[si] = (st.m1 + log2f(L1)) * kLn2;
+        p.lse2[si] = (st.m2 + log2f(L2)) * kLn2;
+        p.rstd[si] = rstd;
+      }
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_onepass(const FwdParams &p, hipStream_t st) {
+size_t fwd_workspace_bytes(int B, int S, int H) { return vconv_bytes(B, S, H); }
+
+hipError_t launch_fwd(const FwdParams &p0, void *workspace, hipStream_t st) {
+  // The fp16 copy of V (with its per-chunk shifts) is written first; the
+  // one-pass kernel reads it.
+  FwdParams p = p0;
+  VConvParams vc{p.v, p.vs_b, p.vs_s, p.vs_h, p.B, p.S, p.H, static_cast<f16 *>(workspace), nullptr};
+  vc.kexp = reinterpret_cast<int *>(static_cast<char *>(workspace) +
+                                    (((size_t)p.B * p.H * p.S * DV * 2 + 255) & ~(size_t)255));
+  hipError_t e = launch_vconv(vc, st);
+  if (e != hipSuccess) return e;
+  p.v16 = vc.v16;
+  p.vexp = vc.kexp;
   const int n_qt = (p.S + OBM - 1) / OBM;
   dim3 grid(n_qt * p.B * p.H), block(NT);
-  hipLaunchKernelGGL(fwd_onepass_kernel, grid, block, 0, st, p);
+  if (p.lse1)
+    hipLaunchKernelGGL(fwd_onepass_kernel<true>, grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL(fwd_onepass_kernel<false>, grid, block, 0, st, p);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ struct FwdParams {
   float eps;
   float *lambda_out;
   float *lse1, *lse2, *rstd, *o_pre, *a2;  // training saves (all or none)
-  const unsigned *vpart;  // V range partials (vrange.hip): the training forward
+  const unsigned *vpart;  // V range partials (vrange.hip): the fp8-logit forward
   const _Float16 *v16;    // the one-pass forward's fp16 copy of V and its
   const int *vexp;        // per-256-row-chunk shifts (vrange.hip)
 };
@@ -139,12 +139,11 @@ hipError_t launch_vconv(const VConvParams &p, hipStream_t st);
 
 // Reference vector-ALU forward: any supported (d, dv), f32 or bf16.
 hipError_t launch_fwd_generic(const FwdParams &p, int dtype, int d, int dv, hipStream_t st);
-// Fused bf16 matrix-core forward, d = 64, dv = 128: the one-pass kernel
-// without training saves, the two-pass kernel with them.
-// The workspace holds the pass over V's results (vrange.hip).
-size_t fwd_mfma_workspace_bytes(int B, int S, int H, bool training);
-hipError_t launch_fwd_mfma(const FwdParams &p, void *workspace, hipStream_t st);
-hipError_t launch_fwd_onepass(const FwdParams &p, hipStream_t st);
+// Fused bf16 matrix-core forward, d = 64, dv = 128 (one-pass kernel, with or
+// without the training saves).  The workspace holds the fp16 copy of V and
+// its per-chunk shifts (vrange.hip).
+size_t fwd_workspace_bytes(int B, int S, int H);
+hipError_t launch_fwd(const FwdParams &p, void *workspace, hipStream_t st);
 // The same forward with fp8 e4m3 score operands (per-row power-of-two absmax
 // scales); the workspace holds the codes and exponents.
 size_t fwd_fp8_workspace_bytes(int B, int S, int H);

@@ -1,6 +1,6 @@
 // Global -> LDS staging of the DIFF V1 forward's key tiles (bf16, d = 64,
 // dv = 128): 64 keys of K1, K2 and V per tile, 256 threads.  The loader is
-// shared by the training forward (which converts V to fp16 on its way into
+// shared by the fp8-logit forward (which converts V to fp16 on its way into
 // LDS) and the backward's dQ kernel (which stages K1, K2 and V as fp16).
 #pragma once
 

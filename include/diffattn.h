@@ -85,13 +85,10 @@ extern "C" {
  *   workspace: device memory of at least diffattn_fwd_workspace_size() bytes,
  *     16-byte aligned (contents on entry do not matter), for the bf16
  *     matrix-core path: a first pass over V writes there an fp16 copy of V
- *     with one power-of-two shift per 256-row chunk (inference), or the
- *     largest |v| of every 256-row chunk from which each workgroup picks the
- *     shift of its own fp16 copy (training saves), so V may take any finite
- *     bf16 magnitude (B x H x S x 256 bytes and a little more for inference,
- *     a few bytes per 256 rows with training saves).  Not read by the
- *     vector-kernel paths (size 0) nor by diffattn_fwd_fp8, which takes its
- *     own workspace.
+ *     with one power-of-two shift per 256-row chunk, so V may take any finite
+ *     bf16 magnitude (B x H x S x 256 bytes and a few bytes per 256 rows,
+ *     with or without training saves).  Not read by the vector-kernel paths
+ *     (size 0) nor by diffattn_fwd_fp8, which takes its own workspace.
  *   batch = 0 or seqlen = 0 is an empty problem: DIFFATTN_OK, nothing read.
  */
 typedef struct diffattn_fwd_args {
