@@ -1,5 +1,6 @@
-// One-pass causal/non-causal inference forward of multi-head differential
-// attention on gfx950 matrix cores: bf16 storage, d = 64, dv = 128.
+// One-pass causal/non-causal forward of multi-head differential attention on
+// gfx950 matrix cores: bf16 storage, d = 64, dv = 128; inference, or with the
+// training saves the backward reads (lse1, lse2, rstd, O, A2).
 //
 // The operator (glossary page "Differential Transformer", section "How
 // differential attention works"; news write-up, multi-head section):
@@ -23,7 +24,10 @@
 // l1 and l2 by bnd keeps every weight inside fp16 (e_m <= l_m and
 // |kappa e2| <~ |lambda| l1).
 // Matrix-core work per (query, key) pair: 2 QK^T products of width 64 and
-// 2 PV products of width 128 (768 flop); two exponentials.
+// 2 PV products of width 128 (768 flop); two exponentials.  The training
+// variant keeps kappa at 0 and splits both weights into fp16 hi + lo halves
+// (4 PV products, 1280 flop issued per pair), so the saved O and A2 carry
+// about 2^-22 relative error rather than fp16's 2^-11.
 //
 // Work split.  One workgroup of 8 waves (two per SIMD) owns 256 query rows of
 // one (batch, head); each wave owns a 32-row block, the two waves sharing a
