@@ -7,8 +7,11 @@
 // Decode is bound by HBM bandwidth (that page, item 1): the kernel's job is to
 // stream the K and V cache exactly once at full rate.  Split-K layout:
 //   decode_split: one workgroup per (key chunk, KV head (or part of its query
-//     group), batch).  Every query head of the group is served by the same
-//     workgroup, so each K/V byte is read once for all of them.  Phase 1
+//     group), batch).  Up to four query heads of the group are served by the
+//     same workgroup, so for groups of 2 or 4 heads each K/V byte is read
+//     once for all of them; larger groups take several workgroups per KV head
+//     whose repeated reads of a chunk are meant to hit the L2 (ordinary loads
+//     there, non-temporal ones only for a chunk's single reader).  Phase 1
 //     streams K (D / 8 lanes per key row, 16-byte loads, whole rows per load
 //     instruction) and writes log2-domain scores to LDS; phase 2 takes each
 //     head's max and sum over the chunk; phase 3 streams V and accumulates the
@@ -55,27 +58,32 @@ struct Raw8 {
   u32x4 a, b;
 };
 
-template <typename T>
+template <typename T, bool STREAM = true>
 struct RowLoad;
 
-// Cache rows are read exactly once per call, so the loads carry the
-// non-temporal hint: the lines are not kept in the caches for reuse, which
-// lets the stream run about 10 % faster than with ordinary loads.
-template <>
-struct RowLoad<bf16> {
+// 16-byte loads of cache rows.  STREAM: the row is read once per call, so the
+// load carries the non-temporal hint (the line is not kept in the caches for
+// reuse, which lets the stream run about 10 % faster than ordinary loads).
+// Without STREAM (rows that other workgroups of the same call read again)
+// the loads are ordinary, so the repeats can hit the L2.
+template <bool STREAM>
+struct RowLoad<bf16, STREAM> {
   typedef u32x4 raw_t;
   static __device__ __forceinline__ raw_t load(const bf16 *p) {
-    return __builtin_nontemporal_load((const u32x4 *)p);
+    if constexpr (STREAM) return __builtin_nontemporal_load((const u32x4 *)p);
+    else return *(const u32x4 *)p;
   }
   static __device__ __forceinline__ raw_t zero() { return u32x4{0, 0, 0, 0}; }
   static __device__ __forceinline__ void cvt(const raw_t &r, float *f) { to_f32x8<bf16>(r, f); }
 };
 
-template <>
-struct RowLoad<float> {
+template <bool STREAM>
+struct RowLoad<float, STREAM> {
   typedef Raw8 raw_t;
   static __device__ __forceinline__ raw_t load(const float *p) {
-    return Raw8{__builtin_nontemporal_load((const u32x4 *)p), __builtin_nontemporal_load((const u32x4 *)(p + 4))};
+    if constexpr (STREAM)
+      return Raw8{__builtin_nontemporal_load((const u32x4 *)p), __builtin_nontemporal_load((const u32x4 *)(p + 4))};
+    else return Raw8{*(const u32x4 *)p, *(const u32x4 *)(p + 4)};
   }
   static __device__ __forceinline__ raw_t zero() { return Raw8{{0, 0, 0, 0}, {0, 0, 0, 0}}; }
   static __device__ __forceinline__ void cvt(const raw_t &r, float *f) {
@@ -87,13 +95,15 @@ struct RowLoad<float> {
   }
 };
 
-template <typename T, int D, int NH>
+// STREAM: this workgroup serves every query head of its KV head (the group
+// has at most NH heads), so it is the only reader of its K/V chunk.
+template <typename T, int D, int NH, bool STREAM>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;      // lanes per key row (8 channels each)
   constexpr int KPW = 64 / LPK;   // keys per wave per load step
   constexpr int U = 4;            // load steps in flight per lane
   constexpr int STEP = 4 * KPW * U;
-  typedef RowLoad<T> RL;
+  typedef RowLoad<T, STREAM> RL;
   typedef typename RL::raw_t raw_t;
 
   __shared__ float s_lds[NH][MAX_CHUNK];
@@ -262,10 +272,18 @@ hipError_t launch_typed(const DecodeParams &p, hipStream_t st) {
   const int G = p.Hq / p.Hkv;
   const int nh = (G % 4 == 0) ? 4 : 2;
   dim3 grid(p.splits, p.Hkv * (G / nh), p.B);
-  if (nh == 4)
-    hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(NT), 0, st, p);
+  // Groups of more than nh query heads take G / nh workgroups per KV head,
+  // which read the same chunk: those loads stay ordinary so the repeats can
+  // be served by the L2.
+  const bool stream = G == nh;
+  if (nh == 4 && stream)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, 4, true>), grid, dim3(NT), 0, st, p);
+  else if (nh == 4)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, 4, false>), grid, dim3(NT), 0, st, p);
+  else if (stream)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, 2, true>), grid, dim3(NT), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, 2>), grid, dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, 2, false>), grid, dim3(NT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.Hq / 2, p.B), dim3(D), 0, st, p);

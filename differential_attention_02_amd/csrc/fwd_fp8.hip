@@ -1,8 +1,9 @@
 // Differential attention forward with fp8 attention logits on gfx950: the
 // score products Q1 K1^T and Q2 K2^T run on fp8 e4m3 operands (scaled fp8
 // matrix instructions, v_mfma_scale_f32_32x32x64_f8f6f4), everything after
-// the scores as in the bf16 forward (two passes, combined fp16 weight, fp16 V,
-// per-head RMSNorm x (1 - lambda_init)).  bf16 storage, d = 64, dv = 128.
+// the scores in two passes (pass 1: each map's exact log-sum-exp; pass 2: the
+// combined weight rounded once to fp16, fp16 V, per-head RMSNorm x
+// (1 - lambda_init)).  bf16 storage, d = 64, dv = 128.
 //
 // Quantisation (the low-bit attention-logit study and the "low-bit
 // FlashAttention" outlook on the pages: absmax dynamic post-training

@@ -64,10 +64,10 @@ def test_split_invariance():
     assert_f32(outs[0], _ref(inp), "decode splits")
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (12, 2), (4, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (12, 2), (4, 2), (16, 2)])
 def test_query_groups(Hq, Hkv):
-    """Groups of 4 and 6 query heads per KV head: even/odd pairs stay inside
-    their group."""
+    """Groups of 2, 4, 6 and 8 query heads per KV head (6 and 8 take several
+    workgroups per KV head): even/odd pairs stay inside their group."""
     inp = _case(3, 2, Hq, Hkv, 64, 400, torch.float32)
     assert_f32(_run(inp), _ref(inp), f"decode Hq={Hq} Hkv={Hkv}")
 
