@@ -46,6 +46,8 @@
 // their largest magnitudes (bwd_pre, bwd_scales; vrange.h), so any finite bf16
 // inputs convert without saturating or losing precision, and every result is
 // unscaled exactly.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "v1_stage.h"
@@ -363,6 +365,7 @@ __device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int t
 // masked for this lane's key iff o < lo (lo = my_key - qb under the causal
 // mask, 32 for a key past the end, else below 0): one compare per score.
 // Rows past the end already have zero probabilities (infinite lse').
+template <bool MASK>
 __device__ __forceinline__ void dkdv_elem(const SmemA &sm, const f32x16 &s1, const f32x16 &s2, const f32x16 &dp,
                                           int sub, int h, float c, float sig, float fW2, int lo, float *wv,
                                           float *ds1, float *ds2) {
@@ -371,7 +374,7 @@ __device__ __forceinline__ void dkdv_elem(const SmemA &sm, const f32x16 &s1, con
     const int qi = sub * 32 + row_of_reg(r, h);
     // The mask selects the exponent (-inf for a masked pair), not the result:
     // a select of the exponential itself was compiled into branches.
-    const bool dead = row_of_reg(r, h) < lo;
+    const bool dead = MASK && row_of_reg(r, h) < lo;
     const float a1 = fmaf(s1[r], c, -sm.lse1[qi]), a2 = fmaf(s2[r], c, -sm.lse2[qi]);
     const float p1 = fast_exp2(dead ? -__builtin_inff() : a1);  // P1 2^kappa
     const float p2 = fast_exp2(dead ? -__builtin_inff() : a2);  // |lambda| P2 2^kappa
@@ -436,7 +439,13 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
     store_chunk(smb[0], nxt, tid, q_begin, S, fold);
   }
   __syncthreads();
-  for (int q0 = q_begin, it = 0; q0 < S; q0 += QCH, ++it) {
+  // One chunk; MASKED applies the key-range and causal masks.  Only the chunks
+  // on this workgroup's diagonal (the first KVB / QCH under the causal mask)
+  // and, in the workgroup holding the last keys, every chunk need them: two
+  // loops, one per form, so the unmasked one carries no mask arithmetic and
+  // no branch.
+  auto chunk = [&](auto masked, int q0, int it) {
+    constexpr bool MASKED = decltype(masked)::value;
     SmemA &sm = smb[it & 1];
     const bool more = q0 + QCH < S;
     if (more) load_chunk(p, w, statb, q0 + QCH, S, tid, nxt);
@@ -459,7 +468,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
       for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(ga + kc * 16), vf[kc], dp);
       float wv[16], ds1[16], ds2[16];
       const int lo = my_key >= S ? 32 : (p.causal ? my_key - qs : -1);
-      dkdv_elem(sm, s1, s2, dp, sub, h, c, fold.sig, fW2, lo, wv, ds1, ds2);
+      dkdv_elem<MASKED>(sm, s1, s2, dp, sub, h, c, fold.sig, fW2, lo, wv, ds1, ds2);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const f16x8 wb = pack8h(wv + 8 * kc2), b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
@@ -475,7 +484,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
     }
     if (more) store_chunk(smb[(it + 1) & 1], nxt, tid, q0 + QCH, S, fold);
     __syncthreads();
-  }
+  };
+  const int n_ch = q_begin < S ? (S - q_begin + QCH - 1) / QCH : 0;
+  const int n_mask = kb + KVB > S ? n_ch : (p.causal ? min(n_ch, KVB / QCH) : 0);
+  int it = 0;
+  for (; it < n_mask; ++it) chunk(std::true_type{}, q_begin + it * QCH, it);
+  for (; it < n_ch; ++it) chunk(std::false_type{}, q_begin + it * QCH, it);
 
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
   if (my_key < S) {
@@ -562,12 +576,13 @@ __device__ __forceinline__ void dq_products(const SmemB &sm, int sub, int krow, 
 // from the folded row terms L1, L2, E1, E2 (RowFold).  Key sb + o of this
 // lane is masked iff o > lim, lim = (last visible key) - sb: one compare per
 // score against the register's fixed offset o.
+template <bool MASK>
 __device__ __forceinline__ void dq_elem(const f32x16 &s1, const f32x16 &s2, const f32x16 &dp, int h, float c,
                                         float L1, float L2, float e1, float e2, float sig, int lim, float *ds1,
                                         float *ds2) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const bool dead = row_of_reg(r, h) > lim;  // selects the exponent, as in dkdv_elem
+    const bool dead = MASK && row_of_reg(r, h) > lim;  // selects the exponent, as in dkdv_elem
     const float p1 = fast_exp2(dead ? -__builtin_inff() : fmaf(s1[r], c, -L1));
     const float p2 = fast_exp2(dead ? -__builtin_inff() : fmaf(s2[r], c, -L2));
     ds1[r] = p1 * (dp[r] - e1);
@@ -642,7 +657,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   ld.load_v(0, nx);
   store_v(smb[0], nx, tid, scv);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // One key tile; MASKED applies the causal and key-range masks, which only
+  // the tiles from the query tile's start on (causal) and a partial last tile
+  // need: two loops, so the interior one carries no mask arithmetic.
+  auto tile = [&](auto masked, int kt) {
+    constexpr bool MASKED = decltype(masked)::value;
     const SmemB &sm = smb[kt & 1];
     SmemB &sn = smb[(kt + 1) & 1];
     const bool more = kt + 1 < n_kt;
@@ -657,7 +676,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
       f32x16 s1, s2, dp;
       dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
       float ds1[16], ds2[16];
-      dq_elem(s1, s2, dp, h, c, L1, L2, e1, e2, fold.sig, key_lim - sb, ds1, ds2);
+      dq_elem<MASKED>(s1, s2, dp, h, c, L1, L2, e1, e2, fold.sig, key_lim - sb, ds1, ds2);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const f16x8 b1 = pack8h(ds1 + 8 * kc2), b2 = pack8h(ds2 + 8 * kc2);
@@ -675,7 +694,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
       }
     }
     __syncthreads();
-  }
+  };
+  const int n_full = min(p.causal ? q0 / KT : n_kt, S / KT);  // tiles no query of the tile needs masked
+  int kt = 0;
+  for (; kt < n_full; ++kt) tile(std::false_type{}, kt);
+  for (; kt < n_kt; ++kt) tile(std::true_type{}, kt);
   if (qok) {
     const float fq = p.scale * exp2i(-(kap + sg + kv + kk));
     bf16 *d1 = (bf16 *)p.dq1 + b * p.dqs_b + (int64_t)my_q * p.dqs_s + hd * p.dqs_h;

@@ -36,6 +36,8 @@
 // their largest magnitudes (v2b_pre, v2b_scales; vrange.h), so any finite bf16
 // inputs convert without saturating or losing precision; results are unscaled
 // exactly.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "vrange.h"
@@ -386,7 +388,11 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   ld.load(nx, 0);
   store_kv(smb[0], nx, tid, sck, scv);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // One key tile; MASKED applies the causal and key-range masks, which only
+  // the tiles from the query tile's start on (causal) and a partial last tile
+  // need: two loops, so the interior one carries no mask arithmetic.
+  auto tile = [&](auto masked, int kt) {
+    constexpr bool MASKED = decltype(masked)::value;
     const SmemQ &sm = smb[kt & 1];
     if (kt + 1 < n_kt) ld.load(nx, (kt + 1) * KT);
 #pragma unroll
@@ -409,7 +415,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
       for (int r = 0; r < 16; ++r) {
         // The mask selects the exponent (-inf), not the exponential (a select
         // of the exponential was compiled into branches).
-        const bool dead = row_of_reg(r, h) > lim;
+        const bool dead = MASKED && row_of_reg(r, h) > lim;
         const float pe = fast_exp2(dead ? -__builtin_inff() : fmaf(s_e[r], c, -Le));  // P_e 2^kappa
         const float po = fast_exp2(dead ? -__builtin_inff() : fmaf(s_o[r], c, -Lo));  // sigma P_o 2^kappa
         dse[r] = pe * (dp[r] - ee);
@@ -429,7 +435,11 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
     }
     if (kt + 1 < n_kt) store_kv(smb[(kt + 1) & 1], nx, tid, sck, scv);  // the buffer tile kt - 1 used
     __syncthreads();
-  }
+  };
+  const int n_full = min(causal ? q0 / KT : n_kt, S / KT);  // tiles no query of the tile needs masked
+  int kt = 0;
+  for (; kt < n_full; ++kt) tile(std::false_type{}, kt);
+  for (; kt < n_kt; ++kt) tile(std::true_type{}, kt);
   if (qok) {
     const float fq = p.scale * fast_exp2(-(kap + sg + kv + kk));
     bf16 *de = (bf16 *)p.dq + b * p.dqs_b + (int64_t)my_q * p.dqs_s + 2 * pr * p.dqs_h;
@@ -577,7 +587,13 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
     store_chunk2(smb[0], nxt, tid, q_begin, S, fE, kap);
   }
   __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
+  // One (pair, chunk) step; MASKED applies the key-range and causal masks,
+  // which only the chunks on this workgroup's diagonal (the first KVB / QCH of
+  // each pair under the causal mask) and, in the workgroup holding the last
+  // keys, every chunk need: separate loops, so the others carry no mask
+  // arithmetic and no branch.
+  auto step = [&](auto masked, int it) {
+    constexpr bool MASKED = decltype(masked)::value;
     SmemC &sm = smb[it & 1];
     const int q0 = q_begin + (it % n_ch) * QCH;
     const bool more = it + 1 < n_it;
@@ -609,7 +625,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = sub * 32 + row_of_reg(r, h);
-        const bool dead = row_of_reg(r, h) < lo;
+        const bool dead = MASKED && row_of_reg(r, h) < lo;
         const float ae = fmaf(s_e[r], c, -sm.le[qi]), ao = fmaf(s_o[r], c, -sm.lo[qi]);
         const float pe = fast_exp2(dead ? -__builtin_inff() : ae);  // P_e 2^kappa
         const float po = fast_exp2(dead ? -__builtin_inff() : ao);  // sigma P_o 2^kappa
@@ -631,6 +647,11 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
     }
     if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid, q_begin + ((it + 1) % n_ch) * QCH, S, fE, kap);
     __syncthreads();
+  };
+  const int n_mask = kb + KVB > S ? n_ch : (causal ? min(n_ch, KVB / QCH) : 0);
+  for (int pp = 0, it = 0; pp < ppk; ++pp) {
+    for (int ci = 0; ci < n_mask; ++ci, ++it) step(std::true_type{}, it);
+    for (int ci = n_mask; ci < n_ch; ++ci, ++it) step(std::false_type{}, it);
   }
 
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
