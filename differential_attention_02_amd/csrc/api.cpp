@@ -120,6 +120,8 @@ int diffattn_fwd(const diffattn_fwd_args *a, void *stream) {
   if (!fused && !generic_dims(a->head_dim, a->v_dim))
     return fail(DIFFATTN_ERR_UNSUPPORTED, "(head_dim, v_dim) = (%d, %d) not instantiated", a->head_dim, a->v_dim);
   if (nsave && !fused) return fail(DIFFATTN_ERR_UNSUPPORTED, "training saves need bf16 with head_dim 64, v_dim 128");
+  if (nsave && !(aligned16(a->o_pre) && aligned16(a->a2)))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "training saves o_pre and a2 must be 16-byte aligned");
   if (fused) {
     const void *ptrs[] = {a->q1, a->k1, a->q2, a->k2, a->v, a->out};
     const int64_t *str[] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
@@ -231,6 +233,8 @@ static int check_bwd(const diffattn_bwd_args *a) {
   if (!a->dout) return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "dout must be non-NULL");
   if (!a->lse1 || !a->lse2 || !a->rstd || !a->o_pre || !a->a2)
     return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "backward needs the five forward saves");
+  if (!(aligned16(a->o_pre) && aligned16(a->a2)))
+    return fail(DIFFATTN_ERR_UNSUPPORTED, "forward saves o_pre and a2 must be 16-byte aligned");
   if (!a->dq1 || !a->dk1 || !a->dq2 || !a->dk2 || !a->dv)
     return fail(DIFFATTN_ERR_INVALID_ARGUMENT, "dq1, dk1, dq2, dk2 and dv must be non-NULL");
   if (!strides_ok(a->do_stride, 3) || !strides_ok(a->dq_stride, 3) || !strides_ok(a->dk_stride, 3) ||

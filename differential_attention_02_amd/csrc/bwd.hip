@@ -100,50 +100,80 @@ __host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
 __device__ __forceinline__ float exp2i(float e) { return fast_exp2(e); }  // e integral: exact power of 2
 
 // ---------------------------------------------------------------------------
-// bwd_pre: one wave per (b, h, s) row; lane holds channels 2 lane, 2 lane + 1.
+// Row kernels (bwd_pre, bwd_gconv): 16 lanes per (b, h, s) row, 8 channels per
+// lane (16-byte bf16 and 32-byte float32 accesses), four rows per wave.  Lanes
+// past the last row work on the last row and store nothing (every lane takes
+// part in the wave-wide lambda reduction and the row reductions).
+constexpr int RPB = NT / kRowLanes;  // rows per workgroup
+
+// bwd_pre: g (the gradient reaching the pre-norm output O), row norms, the
+// row's lambda share -g . A2, and the row's largest |Q|, |K|, |V| (their fp16
+// copies are scaled by powers of two chosen from these, vrange.h).
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over [B, H, S]
+  const int part = threadIdx.x & (kRowLanes - 1);
   const int64_t nrows = (int64_t)p.B * p.H * p.S;
-  if (row >= nrows) return;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 4);  // over [B, H, S]
+  const bool ok = row0 < nrows;
+  const int64_t row = ok ? row0 : nrows - 1;
   const int s = row % p.S;
   const int bh = row / p.S;
   const int b = bh / p.H, h = bh % p.H;
-  const int c = 2 * lane;
-  const bf16 *dyp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + h * p.ds_h + c;
-  const bf16 *vp = (const bf16 *)p.v + b * p.vs_b + (int64_t)s * p.vs_s + h * p.vs_h + c;
+  const int c = part * 8;
+  float dy[8], v[8], o[8], a2[8], g[8];
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + h * p.ds_h + c), dy);
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)p.v + b * p.vs_b + (int64_t)s * p.vs_s + h * p.vs_h + c), v);
   const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
-  const float2 o = *(const float2 *)(p.o_pre + srow * DV + c);
-  const float2 a2 = *(const float2 *)(p.a2 + srow * DV + c);
-  const float dy0 = bf2f(dyp[0]), dy1 = bf2f(dyp[1]);
-  const float v0 = bf2f(vp[0]), v1 = bf2f(vp[1]);
-  float g0 = dy0, g1 = dy1;
+  load_f32x8(p.o_pre + srow * DV + c, o);
+  load_f32x8(p.a2 + srow * DV + c, a2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) g[i] = dy[i];
   if (p.norm) {
     const float r = p.rstd[((int64_t)b * p.H + h) * p.S + s];
     const float a = 1.f - p.lambda_init;
-    const float t = wave_sum(dy0 * o.x + dy1 * o.y);
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t = fmaf(dy[i], o[i], t);
+    t = row_sum(t);
     const float k = a * r * r * r * t * (1.f / DV);
-    g0 = a * r * dy0 - k * o.x;
-    g1 = a * r * dy1 - k * o.y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = a * r * dy[i] - k * o[i];
   }
-  const float gn = wave_sum(g0 * g0 + g1 * g1);
-  const float vn = wave_sum(v0 * v0 + v1 * v1);
-  const float ga = wave_sum(g0 * a2.x + g1 * a2.y);
-  // Largest magnitudes of the row's Q1 | Q2 and K1 | K2 (lanes 0..31 the
-  // first, 32..63 the second, two channels each) and V: their fp16 copies
-  // are scaled by powers of two chosen from these (vrange.h).
-  const int qc = 2 * (lane & 31);
-  const bf16 *qp = (const bf16 *)(lane < 32 ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s + h * p.qs_h + qc;
-  const bf16 *kp = (const bf16 *)(lane < 32 ? p.k1 : p.k2) + b * p.ks_b + (int64_t)s * p.ks_s + h * p.ks_h + qc;
-  const float qm = wave_max(fmaxf(fabsf(bf2f(qp[0])), fabsf(bf2f(qp[1]))));
-  const float km = wave_max(fmaxf(fabsf(bf2f(kp[0])), fabsf(bf2f(kp[1]))));
-  const float vm = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  *(float2 *)(w.g + row * DV + c) = make_float2(g0, g1);
-  if (lane == 0) {
-    w.gnorm[row] = sqrtf(gn);
-    w.vnorm[row] = sqrtf(vn);
-    w.dlam_row[row] = -ga;
-    *(f32x4 *)(w.amax + row * 4) = f32x4{qm, km, vm, 0.f};
+  float gn = 0.f, vn = 0.f, ga = 0.f, vm = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gn = fmaf(g[i], g[i], gn);
+    vn = fmaf(v[i], v[i], vn);
+    ga = fmaf(g[i], a2[i], ga);
+    vm = fmaxf(vm, fabsf(v[i]));
+  }
+  // Q1 | Q2 and K1 | K2: lanes 0..7 the first (64 channels), 8..15 the second.
+  const int qc = (part & 7) * 8;
+  float q[8], kk[8];
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)(part < 8 ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s +
+                              h * p.qs_h + qc), q);
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)(part < 8 ? p.k1 : p.k2) + b * p.ks_b + (int64_t)s * p.ks_s +
+                              h * p.ks_h + qc), kk);
+  float qm = 0.f, km = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    qm = fmaxf(qm, fabsf(q[i]));
+    km = fmaxf(km, fabsf(kk[i]));
+  }
+  gn = row_sum(gn);
+  vn = row_sum(vn);
+  ga = row_sum(ga);
+  qm = row_max(qm);
+  km = row_max(km);
+  vm = row_max(vm);
+  if (ok) {
+    *(f32x4 *)(w.g + row * DV + c) = f32x4{g[0], g[1], g[2], g[3]};
+    *(f32x4 *)(w.g + row * DV + c + 4) = f32x4{g[4], g[5], g[6], g[7]};
+    if (part == 0) {
+      w.gnorm[row] = sqrtf(gn);
+      w.vnorm[row] = sqrtf(vn);
+      w.dlam_row[row] = -ga;
+      *(f32x4 *)(w.amax + row * 4) = f32x4{qm, km, vm, 0.f};
+    }
   }
 }
 
@@ -203,35 +233,47 @@ __global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_gconv: one wave per (b, h, s) row: g' = fp16(g 2^sg) and the row terms
+// bwd_gconv: per (b, h, s) row, g' = fp16(g 2^sg) and the row terms
 // E_m = g' . A_m (A2 saved by the forward, A1 = O + lambda A2), stored
 // unscaled.  Taking E from the same fp16 g' the matrix products use makes it
 // equal to sum_j P_m dP' up to float32 rounding, so dS = P (dP - E) stays
 // self-consistent where one key dominates a row and dP - E cancels.
 __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over [B, H, S]
+  const int part = threadIdx.x & (kRowLanes - 1);
   const int64_t nrows = (int64_t)p.B * p.H * p.S;
-  if (row >= nrows) return;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 4);  // over [B, H, S]
+  const bool ok = row0 < nrows;
+  const int64_t row = ok ? row0 : nrows - 1;
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int s = row % p.S;
   const int bh = row / p.S;
   const int b = bh / p.H, h = bh % p.H;
-  const int c = 2 * lane;
+  const int c = part * 8;
   const float sg = w.scales[bh * 8 + 0], f = exp2i(sg);
-  const float2 g = *(const float2 *)(w.g + row * DV + c);
-  const f16x2 gh = {(f16)(g.x * f), (f16)(g.y * f)};
-  *(f16x2 *)(w.gh + row * DV + c) = gh;
+  float g[8], o[8], a2[8];
+  load_f32x8(w.g + row * DV + c, g);
   const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
-  const float2 o = *(const float2 *)(p.o_pre + srow * DV + c);
-  const float2 a2 = *(const float2 *)(p.a2 + srow * DV + c);
-  const float g0 = (float)gh[0], g1 = (float)gh[1];
-  const float e2 = wave_sum(g0 * a2.x + g1 * a2.y);
-  const float e1 = wave_sum(g0 * fmaf(lam, a2.x, o.x) + g1 * fmaf(lam, a2.y, o.y));
-  if (lane == 0) {
-    const float un = exp2i(-sg);
-    w.e1[row] = e1 * un;
-    w.e2[row] = e2 * un;
+  load_f32x8(p.o_pre + srow * DV + c, o);
+  load_f32x8(p.a2 + srow * DV + c, a2);
+  f16x8 gh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gh[i] = (f16)(g[i] * f);
+  float e1 = 0.f, e2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float gi = (float)gh[i];
+    e2 = fmaf(gi, a2[i], e2);
+    e1 = fmaf(gi, fmaf(lam, a2[i], o[i]), e1);
+  }
+  e1 = row_sum(e1);
+  e2 = row_sum(e2);
+  if (ok) {
+    *(f16x8 *)(w.gh + row * DV + c) = gh;
+    if (part == 0) {
+      const float un = exp2i(-sg);
+      w.e1[row] = e1 * un;
+      w.e2[row] = e2 * un;
+    }
   }
 }
 
@@ -763,9 +805,9 @@ size_t bwd_workspace_bytes(int B, int S, int H, int d, int dv) {
 hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
   Ws w = carve(p.workspace, p.B, p.S, p.H);
   const int64_t rows = (int64_t)p.B * p.H * p.S;
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.B * p.H), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(bwd_gconv_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_gconv_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);

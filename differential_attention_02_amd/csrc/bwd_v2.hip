@@ -89,42 +89,60 @@ __device__ __forceinline__ float sigmoid_of(const V2BwdParams &p, int b, int s, 
 }
 
 // ---------------------------------------------------------------------------
-// v2b_pre: one wave per (b, pair, s) row; lane holds channels 2 lane, 2 lane + 1.
+// Row kernels (v2b_pre, v2b_gconv): 16 lanes per (b, pair, s) row, 8 channels
+// per lane (16-byte bf16 and 32-byte float32 accesses), four rows per wave.
+constexpr int RPB = NT / kRowLanes;  // rows per workgroup
+
 __global__ __launch_bounds__(NT) void v2b_pre_kernel(V2BwdParams p, Ws2 w) {
-  const int lane = threadIdx.x & 63;
+  const int part = threadIdx.x & (kRowLanes - 1);
   const int P = p.Hq / 2;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over [B, P, S]
-  if (row >= (int64_t)p.B * P * p.S) return;
+  const int64_t row = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 4);  // over [B, P, S]
+  if (row >= (int64_t)p.B * P * p.S) return;  // whole 16-lane groups leave together
   const int s = row % p.S;
   const int bp = row / p.S, b = bp / P, pr = bp % P;
-  const int c = 2 * lane;
-  const bf16 *gp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c;
+  const int c = part * 8;
+  float g[8], ao[8], qe[8], qo[8];
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c), g);
   const int64_t srow = (((int64_t)b * p.S + s) * P + pr) * D;
-  const float2 ao = *(const float2 *)(p.a_odd + srow + c);
-  const float g0 = bf2f(gp[0]), g1 = bf2f(gp[1]);
-  const float gg = wave_sum(g0 * g0 + g1 * g1);
-  const float ga = wave_sum(g0 * ao.x + g1 * ao.y);
+  load_f32x8(p.a_odd + srow + c, ao);
   // Largest magnitudes of the row's Q_e, Q_o (and, once per KV head, K and V):
   // their fp16 copies are scaled by powers of two chosen from these (vrange.h).
   const bf16 *qp = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + 2 * pr * p.qs_h + c;
-  const float qmx = wave_max(fmaxf(fmaxf(fabsf(bf2f(qp[0])), fabsf(bf2f(qp[1]))),
-                                   fmaxf(fabsf(bf2f(qp[p.qs_h])), fabsf(bf2f(qp[p.qs_h + 1])))));
-  if (lane == 0) {
+  bf16x8_f32(*(const u32x4 *)qp, qe);
+  bf16x8_f32(*(const u32x4 *)(qp + p.qs_h), qo);
+  float gg = 0.f, ga = 0.f, qmx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gg = fmaf(g[i], g[i], gg);
+    ga = fmaf(g[i], ao[i], ga);
+    qmx = fmaxf(qmx, fmaxf(fabsf(qe[i]), fabsf(qo[i])));
+  }
+  gg = row_sum(gg);
+  ga = row_sum(ga);
+  qmx = row_max(qmx);
+  if (part == 0) {
     const float sg = sigmoid_of(p, b, s, pr);
     w.gn[row] = sqrtf(gg);
     w.qm[row] = qmx;
     p.dlam[((int64_t)b * p.S + s) * P + pr] = -sg * (1.f - sg) * ga;
   }
   const int ppk = p.Hq / p.Hkv / 2, j = pr / ppk;
-  if (pr % ppk == 0) {  // wave-uniform
-    const bf16 *vr = (const bf16 *)p.v + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c;
-    const bf16 *kr = (const bf16 *)p.k + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c;
-    const float v0 = bf2f(vr[0]), v1 = bf2f(vr[1]);
-    const float vv = wave_sum(v0 * v0 + v1 * v1);
-    const float vmx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-    const float kmx = wave_max(fmaxf(fabsf(bf2f(kr[0])), fabsf(bf2f(kr[1]))));
+  if (pr % ppk == 0) {  // uniform over the row's 16 lanes
+    float v[8], k[8];
+    bf16x8_f32(*(const u32x4 *)((const bf16 *)p.v + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c), v);
+    bf16x8_f32(*(const u32x4 *)((const bf16 *)p.k + b * p.kvs_b + (int64_t)s * p.kvs_s + j * p.kvs_h + c), k);
+    float vv = 0.f, vmx = 0.f, kmx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vv = fmaf(v[i], v[i], vv);
+      vmx = fmaxf(vmx, fabsf(v[i]));
+      kmx = fmaxf(kmx, fabsf(k[i]));
+    }
+    vv = row_sum(vv);
+    vmx = row_max(vmx);
+    kmx = row_max(kmx);
     const int64_t kr_row = ((int64_t)b * p.Hkv + j) * p.S + s;
-    if (lane == 0) {
+    if (part == 0) {
       w.vn[kr_row] = sqrtf(vv);
       *(float2 *)(w.kvm + kr_row * 2) = make_float2(kmx, vmx);
     }
@@ -192,28 +210,37 @@ __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
 }
 
 // ---------------------------------------------------------------------------
-// v2b_gconv: one wave per (b, pair, s) row: g' = fp16(g 2^sg) and
-// E_e = g' . A_e, E_o = g' . A_o, stored unscaled.
+// v2b_gconv: per (b, pair, s) row, g' = fp16(g 2^sg) and E_e = g' . A_e,
+// E_o = g' . A_o, stored unscaled.
 __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
-  const int lane = threadIdx.x & 63;
+  const int part = threadIdx.x & (kRowLanes - 1);
   const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)p.B * P * p.S) return;
+  const int64_t row = (int64_t)blockIdx.x * RPB + (threadIdx.x >> 4);
+  if (row >= (int64_t)p.B * P * p.S) return;  // whole 16-lane groups leave together
   const int s = row % p.S;
   const int bp = row / p.S, b = bp / P, pr = bp % P;
   const int bj = b * p.Hkv + pr / ppk;
-  const int c = 2 * lane;
+  const int c = part * 8;
   const float sg = w.scales[bj * 8 + 0], f = fast_exp2(sg);
-  const bf16 *gp = (const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c;
-  const f16x2 gh = {(f16)(bf2f(gp[0]) * f), (f16)(bf2f(gp[1]) * f)};
-  *(f16x2 *)(w.gh + row * D + c) = gh;
+  float g[8], ae[8], ao[8];
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c), g);
   const int64_t srow = (((int64_t)b * p.S + s) * P + pr) * D;
-  const float2 ae = *(const float2 *)(p.a_even + srow + c);
-  const float2 ao = *(const float2 *)(p.a_odd + srow + c);
-  const float g0 = (float)gh[0], g1 = (float)gh[1];
-  const float eo = wave_sum(g0 * ao.x + g1 * ao.y);
-  const float ee = wave_sum(g0 * ae.x + g1 * ae.y);
-  if (lane == 0) {
+  load_f32x8(p.a_even + srow + c, ae);
+  load_f32x8(p.a_odd + srow + c, ao);
+  f16x8 gh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gh[i] = (f16)(g[i] * f);
+  *(f16x8 *)(w.gh + row * D + c) = gh;
+  float ee = 0.f, eo = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float gi = (float)gh[i];
+    ee = fmaf(gi, ae[i], ee);
+    eo = fmaf(gi, ao[i], eo);
+  }
+  ee = row_sum(ee);
+  eo = row_sum(eo);
+  if (part == 0) {
     const float un = fast_exp2(-sg);
     w.ee[row] = ee * un;
     w.eo[row] = eo * un;
@@ -681,9 +708,9 @@ hipError_t launch_v2_bwd(const V2BwdParams &p, hipStream_t st) {
   const int P = p.Hq / 2;
   Ws2 w = carve2(p.workspace, p.B, p.S, P, p.Hkv);
   const int64_t rows = (int64_t)p.B * P * p.S;
-  hipLaunchKernelGGL(v2b_pre_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_pre_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(v2b_scales_kernel, dim3(p.B * p.Hkv), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(v2b_gconv_kernel, dim3((rows + 3) / 4), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_gconv_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(v2b_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(v2b_dq_kernel, dim3(n_qt * p.B * P), dim3(NT), 0, st, p, w);

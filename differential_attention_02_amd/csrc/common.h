@@ -76,6 +76,39 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Reductions over aligned groups of 16 lanes (one row of 128 channels at
+// 8 channels per lane).
+constexpr int kRowLanes = 16;
+
+__device__ __forceinline__ float row_sum(float x) {
+  for (int o = kRowLanes / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float row_max(float x) {
+  for (int o = kRowLanes / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Eight bf16 values (one 16-byte load) to float32.
+__device__ __forceinline__ void bf16x8_f32(const u32x4 &r, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(r[i] << 16);
+    f[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+  }
+}
+
+// Eight float32 values from a 16-byte aligned address.
+__device__ __forceinline__ void load_f32x8(const float *p, float *f) {
+  const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = a[i];
+    f[4 + i] = b[i];
+  }
+}
+
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 __device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }  // round to nearest even
 

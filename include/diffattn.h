@@ -76,7 +76,8 @@ extern "C" {
  *   lambda_dim each) when all four are non-NULL, else lambda_fixed.
  *   softmax_scale <= 0 selects 1/sqrt(d).  eps sits inside the RMS root.
  *   lambda_out (optional, device float32[1]) receives the lambda used.
- *   Training saves (all five non-NULL, or all NULL; bf16 fused path only):
+ *   Training saves (all five non-NULL, or all NULL; bf16 fused path only;
+ *   o_pre and a2 16-byte aligned, else DIFFATTN_ERR_UNSUPPORTED):
  *     lse1, lse2, rstd: float32 [B, H, S] contiguous - natural-log partition
  *       function of each map's scaled scores, and the RMSNorm reciprocal
  *       root (1 when norm = 0);
@@ -117,7 +118,7 @@ typedef struct diffattn_fwd_args {
  * Backward arguments: gradients of L = <dout, out> for a forward with the same
  * inputs and flags (bf16, d = 64, dv = 128, causal or not).
  *   Needs the five training saves of that forward (lse1, lse2, rstd, o_pre,
- *   a2).
+ *   a2), o_pre and a2 16-byte aligned (else DIFFATTN_ERR_UNSUPPORTED).
  *   dout has strides do_stride; outputs dq1, dq2 (strides dq_stride), dk1,
  *   dk2 (dk_stride), dv (dv_stride) in the activation dtype.
  *   With the four lambda vectors given, dlq1, dlk1, dlq2, dlk2 (device
