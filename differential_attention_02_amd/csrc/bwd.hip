@@ -16,7 +16,7 @@
 //   dlq2 = -dlam e^be lk2, dlk2 = -dlam e^be lq2.
 //
 // Kernels, in launch order:
-//   bwd_pre    one wave per query row: g (float32), |g|, |V_row| and the row's
+//   bwd_pre    per query row: g (float32), |g|, |V_row| and the row's
 //              share -g.A2 of dL/dlambda from the forward's float32 A2
 //              (the sum over rows cancels by orders of magnitude, so it takes
 //              float32 g rather than the fp16 copy the matrix products use);
@@ -25,12 +25,12 @@
 //              the bound |dS| <= max(1,|lambda|) (|g| |V| + |E|) <= 2 max(1,|lambda|)
 //              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|), and the
 //              (batch, head) sum of the rows' dL/dlambda shares (fixed order);
-//   bwd_gconv  one wave per row: g' = fp16(g 2^sg) and E_m = g' . A_m (A2
-//              saved by the forward, A1 = O + lambda A2): from the same fp16
-//              g' the matrix products use, E equals sum_j P_m dP' up to
-//              float32 rounding, so dS = P (dP - E) stays self-consistent
-//              where one key dominates a row and dP - E cancels;
-//   bwd_qconv  Q1 | Q2 rows to fp16 for the key-outer kernel's staging;
+//   bwd_gconv  per row: g' = fp16(g 2^sg) and E_m = g' . A_m (A2 saved by
+//              the forward, A1 = O + lambda A2): from the same fp16 g' the
+//              matrix products use, E equals sum_j P_m dP' up to float32
+//              rounding, so dS = P (dP - E) stays self-consistent where one
+//              key dominates a row and dP - E cancels; also the row's Q1 | Q2
+//              in fp16 for the key-outer kernel's staging;
 //   bwd_dq     query-outer (the forward's layout): each workgroup owns 128
 //              queries and streams 64-key tiles: dS and dQ1, dQ2 accumulated
 //              in registers;
@@ -178,15 +178,37 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_scales: one workgroup per (b, h).
-__global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
-  __shared__ float red[6][NT / 64];
+// bwd_scales: one workgroup of NTS threads per (b, h) (many loads in flight:
+// the pass is latency-bound).
+constexpr int NTS = 1024, NWS = NTS / 64;
+
+// Fixed-order pairwise sum / maximum of the NWS per-wave values.
+__device__ __forceinline__ float tree_sum(const float *v) {
+  float t[NWS];
+#pragma unroll
+  for (int i = 0; i < NWS; ++i) t[i] = v[i];
+#pragma unroll
+  for (int n = NWS / 2; n > 0; n >>= 1)
+#pragma unroll
+    for (int i = 0; i < n; ++i) t[i] = t[i] + t[i + n];
+  return t[0];
+}
+
+__device__ __forceinline__ float tree_max(const float *v) {
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < NWS; ++i) m = fmaxf(m, v[i]);
+  return m;
+}
+
+__global__ __launch_bounds__(NTS) void bwd_scales_kernel(BwdParams p, Ws w) {
+  __shared__ float red[6][NWS];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int64_t base = (int64_t)bh * p.S;
   float gm = 0.f, vm = 0.f, dl = 0.f;
   f32x4 am = {0.f, 0.f, 0.f, 0.f};
-  for (int s = tid; s < p.S; s += NT) {
+  for (int s = tid; s < p.S; s += NTS) {
     gm = fmaxf(gm, w.gnorm[base + s]);
     vm = fmaxf(vm, w.vnorm[base + s]);
     dl += w.dlam_row[base + s];
@@ -209,14 +231,12 @@ __global__ __launch_bounds__(NT) void bwd_scales_kernel(BwdParams p, Ws w) {
   }
   __syncthreads();
   if (tid == 0) {
-    gm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    vm = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    gm = tree_max(red[0]);
+    vm = tree_max(red[1]);
     float ks[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      ks[i] = (float)v_shift_of_max(__float_as_uint(fmaxf(fmaxf(red[3 + i][0], red[3 + i][1]),
-                                                          fmaxf(red[3 + i][2], red[3 + i][3]))) >> 16);
-    w.dlam_bh[bh] = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
+    for (int i = 0; i < 3; ++i) ks[i] = (float)v_shift_of_max(__float_as_uint(tree_max(red[3 + i])) >> 16);
+    w.dlam_bh[bh] = tree_sum(red[2]);
     const float al = fmaxf(1.f, fabsf(lam));
     const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
     const float x = 2.f * al * gm * vm;  // bound on |dS| before scaling by 2^sg
@@ -269,28 +289,19 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
   e2 = row_sum(e2);
   if (ok) {
     *(f16x8 *)(w.gh + row * DV + c) = gh;
+    // The row's Q1 | Q2 to fp16 times 2^kq (exact) for the key-outer kernel's
+    // staging: lanes 0..7 Q1, 8..15 Q2, eight channels each.
+    const int qc = (part & 7) * 8;
+    const u32x4 raw = *(const u32x4 *)((const bf16 *)(part < 8 ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s +
+                                       h * p.qs_h + qc);
+    const VScale sq((int)w.scales[bh * 8 + 3]);
+    *(u32x4 *)(w.qh + row * (2 * D) + c) = sq.on ? bf16x8_to_f16x8<true>(raw, sq) : bf16x8_to_f16x8<false>(raw, sq);
     if (part == 0) {
       const float un = exp2i(-sg);
       w.e1[row] = e1 * un;
       w.e2[row] = e2 * un;
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// bwd_qconv: Q1 | Q2 rows to fp16 times 2^kq (exact), 8 channels per thread,
-// into [B, H, S, 2 D] for the key-outer kernel's staging.
-__global__ __launch_bounds__(NT) void bwd_qconv_kernel(BwdParams p, Ws w) {
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8
-  const int64_t n = (int64_t)p.B * p.H * p.S * (2 * D / 8);
-  if (i >= n) return;
-  const int64_t row = i / (2 * D / 8);
-  const int ch = (int)(i % (2 * D / 8)) * 8;
-  const int s = row % p.S, bh = row / p.S, b = bh / p.H, hd = bh % p.H;
-  const bf16 *q = (const bf16 *)(ch < D ? p.q1 : p.q2) + b * p.qs_b + (int64_t)s * p.qs_s + hd * p.qs_h + (ch & (D - 1));
-  const u32x4 raw = *(const u32x4 *)q;
-  const VScale sq((int)w.scales[bh * 8 + 3]);
-  *(u32x4 *)(w.qh + i * 8) = sq.on ? bf16x8_to_f16x8<true>(raw, sq) : bf16x8_to_f16x8<false>(raw, sq);
 }
 
 // Permutation of rows 0..31 used for the A operand of score-like products so
@@ -806,9 +817,8 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
   Ws w = carve(p.workspace, p.B, p.S, p.H);
   const int64_t rows = (int64_t)p.B * p.H * p.S;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.B * p.H), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_scales_kernel, dim3(p.B * p.H), dim3(NTS), 0, st, p, w);
   hipLaunchKernelGGL(bwd_gconv_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(bwd_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.S + KVB - 1) / KVB * p.B * p.H), dim3(NT), 0, st, p, w);

@@ -13,7 +13,7 @@
 //   dQ_t = s dS_t K,  dK = s sum_t dS_t^T Q_t (over every head reading j)
 //
 // Kernels, in launch order:
-//   v2b_pre    one wave per (batch, pair, token) row: |g| and dlam from the
+//   v2b_pre    per (batch, pair, token) row: |g| and dlam from the
 //              float32 g and the saved A_o (and |V| of the row's key when the
 //              pair is the first on its KV head);
 //   v2b_scales one workgroup per (batch, KV head): power-of-two scales that
@@ -21,11 +21,11 @@
 //              of the pairs on the head, dS by the bound
 //              |dS| <= 2 max|g| max|V| (|A_t| <= max|V|), W = P_e - sigma P_o
 //              (|W| <= 1) by a fixed 2^12;
-//   v2b_gconv  one wave per row: g' = fp16(g 2^sg) and E_t = g' . A_t from
-//              that same fp16 g' and A_t accumulated with head t's own
-//              weights (so dS = P (dP - E) stays self-consistent where one key
-//              dominates a row and dP - E cancels);
-//   v2b_qconv  Q_e | Q_o rows to fp16 for the key-outer kernel's staging;
+//   v2b_gconv  per row: g' = fp16(g 2^sg) and E_t = g' . A_t from that same
+//              fp16 g' and A_t accumulated with head t's own weights (so
+//              dS = P (dP - E) stays self-consistent where one key dominates a
+//              row and dP - E cancels); also Q_e | Q_o in fp16 for the
+//              key-outer kernel's staging;
 //   v2b_dq     query-outer: 128 queries of one (batch, pair) per workgroup,
 //              64-key tiles; dS and dQ of both heads in registers;
 //   v2b_dkdv   key-outer: 128 keys of one (batch, KV head) per workgroup,
@@ -150,16 +150,19 @@ __global__ __launch_bounds__(NT) void v2b_pre_kernel(V2BwdParams p, Ws2 w) {
 }
 
 // ---------------------------------------------------------------------------
-// v2b_scales: one workgroup per (b, KV head j).
-__global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
-  __shared__ float red[5][NT / 64];
+// v2b_scales: one workgroup of NTS threads per (b, KV head j) (many loads in
+// flight: the pass is latency-bound).
+constexpr int NTS = 1024, NWS = NTS / 64;
+
+__global__ __launch_bounds__(NTS) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
+  __shared__ float red[5][NWS];
   const int bj = blockIdx.x, b = bj / p.Hkv, j = bj % p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;  // pairs per KV head
   float gm = 0.f, qm = 0.f;
   for (int pp = 0; pp < ppk; ++pp) {
     const int64_t base = ((int64_t)b * P + j * ppk + pp) * p.S;
-    for (int s = tid; s < p.S; s += NT) {
+    for (int s = tid; s < p.S; s += NTS) {
       gm = fmaxf(gm, w.gn[base + s]);
       qm = fmaxf(qm, w.qm[base + s]);
     }
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
   float vm = 0.f, km = 0.f, vx = 0.f;
   const float *vn = w.vn + (int64_t)bj * p.S;
   const float *kvm = w.kvm + (int64_t)bj * p.S * 2;
-  for (int s = tid; s < p.S; s += NT) {
+  for (int s = tid; s < p.S; s += NTS) {
     vm = fmaxf(vm, vn[s]);
     km = fmaxf(km, kvm[2 * s]);
     vx = fmaxf(vx, kvm[2 * s + 1]);
@@ -190,7 +193,11 @@ __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
   if (tid == 0) {
     float mx[5];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) mx[i] = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
+    for (int i = 0; i < 5; ++i) {
+      mx[i] = red[i][0];
+#pragma unroll
+      for (int k = 1; k < NWS; ++k) mx[i] = fmaxf(mx[i], red[i][k]);
+    }
     gm = mx[0];
     vm = mx[1];
     const float kq = (float)v_shift_of_max(__float_as_uint(mx[2]) >> 16);
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(NT) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
 
 // ---------------------------------------------------------------------------
 // v2b_gconv: per (b, pair, s) row, g' = fp16(g 2^sg) and E_e = g' . A_e,
-// E_o = g' . A_o, stored unscaled.
+// E_o = g' . A_o, stored unscaled; also the row's Q_e | Q_o in fp16.
 __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
   const int part = threadIdx.x & (kRowLanes - 1);
   const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
@@ -240,29 +247,17 @@ __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
   }
   ee = row_sum(ee);
   eo = row_sum(eo);
+  // The row's Q_e | Q_o to fp16 times 2^kq for the key-outer kernel's
+  // staging ([B, P, S, 2 D]), eight channels of each head per lane.
+  const VScale sq((int)w.scales[bj * 8 + 3]);
+  const bf16 *qp = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + 2 * pr * p.qs_h + c;
+  *(u32x4 *)(w.qh + row * (2 * D) + c) = bf16x8_to_f16x8_scaled(*(const u32x4 *)qp, sq);
+  *(u32x4 *)(w.qh + row * (2 * D) + D + c) = bf16x8_to_f16x8_scaled(*(const u32x4 *)(qp + p.qs_h), sq);
   if (part == 0) {
     const float un = fast_exp2(-sg);
     w.ee[row] = ee * un;
     w.eo[row] = eo * un;
   }
-}
-
-// ---------------------------------------------------------------------------
-// v2b_qconv: Q_e | Q_o rows to fp16 times 2^kq, 8 channels per thread, into
-// [B, P, S, 2 D].
-__global__ __launch_bounds__(NT) void v2b_qconv_kernel(V2BwdParams p, Ws2 w) {
-  const int P = p.Hq / 2;
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;  // chunk of 8 channels
-  const int64_t n = (int64_t)p.B * P * p.S * (2 * D / 8);
-  if (i >= n) return;
-  const int64_t row = i / (2 * D / 8);
-  const int ch = (int)(i % (2 * D / 8)) * 8;
-  const int s = row % p.S, bp = row / p.S, b = bp / P, pr = bp % P;
-  const int t = 2 * pr + (ch >= D);
-  const bf16 *q = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + t * p.qs_h + (ch & (D - 1));
-  const u32x4 raw = *(const u32x4 *)q;
-  const VScale sq((int)w.scales[(b * p.Hkv + pr / (p.Hq / p.Hkv / 2)) * 8 + 3]);
-  *(u32x4 *)(w.qh + i * 8) = bf16x8_to_f16x8_scaled(raw, sq);
 }
 
 // Permutation of rows 0..31 used for the A operand of score-like products so
@@ -709,9 +704,8 @@ hipError_t launch_v2_bwd(const V2BwdParams &p, hipStream_t st) {
   Ws2 w = carve2(p.workspace, p.B, p.S, P, p.Hkv);
   const int64_t rows = (int64_t)p.B * P * p.S;
   hipLaunchKernelGGL(v2b_pre_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(v2b_scales_kernel, dim3(p.B * p.Hkv), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(v2b_scales_kernel, dim3(p.B * p.Hkv), dim3(NTS), 0, st, p, w);
   hipLaunchKernelGGL(v2b_gconv_kernel, dim3((rows + RPB - 1) / RPB), dim3(NT), 0, st, p, w);
-  hipLaunchKernelGGL(v2b_qconv_kernel, dim3((rows * (2 * D / 8) + NT - 1) / NT), dim3(NT), 0, st, p, w);
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(v2b_dq_kernel, dim3(n_qt * p.B * P), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(v2b_dkdv_kernel, dim3((p.S + KVB - 1) / KVB * p.B * p.Hkv), dim3(NT), 0, st, p, w);
