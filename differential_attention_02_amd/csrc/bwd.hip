@@ -16,21 +16,23 @@
 //   dlq2 = -dlam e^be lk2, dlk2 = -dlam e^be lq2.
 //
 // Kernels, in launch order:
-//   bwd_pre    per query row: g (float32), |g|, |V_row| and the row's
-//              share -g.A2 of dL/dlambda from the forward's float32 A2
-//              (the sum over rows cancels by orders of magnitude, so it takes
-//              float32 g rather than the fp16 copy the matrix products use);
+//   bwd_pre    per query row: |g|, |V_row| and the row's share -g.A2 of
+//              dL/dlambda from float32 g (formed from dY, the saved O and
+//              rstd; never stored) and the forward's float32 A2 (the sum over
+//              rows cancels by orders of magnitude, so it takes float32 g
+//              rather than the fp16 copy the matrix products use);
 //   bwd_scales one workgroup per (batch, head): power-of-two scales that keep
 //              the fp16 operands below 2^13 (g by its largest row norm; dS by
 //              the bound |dS| <= max(1,|lambda|) (|g| |V| + |E|) <= 2 max(1,|lambda|)
 //              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|), and the
 //              (batch, head) sum of the rows' dL/dlambda shares (fixed order);
-//   bwd_gconv  per row: g' = fp16(g 2^sg) and E_m = g' . A_m (A2 saved by
-//              the forward, A1 = O + lambda A2): from the same fp16 g' the
-//              matrix products use, E equals sum_j P_m dP' up to float32
-//              rounding, so dS = P (dP - E) stays self-consistent where one
-//              key dominates a row and dP - E cancels; also the row's Q1 | Q2
-//              in fp16 for the key-outer kernel's staging;
+//   bwd_gconv  per row: g formed again as in bwd_pre, g' = fp16(g 2^sg) and
+//              E_m = g' . A_m (A2 saved by the forward, A1 = O + lambda A2):
+//              from the same fp16 g' the matrix products use, E equals
+//              sum_j P_m dP' up to float32 rounding, so dS = P (dP - E) stays
+//              self-consistent where one key dominates a row and dP - E
+//              cancels; also the row's Q1 | Q2 in fp16 for the key-outer
+//              kernel's staging;
 //   bwd_dq     query-outer (the forward's layout): each workgroup owns 128
 //              queries and streams 64-key tiles: dS and dQ1, dQ2 accumulated
 //              in registers;
@@ -61,7 +63,6 @@ constexpr int QST = D + 8;    // LDS row stride (fp16) of Q / K tiles
 constexpr int GST = DV + 32;  // LDS row stride (fp16) of g / V tiles (tr16-friendly)
 
 struct Ws {
-  float *g;        // [B, H, S, DV] float32
   f16 *gh;         // [B, H, S, DV] fp16, g * 2^sg
   f16 *qh;         // [B, H, S, 2 D] fp16: Q1 (channels 0..63) and Q2 (64..127)
   float *e1, *e2;  // [B, H, S]  E_m = sum_j P_m dP (unscaled)
@@ -77,7 +78,6 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
   char *p = static_cast<char *>(base);
   const size_t rows = (size_t)B * H * S;
   Ws w;
-  w.g = (float *)p; p += align256(rows * DV * 4);
   w.gh = (f16 *)p; p += align256(rows * DV * 2);
   w.qh = (f16 *)p; p += align256(rows * 2 * D * 2);
   w.e1 = (float *)p; p += align256(rows * 4);
@@ -93,7 +93,7 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
 
 __host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
   const size_t rows = (size_t)B * H * S;
-  return align256(rows * DV * 4) + align256(rows * DV * 2) + align256(rows * 2 * D * 2) + 5 * align256(rows * 4) +
+  return align256(rows * DV * 2) + align256(rows * 2 * D * 2) + 5 * align256(rows * 4) +
          align256(rows * 16) + align256((size_t)B * H * 32) + align256((size_t)B * H * 4);
 }
 
@@ -106,9 +106,30 @@ __device__ __forceinline__ float exp2i(float e) { return fast_exp2(e); }  // e i
 // part in the wave-wide lambda reduction and the row reductions).
 constexpr int RPB = NT / kRowLanes;  // rows per workgroup
 
-// bwd_pre: g (the gradient reaching the pre-norm output O), row norms, the
-// row's lambda share -g . A2, and the row's largest |Q|, |K|, |V| (their fp16
-// copies are scaled by powers of two chosen from these, vrange.h).
+// g = dL/dO for one row's eight channels (the RMSNorm backward when the norm
+// is on): g = a r dy - a r^3 o (sum_c dy o) / dv.  bwd_pre and bwd_gconv both
+// form it from dy, the saved O and rstd with this code (explicit fma, fixed
+// reduction order), so the two get the same g and it is never stored.
+__device__ __forceinline__ void row_grad(const BwdParams &p, int b, int h, int s, const float *dy, const float *o,
+                                         float *g) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) g[i] = dy[i];
+  if (p.norm) {
+    const float r = p.rstd[((int64_t)b * p.H + h) * p.S + s];
+    const float ar = (1.f - p.lambda_init) * r;
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t = fmaf(dy[i], o[i], t);
+    t = row_sum(t);
+    const float k = ar * r * r * t * (1.f / DV);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = fmaf(-k, o[i], ar * dy[i]);
+  }
+}
+
+// bwd_pre: row norms of g (the gradient reaching the pre-norm output O) and
+// V, the row's lambda share -g . A2, and the row's largest |Q|, |K|, |V|
+// (their fp16 copies are scaled by powers of two chosen from these, vrange.h).
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   const int part = threadIdx.x & (kRowLanes - 1);
   const int64_t nrows = (int64_t)p.B * p.H * p.S;
@@ -125,19 +146,7 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
   load_f32x8(p.o_pre + srow * DV + c, o);
   load_f32x8(p.a2 + srow * DV + c, a2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) g[i] = dy[i];
-  if (p.norm) {
-    const float r = p.rstd[((int64_t)b * p.H + h) * p.S + s];
-    const float a = 1.f - p.lambda_init;
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t = fmaf(dy[i], o[i], t);
-    t = row_sum(t);
-    const float k = a * r * r * r * t * (1.f / DV);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) g[i] = a * r * dy[i] - k * o[i];
-  }
+  row_grad(p, b, h, s, dy, o, g);
   float gn = 0.f, vn = 0.f, ga = 0.f, vm = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -166,8 +175,6 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   km = row_max(km);
   vm = row_max(vm);
   if (ok) {
-    *(f32x4 *)(w.g + row * DV + c) = f32x4{g[0], g[1], g[2], g[3]};
-    *(f32x4 *)(w.g + row * DV + c + 4) = f32x4{g[4], g[5], g[6], g[7]};
     if (part == 0) {
       w.gnorm[row] = sqrtf(gn);
       w.vnorm[row] = sqrtf(vn);
@@ -270,11 +277,12 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
   const int b = bh / p.H, h = bh % p.H;
   const int c = part * 8;
   const float sg = w.scales[bh * 8 + 0], f = exp2i(sg);
-  float g[8], o[8], a2[8];
-  load_f32x8(w.g + row * DV + c, g);
+  float dy[8], g[8], o[8], a2[8];
+  bf16x8_f32(*(const u32x4 *)((const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + h * p.ds_h + c), dy);
   const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
   load_f32x8(p.o_pre + srow * DV + c, o);
   load_f32x8(p.a2 + srow * DV + c, a2);
+  row_grad(p, b, h, s, dy, o, g);
   f16x8 gh;
 #pragma unroll
   for (int i = 0; i < 8; ++i) gh[i] = (f16)(g[i] * f);
