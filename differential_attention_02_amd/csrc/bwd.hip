@@ -38,8 +38,10 @@
 //              in registers;
 //   bwd_dkdv   KV-outer: each workgroup owns 128 keys (4 waves x 32) and
 //              streams 64-query chunks: recomputes P1, P2 and dP, accumulates
-//              dV, dK1, dK2 in registers.  Recomputing rather than
-//              accumulating dQ with atomics keeps every result deterministic;
+//              dV, dK1, dK2 in registers; past the diagonal, one sub-chunk's
+//              elementwise work runs under the matrix products of its
+//              neighbours.  Recomputing rather than accumulating dQ with
+//              atomics keeps every result deterministic;
 //   bwd_lambda one workgroup: dL/dlambda = sum of the row shares in a fixed
 //              order, then the chain rule into the four lambda vectors.
 // Matrix-core operands are fp16 with float32 accumulation: bf16 rounding of g,
@@ -48,6 +50,7 @@
 // their largest magnitudes (bwd_pre, bwd_scales; vrange.h), so any finite bf16
 // inputs convert without saturating or losing precision, and every result is
 // unscaled exactly.
+#include <cstddef>
 #include <type_traits>
 
 #include "common.h"
@@ -347,7 +350,10 @@ __device__ __forceinline__ f16x8 tr_operand(const f16 *tile, int stride, int r0,
 
 // ---------------------------------------------------------------------------
 // bwd_dkdv: KV-outer.  Workgroup = 128 keys of one (b, h); wave w owns keys
-// kb + 32 w + 0..31 (lane l % 32).  Streams 64-query chunks through LDS.
+// kb + 32 w + 0..31 (lane l % 32).  Streams 64-query chunks through three LDS
+// buffers: the masked chunks (the diagonal, or every chunk of the last key
+// block) one 32-query sub-chunk after another, the rest as a software
+// pipeline over sub-chunks (see the loop).
 constexpr int KVB = 128, QCH = 64;
 
 struct SmemA {
@@ -420,6 +426,50 @@ __device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int t
   }
 }
 
+// Half of a chunk's staging (part 0: the fp16 Q1 | Q2 rows and the row
+// statistics; part 1: the fp16 g' rows), for the pipelined loop, which stages
+// the next chunk over two steps so that only half of it is ever in registers.
+struct HalfRegs {
+  u32x4 v[4];
+  float lse1, lse2, e1, e2;
+};
+
+__device__ __forceinline__ void load_half(const BwdParams &p, const Ws &w, int64_t statb, int q0, int S, int tid,
+                                          int part, HalfRegs &r) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
+    const bool ok = q < S;
+    const f16 *src = part == 0 ? w.qh + (statb + q) * (2 * D) + col : w.gh + (statb + q) * DV + col;
+    r.v[k] = ok ? *(const u32x4 *)src : u32x4{0, 0, 0, 0};
+  }
+  if (part == 0 && tid < QCH) {
+    const int64_t q = statb + min(q0 + tid, S - 1);
+    r.lse1 = p.lse1[q];
+    r.lse2 = p.lse2[q];
+    r.e1 = w.e1[q];
+    r.e2 = w.e2[q];
+  }
+}
+
+__device__ __forceinline__ void store_half(SmemA &sm, const HalfRegs &r, int tid, int q0, int S, int part,
+                                           const RowFold &f) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8;
+    f16 *dst = part == 1 ? sm.g + row * GST + col
+                         : (col < D ? sm.q1 + row * QST + col : sm.q2 + row * QST + (col - D));
+    *(u32x4 *)dst = r.v[k];
+  }
+  if (part == 0 && tid < QCH) {
+    const bool ok = q0 + tid < S;
+    sm.lse1[tid] = ok ? fmaf(r.lse1, kLog2e, -f.kap) : __builtin_inff();
+    sm.lse2[tid] = ok ? fmaf(r.lse2, kLog2e, -(f.kap + f.l2lam)) : __builtin_inff();
+    sm.e1[tid] = ok ? r.e1 * f.fE : 0.f;
+    sm.e2[tid] = ok ? -f.sig * r.e2 * f.fE : 0.f;
+  }
+}
+
 // Elementwise part of one 32 x 32 block of the key-outer kernel (lane = key,
 // registers = queries qb + row_of_reg(r, h)): the merged dV weight
 // (P1 - lambda P2) 2^omega and dS_m 2^kappa for both maps.  Query qb + o is
@@ -446,7 +496,7 @@ __device__ __forceinline__ void dkdv_elem(const SmemA &sm, const f32x16 &s1, con
 }
 
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
-  __shared__ SmemA smb[2];
+  __shared__ SmemA smb[3];
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
@@ -479,6 +529,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) vf[kc] = ok ? to_f16x8(*(const u32x4 *)(vv + kc * 16), scv) : f16x8{};
   }
+  // These only feed matrix instructions, which read AGPRs as well: keep them
+  // there (the vector registers are the scarce side of this kernel).
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) asm volatile("" : "+a"(kf1[kc]), "+a"(kf2[kc]));
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) asm volatile("" : "+a"(vf[kc]));
 
   f32x16 dv[4], dk1[2], dk2[2];
 #pragma unroll
@@ -507,7 +563,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
   // no branch.
   auto chunk = [&](auto masked, int q0, int it) {
     constexpr bool MASKED = decltype(masked)::value;
-    SmemA &sm = smb[it & 1];
+    SmemA &sm = smb[it % 3];
     const bool more = q0 + QCH < S;
     if (more) load_chunk(p, w, statb, q0 + QCH, S, tid, nxt);
 #pragma unroll
@@ -543,14 +599,188 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
         }
       }
     }
-    if (more) store_chunk(smb[(it + 1) & 1], nxt, tid, q0 + QCH, S, fold);
+    if (more) store_chunk(smb[(it + 1) % 3], nxt, tid, q0 + QCH, S, fold);
     __syncthreads();
   };
   const int n_ch = q_begin < S ? (S - q_begin + QCH - 1) / QCH : 0;
   const int n_mask = kb + KVB > S ? n_ch : (p.causal ? min(n_ch, KVB / QCH) : 0);
-  int it = 0;
-  for (; it < n_mask; ++it) chunk(std::true_type{}, q_begin + it * QCH, it);
-  for (; it < n_ch; ++it) chunk(std::false_type{}, q_begin + it * QCH, it);
+  for (int it = 0; it < n_mask; ++it) chunk(std::true_type{}, q_begin + it * QCH, it);
+
+  // The unmasked chunks run as a software pipeline over their 32-query
+  // sub-chunks.  Step j: the score products of sub-chunk j; its dP products
+  // interleaved with the exponentials (vector ALU); then the dV, dK products
+  // of sub-chunk j - 1 interleaved with the rest of j's elementwise part.
+  // One matrix instruction, then a share of the vector work, in a fixed order:
+  // the single wave on each SIMD issues in order, so that order is what
+  // overlaps the two units.  LDS operands are read two instructions ahead,
+  // from per-step base addresses with the rest in the instructions' offsets.
+  // Chunk n_mask + k (sub-chunks 2k, 2k + 1) is in buffer (n_mask + k) % 3
+  // from the end of step 2k - 1 (the second half of its staging, barrier)
+  // until step 2k + 2 last reads it.
+  const int J = 2 * (n_ch - n_mask);
+  if (J > 0) {
+    typedef DA_LDS const char lchar;
+    const int hq = 8 * h, jj = lane & 15, half16 = (lane >> 4) & 1;
+    // Per-lane byte offsets: row-major operand reads (A), transpose reads (C),
+    // statistics.
+    const uint32_t laQ = (prow * QST + hq) * 2, laG = (prow * GST + hq) * 2;
+    const uint32_t lcQ = ((hq + (jj >> 2)) * QST + 16 * half16 + 4 * (jj & 3)) * 2;
+    const uint32_t lcG = ((hq + (jj >> 2)) * GST + 16 * half16 + 4 * (jj & 3)) * 2;
+    const uint32_t lst = hq * 4;
+    constexpr uint32_t OQ1 = offsetof(SmemA, q1), OQ2 = offsetof(SmemA, q2), OG = offsetof(SmemA, g);
+    constexpr uint32_t OL1 = offsetof(SmemA, lse1), OL2 = offsetof(SmemA, lse2), OE1 = offsetof(SmemA, e1),
+                       OE2 = offsetof(SmemA, e2);
+    // Base address of buffer `buf` plus a lane offset, opaque to the compiler
+    // so that it keeps the constant parts in the instructions' offsets.
+    auto lptr = [&](int buf, uint32_t lane_off) -> lchar * {
+      lchar *q = (lchar *)(smb + buf) + lane_off;
+      asm volatile("" : "+v"(q));
+      return q;
+    };
+    auto tr8 = [&](lchar *q, uint32_t off, int stride) -> f16x8 {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(q + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(q + off + 8 * stride));
+      const f16x4 a = __builtin_bit_cast(f16x4, lo), b = __builtin_bit_cast(f16x4, hi);
+      return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    };
+    struct Ops {
+      f16x8 w[2], b1[2], b2[2];
+    };
+    Ops po[2];
+    // Operand i (0..15) of the dV/dK products of sub-chunk sub: i = 8 kc2 + k;
+    // k < 4: g^T columns 32 k (dV), 4, 5: Q1^T (dK1), 6, 7: Q2^T (dK2).
+    auto fetch_c = [&](lchar *pq, lchar *pg, int sub, int i) -> f16x8 {
+      const int kc2 = i >> 3, k = i & 7, r0 = sub * 32 + kc2 * 16;
+      if (k < 4) return tr8(pg, OG + (r0 * GST + k * 32) * 2, GST);
+      if (k < 6) return tr8(pq, OQ1 + (r0 * QST + (k - 4) * 32) * 2, QST);
+      return tr8(pq, OQ2 + (r0 * QST + (k - 6) * 32) * 2, QST);
+    };
+    auto mfma_c = [&](int i, const f16x8 &op, const Ops &o) {
+      const int kc2 = i >> 3, k = i & 7;
+      if (k < 4) dv[k] = mfma32(op, o.w[kc2], dv[k]);
+      else if (k < 6) dk1[k - 4] = mfma32(op, o.b1[kc2], dk1[k - 4]);
+      else dk2[k - 6] = mfma32(op, o.b2[kc2], dk2[k - 6]);
+    };
+
+    // Staging registers, one per half: each half is loaded right after the
+    // previous chunk's same half was stored (two steps before its own store).
+    HalfRegs hreg[2];
+    if (n_mask + 1 < n_ch) {
+      load_half(p, w, statb, q_begin + (n_mask + 1) * QCH, S, tid, 0, hreg[0]);
+      load_half(p, w, statb, q_begin + (n_mask + 1) * QCH, S, tid, 1, hreg[1]);
+    }
+    auto step = [&](auto has_c, auto parity, int j, const Ops &pops, Ops &nops) {
+      constexpr bool HC = decltype(has_c)::value;
+      constexpr int SUB = decltype(parity)::value;  // j % 2
+      constexpr int SUBC = 1 - SUB;                 // (j - 1) % 2
+      const int cb = n_mask + (j >> 1);
+      const int bb = cb % 3;
+      lchar *pAq = lptr(bb, laQ), *pAg = lptr(bb, laG), *pS = lptr(bb, lst);
+      lchar *pCq = nullptr, *pCg = nullptr;
+      if constexpr (HC) {
+        const int bc = (n_mask + ((j - 1) >> 1)) % 3;
+        pCq = lptr(bc, lcQ);
+        pCg = lptr(bc, lcG);
+      }
+      // Staging: the even step stores part 0 of chunk cb + 1, the odd step
+      // part 1 (then a barrier); each then loads the same part of chunk cb + 2.
+      f32x4 st[4][4];  // statistics of four rows per group: lse1', lse2', E1', E2'
+      auto fetch_st = [&](int g) {
+        const uint32_t rb = (SUB * 32 + ((g & 2) << 3) + (g & 1) * 4) * 4;
+        st[g][0] = *(const DA_LDS f32x4 *)(pS + OL1 + rb);
+        st[g][1] = *(const DA_LDS f32x4 *)(pS + OL2 + rb);
+        st[g][2] = *(const DA_LDS f32x4 *)(pS + OE1 + rb);
+        st[g][3] = *(const DA_LDS f32x4 *)(pS + OE2 + rb);
+      };
+      // Operand i of the score (i < 8: Q1 even, Q2 odd) and dP (i >= 8) products.
+      auto fa = [&](int i) -> f16x8 {
+        if (i < 8) return *(const DA_LDS f16x8 *)(pAq + ((i & 1) ? OQ2 : OQ1) + (SUB * 32 * QST + (i >> 1) * 16) * 2);
+        return *(const DA_LDS f16x8 *)(pAg + OG + (SUB * 32 * GST + (i - 8) * 16) * 2);
+      };
+      f16x8 oa[16], oc[16];
+      oa[0] = fa(0);
+      oa[1] = fa(1);
+      fetch_st(0);
+      fetch_st(1);
+      f32x16 s1 = {}, s2 = {}, dp = {};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        oa[k + 2] = fa(k + 2);
+        if (k == 4) {
+          fetch_st(2);
+          fetch_st(3);
+        }
+        if (k & 1) s2 = mfma32(oa[k], kf2[k >> 1], s2);
+        else s1 = mfma32(oa[k], kf1[k >> 1], s1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // dP products with the exponentials: P1 2^kappa and |lambda| P2 2^kappa.
+      float e1v[16], e2v[16];
+#pragma unroll
+      for (int k = 8; k < 16; ++k) {
+        if (k + 2 < 16) oa[k + 2] = fa(k + 2);
+        if constexpr (HC) {
+          if (k >= 14) oc[k - 14] = fetch_c(pCq, pCg, SUBC, k - 14);
+        }
+        dp = mfma32(oa[k], vf[k - 8], dp);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 2 * (k - 8) + u;
+          e1v[r] = fast_exp2(fmaf(s1[r], c, -st[r >> 2][0][r & 3]));
+          e2v[r] = fast_exp2(fmaf(s2[r], c, -st[r >> 2][1][r & 3]));
+          asm volatile("" : "+v"(e1v[r]), "+v"(e2v[r]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // dV, dK products of sub-chunk j - 1 with the dV weights and dS of j.
+      float pv[2][3];  // one pair of elementwise results awaiting conversion
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if constexpr (HC) {
+          if (k + 2 < 16) oc[k + 2] = fetch_c(pCq, pCg, SUBC, k + 2);
+          mfma_c(k, oc[k], pops);
+        }
+        const int r = k;
+        const float p1 = e1v[r], p2 = e2v[r];
+        pv[r & 1][0] = fmaf(fold.sig, p2, p1) * fW2;
+        pv[r & 1][1] = p1 * (dp[r] - st[r >> 2][2][r & 3]);
+        pv[r & 1][2] = p2 * fmaf(dp[r], fold.sig, st[r >> 2][3][r & 3]);
+        if (r & 1) {
+          const int kc2 = r >> 3, e = r & 7;
+          f16x2 a = __builtin_convertvector((f32x2{pv[0][0], pv[1][0]}), f16x2);
+          f16x2 b = __builtin_convertvector((f32x2{pv[0][1], pv[1][1]}), f16x2);
+          f16x2 d = __builtin_convertvector((f32x2{pv[0][2], pv[1][2]}), f16x2);
+          // Computed here, not where the next step first reads them.
+          asm volatile("" : "+v"(a), "+v"(b), "+v"(d));
+          nops.w[kc2][e - 1] = a[0];
+          nops.w[kc2][e] = a[1];
+          nops.b1[kc2][e - 1] = b[0];
+          nops.b1[kc2][e] = b[1];
+          nops.b2[kc2][e - 1] = d[0];
+          nops.b2[kc2][e] = d[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (cb + 1 < n_ch) store_half(smb[(cb + 1) % 3], hreg[SUB], tid, q_begin + (cb + 1) * QCH, S, SUB, fold);
+      if constexpr (SUB == 1) __syncthreads();
+      if (cb + 2 < n_ch) load_half(p, w, statb, q_begin + (cb + 2) * QCH, S, tid, SUB, hreg[SUB]);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    step(std::false_type{}, P0{}, 0, po[1], po[0]);
+    for (int j = 1; j < J - 1; j += 2) {
+      step(std::true_type{}, P1{}, j, po[0], po[1]);
+      step(std::true_type{}, P0{}, j + 1, po[1], po[0]);
+    }
+    step(std::true_type{}, P1{}, J - 1, po[0], po[1]);
+    // dV, dK products of the last sub-chunk.
+    {
+      const int bc = (n_mask + ((J - 1) >> 1)) % 3;
+      lchar *pCq = lptr(bc, lcQ), *pCg = lptr(bc, lcG);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mfma_c(i, fetch_c(pCq, pCg, 1, i), po[1]);
+    }
+  }
 
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
   if (my_key < S) {
