@@ -428,29 +428,11 @@ __device__ __forceinline__ void store_chunk(SmemA &sm, const ChunkRegs &r, int t
 
 // Half of a chunk's staging (part 0: the fp16 Q1 | Q2 rows and the row
 // statistics; part 1: the fp16 g' rows), for the pipelined loop, which stages
-// the next chunk over two steps so that only half of it is ever in registers.
+// the next chunk over two steps so that only half of it is in flight at once.
 struct HalfRegs {
   u32x4 v[4];
   float lse1, lse2, e1, e2;
 };
-
-__device__ __forceinline__ void load_half(const BwdParams &p, const Ws &w, int64_t statb, int q0, int S, int tid,
-                                          int part, HalfRegs &r) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
-    const bool ok = q < S;
-    const f16 *src = part == 0 ? w.qh + (statb + q) * (2 * D) + col : w.gh + (statb + q) * DV + col;
-    r.v[k] = ok ? *(const u32x4 *)src : u32x4{0, 0, 0, 0};
-  }
-  if (part == 0 && tid < QCH) {
-    const int64_t q = statb + min(q0 + tid, S - 1);
-    r.lse1 = p.lse1[q];
-    r.lse2 = p.lse2[q];
-    r.e1 = w.e1[q];
-    r.e2 = w.e2[q];
-  }
-}
 
 __device__ __forceinline__ void store_half(SmemA &sm, const HalfRegs &r, int tid, int q0, int S, int part,
                                            const RowFold &f) {
@@ -664,10 +646,31 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
 
     // Staging registers, one per half: each half is loaded right after the
     // previous chunk's same half was stored (two steps before its own store).
+    // The rows come through buffer loads over this (batch, head)'s S rows of
+    // 256 bytes (rows past the end read as zeros): no branches, 32-bit offsets.
+    const uint32_t rbytes = (uint32_t)S * 256;
+    const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)(w.qh + statb * (2 * D)), 0, rbytes,
+                                                                         0x00020000);
+    const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc((void *)(w.gh + statb * DV), 0, rbytes,
+                                                                         0x00020000);
+    auto load_part = [&](int q0, int part, HalfRegs &r) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        r.v[k] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(part == 0 ? rsq : rsg, (int)((uint32_t)q0 * 256 + (tid + NT * k) * 16),
+                                                         0, 0));
+      if (part == 0 && tid < QCH) {
+        const int64_t q = statb + min(q0 + tid, S - 1);
+        r.lse1 = p.lse1[q];
+        r.lse2 = p.lse2[q];
+        r.e1 = w.e1[q];
+        r.e2 = w.e2[q];
+      }
+    };
     HalfRegs hreg[2];
     if (n_mask + 1 < n_ch) {
-      load_half(p, w, statb, q_begin + (n_mask + 1) * QCH, S, tid, 0, hreg[0]);
-      load_half(p, w, statb, q_begin + (n_mask + 1) * QCH, S, tid, 1, hreg[1]);
+      load_part(q_begin + (n_mask + 1) * QCH, 0, hreg[0]);
+      load_part(q_begin + (n_mask + 1) * QCH, 1, hreg[1]);
     }
     auto step = [&](auto has_c, auto parity, int j, const Ops &pops, Ops &nops) {
       constexpr bool HC = decltype(has_c)::value;
@@ -763,7 +766,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
       }
       if (cb + 1 < n_ch) store_half(smb[(cb + 1) % 3], hreg[SUB], tid, q_begin + (cb + 1) * QCH, S, SUB, fold);
       if constexpr (SUB == 1) __syncthreads();
-      if (cb + 2 < n_ch) load_half(p, w, statb, q_begin + (cb + 2) * QCH, S, tid, SUB, hreg[SUB]);
+      if (cb + 2 < n_ch) load_part(q_begin + (cb + 2) * QCH, SUB, hreg[SUB]);
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
