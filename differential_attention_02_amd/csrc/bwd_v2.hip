@@ -503,20 +503,24 @@ struct ChunkRegs2 {
 
 // Loads the chunk of QCH query rows of pair pr starting at q0 (rows past the
 // end read as zeros; their statistics are read from the last row and masked
-// when stored).
+// when stored).  The fp16 rows come through buffer loads over the pair's S
+// rows (512 bytes of Q_e | Q_o, 256 of g' per row), whose range check gives
+// the zeros: no per-row branches, 32-bit offsets.
 __device__ __forceinline__ void load_chunk2(const V2BwdParams &p, const Ws2 &w, int b, int pr, int64_t rowb,
                                             int q0, int tid, ChunkRegs2 &r) {
   const int S = p.S;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(w.qh + rowb * (2 * D)), 0, (uint32_t)S * (4 * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(w.gh + rowb * D), 0, (uint32_t)S * (2 * D), 0x00020000);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int i = tid + NT * k, row = i >> 5, col = (i & 31) * 8, q = q0 + row;
-    r.q[k] = q < S ? *(const u32x4 *)(w.qh + (rowb + q) * (2 * D) + col) : u32x4{0, 0, 0, 0};
-  }
+  for (int k = 0; k < 8; ++k)
+    r.q[k] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((uint32_t)q0 * (4 * D) + (tid + NT * k) * 16), 0, 0));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
-    r.g[k] = q < S ? *(const u32x4 *)(w.gh + (rowb + q) * D + col) : u32x4{0, 0, 0, 0};
-  }
+  for (int k = 0; k < 4; ++k)
+    r.g[k] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)((uint32_t)q0 * (2 * D) + (tid + NT * k) * 16), 0, 0));
   if (tid < QCH) {
     const int q = min(q0 + tid, S - 1);
     const int64_t lr = ((int64_t)b * p.Hq + 2 * pr) * S + q;
