@@ -372,17 +372,27 @@ struct ChunkRegs {
   float lse1, lse2, e1, e2;
 };
 
+// Buffer resources over one (batch, head)'s S rows of 256 bytes (the fp16
+// Q1 | Q2 rows, or the fp16 g' rows): rows past the end read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const f16 *rows, int S) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)rows, 0, (uint32_t)S * 256, 0x00020000);
+}
+
+// Thread tid's four 16-byte pieces of the 64 rows starting at q0 (row-major,
+// 16 threads per row).
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs, int q0, int tid, u32x4 *v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    v[k] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((uint32_t)q0 * 256 + (tid + NT * k) * 16), 0, 0));
+}
+
 // Loads the chunk of QCH query rows starting at q0 (rows past the end read as
 // zeros; their statistics are read from the last row and masked when stored).
 __device__ __forceinline__ void load_chunk(const BwdParams &p, const Ws &w, int64_t statb, int q0, int S, int tid,
                                            ChunkRegs &r) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = tid + NT * k, row = i >> 4, col = (i & 15) * 8, q = q0 + row;
-    const bool ok = q < S;
-    r.q[k] = ok ? *(const u32x4 *)(w.qh + (statb + q) * (2 * D) + col) : u32x4{0, 0, 0, 0};
-    r.g[k] = ok ? *(const u32x4 *)(w.gh + (statb + q) * DV + col) : u32x4{0, 0, 0, 0};
-  }
+  load_rows(row_rsrc(w.qh + statb * (2 * D), S), q0, tid, r.q);
+  load_rows(row_rsrc(w.gh + statb * DV, S), q0, tid, r.g);
   if (tid < QCH) {
     const int64_t q = statb + min(q0 + tid, S - 1);
     r.lse1 = p.lse1[q];
@@ -646,19 +656,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
 
     // Staging registers, one per half: each half is loaded right after the
     // previous chunk's same half was stored (two steps before its own store).
-    // The rows come through buffer loads over this (batch, head)'s S rows of
-    // 256 bytes (rows past the end read as zeros): no branches, 32-bit offsets.
-    const uint32_t rbytes = (uint32_t)S * 256;
-    const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc((void *)(w.qh + statb * (2 * D)), 0, rbytes,
-                                                                         0x00020000);
-    const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc((void *)(w.gh + statb * DV), 0, rbytes,
-                                                                         0x00020000);
+    const __amdgpu_buffer_rsrc_t rsq = row_rsrc(w.qh + statb * (2 * D), S), rsg = row_rsrc(w.gh + statb * DV, S);
     auto load_part = [&](int q0, int part, HalfRegs &r) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        r.v[k] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(part == 0 ? rsq : rsg, (int)((uint32_t)q0 * 256 + (tid + NT * k) * 16),
-                                                         0, 0));
+      load_rows(part == 0 ? rsq : rsg, q0, tid, r.v);
       if (part == 0 && tid < QCH) {
         const int64_t q = statb + min(q0 + tid, S - 1);
         r.lse1 = p.lse1[q];
