@@ -521,12 +521,6 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) vf[kc] = ok ? to_f16x8(*(const u32x4 *)(vv + kc * 16), scv) : f16x8{};
   }
-  // These only feed matrix instructions, which read AGPRs as well: keep them
-  // there (the vector registers are the scarce side of this kernel).
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) asm volatile("" : "+a"(kf1[kc]), "+a"(kf2[kc]));
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) asm volatile("" : "+a"(vf[kc]));
 
   f32x16 dv[4], dk1[2], dk2[2];
 #pragma unroll
@@ -638,7 +632,6 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
     struct Ops {
       f16x8 w[2], b1[2], b2[2];
     };
-    Ops po[2];
     // Operand i (0..15) of the dV/dK products of sub-chunk sub: i = 8 kc2 + k;
     // k < 4: g^T columns 32 k (dV), 4, 5: Q1^T (dK1), 6, 7: Q2^T (dK2).
     auto fetch_c = [&](lchar *pq, lchar *pg, int sub, int i) -> f16x8 {
@@ -672,117 +665,138 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
       load_part(q_begin + (n_mask + 1) * QCH, 0, hreg[0]);
       load_part(q_begin + (n_mask + 1) * QCH, 1, hreg[1]);
     }
-    auto step = [&](auto has_c, auto parity, int j, const Ops &pops, Ops &nops) {
-      constexpr bool HC = decltype(has_c)::value;
-      constexpr int SUB = decltype(parity)::value;  // j % 2
-      constexpr int SUBC = 1 - SUB;                 // (j - 1) % 2
+    // Exponentials and dP of a sub-chunk, carried from one step to the next
+    // (two sets: step j writes set j % 2 and reads the other).
+    struct Carry {
+      float e1[16], e2[16];  // P1 2^kappa, |lambda| P2 2^kappa
+      f32x16 dp;
+    };
+    Carry cr[2];
+    Ops ops;
+
+    // Step j, in two halves of 16 matrix instructions each:
+    //   1. the score and dP products of sub-chunk j, with the dV weights and
+    //      dS of sub-chunk j - 1 (from its carried exponentials and dP);
+    //   2. the dV, dK products of sub-chunk j - 1, with the exponentials of j.
+    // Staging: the even step stores part 0 of chunk cb + 1, the odd step
+    // part 1 (then a barrier); each then loads the same part of chunk cb + 2.
+    auto step = [&](auto has_prev, auto has_cur, auto parity, int j, const Carry &prv, Carry &cur) {
+      constexpr bool HP = decltype(has_prev)::value;  // sub-chunk j - 1 exists
+      constexpr bool HJ = decltype(has_cur)::value;   // sub-chunk j exists
+      constexpr int SUB = decltype(parity)::value;    // j % 2
+      constexpr int SUBP = 1 - SUB;                   // (j - 1) % 2
       const int cb = n_mask + (j >> 1);
-      const int bb = cb % 3;
-      lchar *pAq = lptr(bb, laQ), *pAg = lptr(bb, laG), *pS = lptr(bb, lst);
-      lchar *pCq = nullptr, *pCg = nullptr;
-      if constexpr (HC) {
+      lchar *pAq = nullptr, *pAg = nullptr, *pS = nullptr, *pCq = nullptr, *pCg = nullptr, *pSp = nullptr;
+      if constexpr (HJ) {
+        pAq = lptr(cb % 3, laQ);
+        pAg = lptr(cb % 3, laG);
+        pS = lptr(cb % 3, lst);
+      }
+      if constexpr (HP) {
         const int bc = (n_mask + ((j - 1) >> 1)) % 3;
         pCq = lptr(bc, lcQ);
         pCg = lptr(bc, lcG);
+        pSp = lptr(bc, lst);
       }
-      // Staging: the even step stores part 0 of chunk cb + 1, the odd step
-      // part 1 (then a barrier); each then loads the same part of chunk cb + 2.
-      f32x4 st[4][4];  // statistics of four rows per group: lse1', lse2', E1', E2'
-      auto fetch_st = [&](int g) {
-        const uint32_t rb = (SUB * 32 + ((g & 2) << 3) + (g & 1) * 4) * 4;
-        st[g][0] = *(const DA_LDS f32x4 *)(pS + OL1 + rb);
-        st[g][1] = *(const DA_LDS f32x4 *)(pS + OL2 + rb);
-        st[g][2] = *(const DA_LDS f32x4 *)(pS + OE1 + rb);
-        st[g][3] = *(const DA_LDS f32x4 *)(pS + OE2 + rb);
-      };
+      auto rbyte = [&](int sub, int g) -> uint32_t { return (sub * 32 + ((g & 2) << 3) + (g & 1) * 4) * 4; };
       // Operand i of the score (i < 8: Q1 even, Q2 odd) and dP (i >= 8) products.
       auto fa = [&](int i) -> f16x8 {
         if (i < 8) return *(const DA_LDS f16x8 *)(pAq + ((i & 1) ? OQ2 : OQ1) + (SUB * 32 * QST + (i >> 1) * 16) * 2);
         return *(const DA_LDS f16x8 *)(pAg + OG + (SUB * 32 * GST + (i - 8) * 16) * 2);
       };
       f16x8 oa[16], oc[16];
-      oa[0] = fa(0);
-      oa[1] = fa(1);
-      fetch_st(0);
-      fetch_st(1);
-      f32x16 s1 = {}, s2 = {}, dp = {};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        oa[k + 2] = fa(k + 2);
-        if (k == 4) {
-          fetch_st(2);
-          fetch_st(3);
-        }
-        if (k & 1) s2 = mfma32(oa[k], kf2[k >> 1], s2);
-        else s1 = mfma32(oa[k], kf1[k >> 1], s1);
-        __builtin_amdgcn_sched_barrier(0);
+      f32x4 se[4][2], sl[4][2];  // E1', E2' of j - 1; lse1', lse2' of j (four rows per group)
+      auto fetch_e = [&](int g) {
+        se[g][0] = *(const DA_LDS f32x4 *)(pSp + OE1 + rbyte(SUBP, g));
+        se[g][1] = *(const DA_LDS f32x4 *)(pSp + OE2 + rbyte(SUBP, g));
+      };
+      auto fetch_l = [&](int g) {
+        sl[g][0] = *(const DA_LDS f32x4 *)(pS + OL1 + rbyte(SUB, g));
+        sl[g][1] = *(const DA_LDS f32x4 *)(pS + OL2 + rbyte(SUB, g));
+      };
+      f32x16 s1 = {}, s2 = {};
+      if constexpr (HJ) {
+        oa[0] = fa(0);
+        oa[1] = fa(1);
+        cur.dp = f32x16{};
       }
-      // dP products with the exponentials: P1 2^kappa and |lambda| P2 2^kappa.
-      float e1v[16], e2v[16];
-#pragma unroll
-      for (int k = 8; k < 16; ++k) {
-        if (k + 2 < 16) oa[k + 2] = fa(k + 2);
-        if constexpr (HC) {
-          if (k >= 14) oc[k - 14] = fetch_c(pCq, pCg, SUBC, k - 14);
-        }
-        dp = mfma32(oa[k], vf[k - 8], dp);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 2 * (k - 8) + u;
-          e1v[r] = fast_exp2(fmaf(s1[r], c, -st[r >> 2][0][r & 3]));
-          e2v[r] = fast_exp2(fmaf(s2[r], c, -st[r >> 2][1][r & 3]));
-          asm volatile("" : "+v"(e1v[r]), "+v"(e2v[r]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HP) {
+        fetch_e(0);
+        fetch_e(1);
       }
-      // dV, dK products of sub-chunk j - 1 with the dV weights and dS of j.
+      // Half 1.
       float pv[2][3];  // one pair of elementwise results awaiting conversion
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if constexpr (HC) {
-          if (k + 2 < 16) oc[k + 2] = fetch_c(pCq, pCg, SUBC, k + 2);
-          mfma_c(k, oc[k], pops);
+        if constexpr (HJ) {
+          if (k + 2 < 16) oa[k + 2] = fa(k + 2);
+          if (k < 8) {
+            if (k & 1) s2 = mfma32(oa[k], kf2[k >> 1], s2);
+            else s1 = mfma32(oa[k], kf1[k >> 1], s1);
+          } else {
+            cur.dp = mfma32(oa[k], vf[k - 8], cur.dp);
+          }
+          if (k == 12) fetch_l(0);
+          if (k == 14) fetch_l(1);
         }
-        const int r = k;
-        const float p1 = e1v[r], p2 = e2v[r];
-        pv[r & 1][0] = fmaf(fold.sig, p2, p1) * fW2;
-        pv[r & 1][1] = p1 * (dp[r] - st[r >> 2][2][r & 3]);
-        pv[r & 1][2] = p2 * fmaf(dp[r], fold.sig, st[r >> 2][3][r & 3]);
-        if (r & 1) {
-          const int kc2 = r >> 3, e = r & 7;
-          f16x2 a = __builtin_convertvector((f32x2{pv[0][0], pv[1][0]}), f16x2);
-          f16x2 b = __builtin_convertvector((f32x2{pv[0][1], pv[1][1]}), f16x2);
-          f16x2 d = __builtin_convertvector((f32x2{pv[0][2], pv[1][2]}), f16x2);
-          // Computed here, not where the next step first reads them.
-          asm volatile("" : "+v"(a), "+v"(b), "+v"(d));
-          nops.w[kc2][e - 1] = a[0];
-          nops.w[kc2][e] = a[1];
-          nops.b1[kc2][e - 1] = b[0];
-          nops.b1[kc2][e] = b[1];
-          nops.b2[kc2][e - 1] = d[0];
-          nops.b2[kc2][e] = d[1];
+        if constexpr (HP) {
+          if ((k & 3) == 0 && k / 4 + 2 < 4) fetch_e(k / 4 + 2);
+          if (k >= 14) oc[k - 14] = fetch_c(pCq, pCg, SUBP, k - 14);
+          const int r = k;
+          const float p1 = prv.e1[r], p2 = prv.e2[r], dpr = prv.dp[r];
+          pv[r & 1][0] = fmaf(fold.sig, p2, p1) * fW2;
+          pv[r & 1][1] = p1 * (dpr - se[r >> 2][0][r & 3]);
+          pv[r & 1][2] = p2 * fmaf(dpr, fold.sig, se[r >> 2][1][r & 3]);
+          if (r & 1) {
+            const int kc2 = r >> 3, e = r & 7;
+            f16x2 a = __builtin_convertvector((f32x2{pv[0][0], pv[1][0]}), f16x2);
+            f16x2 b = __builtin_convertvector((f32x2{pv[0][1], pv[1][1]}), f16x2);
+            f16x2 d = __builtin_convertvector((f32x2{pv[0][2], pv[1][2]}), f16x2);
+            asm volatile("" : "+v"(a), "+v"(b), "+v"(d));  // computed here, not at first use
+            ops.w[kc2][e - 1] = a[0];
+            ops.w[kc2][e] = a[1];
+            ops.b1[kc2][e - 1] = b[0];
+            ops.b1[kc2][e] = b[1];
+            ops.b2[kc2][e - 1] = d[0];
+            ops.b2[kc2][e] = d[1];
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (cb + 1 < n_ch) store_half(smb[(cb + 1) % 3], hreg[SUB], tid, q_begin + (cb + 1) * QCH, S, SUB, fold);
-      if constexpr (SUB == 1) __syncthreads();
-      if (cb + 2 < n_ch) load_part(q_begin + (cb + 2) * QCH, SUB, hreg[SUB]);
+      // Half 2.
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if constexpr (HP) {
+          if (k + 2 < 16) oc[k + 2] = fetch_c(pCq, pCg, SUBP, k + 2);
+          mfma_c(k, oc[k], ops);
+        }
+        if constexpr (HJ) {
+          if ((k & 3) == 0 && k / 4 + 2 < 4) fetch_l(k / 4 + 2);
+          const int r = k;
+          cur.e1[r] = fast_exp2(fmaf(s1[r], c, -sl[r >> 2][0][r & 3]));
+          cur.e2[r] = fast_exp2(fmaf(s2[r], c, -sl[r >> 2][1][r & 3]));
+          asm volatile("" : "+v"(cur.e1[r]), "+v"(cur.e2[r]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (HJ) {
+        if (cb + 1 < n_ch) store_half(smb[(cb + 1) % 3], hreg[SUB], tid, q_begin + (cb + 1) * QCH, S, SUB, fold);
+        if constexpr (SUB == 1) __syncthreads();
+        if (cb + 2 < n_ch) load_part(q_begin + (cb + 2) * QCH, SUB, hreg[SUB]);
+      }
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    step(std::false_type{}, P0{}, 0, po[1], po[0]);
+    using T = std::true_type;
+    using F = std::false_type;
+    step(F{}, T{}, P0{}, 0, cr[1], cr[0]);
     for (int j = 1; j < J - 1; j += 2) {
-      step(std::true_type{}, P1{}, j, po[0], po[1]);
-      step(std::true_type{}, P0{}, j + 1, po[1], po[0]);
+      step(T{}, T{}, P1{}, j, cr[0], cr[1]);
+      step(T{}, T{}, P0{}, j + 1, cr[1], cr[0]);
     }
-    step(std::true_type{}, P1{}, J - 1, po[0], po[1]);
-    // dV, dK products of the last sub-chunk.
-    {
-      const int bc = (n_mask + ((J - 1) >> 1)) % 3;
-      lchar *pCq = lptr(bc, lcQ), *pCg = lptr(bc, lcG);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mfma_c(i, fetch_c(pCq, pCg, 1, i), po[1]);
-    }
+    step(T{}, T{}, P1{}, J - 1, cr[0], cr[1]);
+    // The last sub-chunk's dV weights and dS, and its dV, dK products.
+    step(T{}, F{}, P0{}, J, cr[1], cr[0]);
   }
 
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
