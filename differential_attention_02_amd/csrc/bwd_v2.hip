@@ -36,6 +36,7 @@
 // their largest magnitudes (v2b_pre, v2b_scales; vrange.h), so any finite bf16
 // inputs convert without saturating or losing precision; results are unscaled
 // exactly.
+#include <cstddef>
 #include <type_traits>
 
 #include "common.h"
@@ -350,7 +351,7 @@ __device__ __forceinline__ void store_kv(SmemQ &sm, const KVRegs &r, int tid, co
 }
 
 __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
-  __shared__ SmemQ smb[2];  // double-buffered: tile kt + 1 is loaded while tile kt is in use
+  __shared__ SmemQ smb[3];  // tile kt in buffer kt % 3 (the pipeline reads two tiles while a third is staged)
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = p.Hq / 2, ppk = p.Hq / p.Hkv / 2;
@@ -415,7 +416,7 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
   // need: two loops, so the interior one carries no mask arithmetic.
   auto tile = [&](auto masked, int kt) {
     constexpr bool MASKED = decltype(masked)::value;
-    const SmemQ &sm = smb[kt & 1];
+    const SmemQ &sm = smb[kt % 3];
     if (kt + 1 < n_kt) ld.load(nx, (kt + 1) * KT);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -455,13 +456,174 @@ __global__ __launch_bounds__(NT, 1) void v2b_dq_kernel(V2BwdParams p, Ws2 w) {
         }
       }
     }
-    if (kt + 1 < n_kt) store_kv(smb[(kt + 1) & 1], nx, tid, sck, scv);  // the buffer tile kt - 1 used
+    if (kt + 1 < n_kt) store_kv(smb[(kt + 1) % 3], nx, tid, sck, scv);
     __syncthreads();
   };
   const int n_full = min(causal ? q0 / KT : n_kt, S / KT);  // tiles no query of the tile needs masked
-  int kt = 0;
-  for (; kt < n_full; ++kt) tile(std::false_type{}, kt);
-  for (; kt < n_kt; ++kt) tile(std::true_type{}, kt);
+
+  // The unmasked tiles run as a software pipeline over their 32-key
+  // sub-tiles.  Step j, in two halves: the score and dP products of sub-tile
+  // j beside the dS of sub-tile j - 1 (from its carried exponentials and dP),
+  // then the dQ products of j - 1 beside the exponentials of j; one matrix
+  // instruction and a share of the vector work at a time behind scheduling
+  // fences (the single wave on each SIMD issues in order, so that order is
+  // what overlaps the two units).  LDS operands are read two instructions
+  // ahead from per-step base addresses.  Staging: the even step 2m stores the
+  // K half of tile m + 1, the odd step its V half (then a barrier); each then
+  // loads the same half of tile m + 2.  Tile m is complete from the end of
+  // step 2m - 1 and last read in step 2m + 2.
+  const int J = 2 * n_full;
+  if (J > 0) {
+    typedef DA_LDS const char lchar;
+    const int jj = lane & 15, half16 = (lane >> 4) & 1;
+    const uint32_t laK = (krow * QST + 8 * h) * 2, laV = (krow * GST + 8 * h) * 2;
+    const uint32_t lcK = ((8 * h + (jj >> 2)) * QST + 16 * half16 + 4 * (jj & 3)) * 2;
+    constexpr uint32_t OK = offsetof(SmemQ, k), OV = offsetof(SmemQ, v);
+    // Base address of buffer `buf` plus a lane offset, opaque to the compiler
+    // so that it keeps the constant parts in the instructions' offsets.
+    auto lptr = [&](int buf, uint32_t lane_off) -> lchar * {
+      lchar *q = (lchar *)(smb + buf) + lane_off;
+      asm volatile("" : "+v"(q));
+      return q;
+    };
+    auto tr8 = [&](lchar *q, uint32_t off) -> f16x8 {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(q + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(q + off + 8 * QST));
+      const f16x4 a = __builtin_bit_cast(f16x4, lo), b = __builtin_bit_cast(f16x4, hi);
+      return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    };
+    // Staging halves: K (part 0) and V (part 1) rows of a tile.
+    auto load_part = [&](int t, int part, u32x4 *r) {
+      const uint32_t tb = (uint32_t)(t * KT) * ld.step;
+#pragma unroll
+      for (int i = 0; i < KT * (D / 8) / NT; ++i)
+        r[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(part == 0 ? ld.rk : ld.rv, (int)(ld.off[i] + tb), 0, 0));
+    };
+    auto store_part = [&](int t, int part, const u32x4 *r) {
+      SmemQ &sm = smb[t % 3];
+#pragma unroll
+      for (int i = 0; i < KT * (D / 8) / NT; ++i) {
+        const int idx = tid + i * NT, row = idx >> 4, col = (idx & 15) * 8;
+        if (part == 0) *(f16x8 *)(sm.k + row * QST + col) = to_f16x8(r[i], sck);
+        else *(f16x8 *)(sm.v + row * GST + col) = to_f16x8(r[i], scv);
+      }
+    };
+    u32x4 hreg[2][KT * (D / 8) / NT];
+    if (1 < n_kt) {
+      load_part(1, 0, hreg[0]);
+      load_part(1, 1, hreg[1]);
+    }
+    // Exponentials and dP of a sub-tile, carried to the next step (two sets:
+    // step j writes set j % 2 and reads the other).
+    struct Carry {
+      float pe[16], po[16];  // P_e 2^kappa, sigma P_o 2^kappa
+      f32x16 dp;
+    };
+    Carry cr[2];
+    f16x8 be[2], bo[2];  // dS operands of the previous sub-tile
+
+    auto step = [&](auto has_prev, auto has_cur, auto parity, int j, const Carry &prv, Carry &cur) {
+      constexpr bool HP = decltype(has_prev)::value;  // sub-tile j - 1 exists
+      constexpr bool HJ = decltype(has_cur)::value;   // sub-tile j exists
+      constexpr int SUB = decltype(parity)::value;    // j % 2
+      constexpr int SUBP = 1 - SUB;
+      const int t = j >> 1;
+      lchar *pK = nullptr, *pV = nullptr, *pC = nullptr;
+      if constexpr (HJ) {
+        pK = lptr(t % 3, laK);
+        pV = lptr(t % 3, laV);
+      }
+      if constexpr (HP) pC = lptr(((j - 1) >> 1) % 3, lcK);
+      // Operand i of the score (i < 8: K columns 16 i) and dP (i >= 8: V
+      // columns 16 (i - 8)) products; products m = 0..23: (K_i, head e),
+      // (K_i, head o) for i < 8, then (V_(m - 16)).
+      auto fa = [&](int i) -> f16x8 {
+        if (i < 8) return *(const DA_LDS f16x8 *)(pK + OK + (SUB * 32 * QST + i * 16) * 2);
+        return *(const DA_LDS f16x8 *)(pV + OV + (SUB * 32 * GST + (i - 8) * 16) * 2);
+      };
+      // Operand i (0..7) of the dQ products of sub-tile j - 1: K^T columns
+      // 32 (i % 4), rows 16 (i / 4).
+      auto fc = [&](int i) -> f16x8 { return tr8(pC, OK + ((SUBP * 32 + (i >> 2) * 16) * QST + (i & 3) * 32) * 2); };
+      f16x8 oa[16], oc[8];
+      f32x16 se = {}, so = {};
+      if constexpr (HJ) {
+        oa[0] = fa(0);
+        oa[1] = fa(1);
+        cur.dp = f32x16{};
+      }
+      // Half 1: products of j with the dS of j - 1.
+      float pv[2][2];  // one pair of dS values awaiting conversion
+#pragma unroll
+      for (int m = 0; m < 24; ++m) {
+        if constexpr (HJ) {
+          const int i = m < 16 ? m >> 1 : m - 8;  // operand of product m
+          const bool first = m < 16 ? !(m & 1) : true;
+          if (first && i + 2 < 16) oa[i + 2] = fa(i + 2);
+          if (m < 16) {
+            if (m & 1) so = mfma32(oa[i], qo[i], so);
+            else se = mfma32(oa[i], qe[i], se);
+          } else {
+            cur.dp = mfma32(oa[i], gf[i - 8], cur.dp);
+          }
+        }
+        if constexpr (HP) {
+          if (m >= 22) oc[m - 22] = fc(m - 22);
+          if (m < 16) {
+            const int r = m;
+            pv[r & 1][0] = prv.pe[r] * (prv.dp[r] - ee);
+            pv[r & 1][1] = prv.po[r] * (eo - prv.dp[r]);
+            if (r & 1) {
+              const int kc2 = r >> 3, e = r & 7;
+              f16x2 a = __builtin_convertvector((f32x2{pv[0][0], pv[1][0]}), f16x2);
+              f16x2 b = __builtin_convertvector((f32x2{pv[0][1], pv[1][1]}), f16x2);
+              asm volatile("" : "+v"(a), "+v"(b));  // computed here, not at first use
+              be[kc2][e - 1] = a[0];
+              be[kc2][e] = a[1];
+              bo[kc2][e - 1] = b[0];
+              bo[kc2][e] = b[1];
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Half 2: dQ products of j - 1 with the exponentials of j.
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        if constexpr (HP) {
+          const int i = m >> 1;
+          if (!(m & 1) && i + 2 < 8) oc[i + 2] = fc(i + 2);
+          const int kc2 = i >> 2, dt = i & 3;
+          if (m & 1) dqo[dt] = mfma32(oc[i], bo[kc2], dqo[dt]);
+          else dqe[dt] = mfma32(oc[i], be[kc2], dqe[dt]);
+        }
+        if constexpr (HJ) {
+          const int r = m;
+          cur.pe[r] = fast_exp2(fmaf(se[r], c, -Le));
+          cur.po[r] = fast_exp2(fmaf(so[r], c, -Lo));
+          asm volatile("" : "+v"(cur.pe[r]), "+v"(cur.po[r]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (HJ) {
+        if (t + 1 < n_kt) store_part(t + 1, SUB, hreg[SUB]);
+        if constexpr (SUB == 1) __syncthreads();
+        if (t + 2 < n_kt) load_part(t + 2, SUB, hreg[SUB]);
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using T = std::true_type;
+    using F = std::false_type;
+    step(F{}, T{}, P0{}, 0, cr[1], cr[0]);
+    for (int j = 1; j < J - 1; j += 2) {
+      step(T{}, T{}, P1{}, j, cr[0], cr[1]);
+      step(T{}, T{}, P0{}, j + 1, cr[1], cr[0]);
+    }
+    step(T{}, T{}, P1{}, J - 1, cr[0], cr[1]);
+    step(T{}, F{}, P0{}, J, cr[1], cr[0]);  // the last sub-tile's dS and dQ products
+  }
+  for (int kt = n_full; kt < n_kt; ++kt) tile(std::true_type{}, kt);
   if (qok) {
     const float fq = p.scale * fast_exp2(-(kap + sg + kv + kk));
     bf16 *de = (bf16 *)p.dq + b * p.dqs_b + (int64_t)my_q * p.dqs_s + 2 * pr * p.dqs_h;
