@@ -763,16 +763,26 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
 
   const int q_begin = causal ? (kb / QCH) * QCH : 0;
   const int n_ch = q_begin < S ? (S - q_begin + QCH - 1) / QCH : 0;
-  const int n_it = n_ch * ppk;  // (pair, chunk) steps, pair-major
+  const int n_it = n_ch * ppk;  // (pair, chunk) steps
+  // Step order: every pair's masked chunks (the diagonal, or all chunks of
+  // the last key block), pair-major, then every pair's unmasked chunks; step
+  // i stages step i + 1 either way.
+  const int n_mask = kb + KVB > S ? n_ch : (causal ? min(n_ch, KVB / QCH) : 0);
+  const int n_un = n_ch - n_mask, M = ppk * n_mask;
+  auto item_pair = [&](int i) { return j * ppk + (i < M ? i / n_mask : (i - M) / n_un); };
+  auto item_q0 = [&](int i) { return q_begin + (i < M ? i % n_mask : n_mask + (i - M) % n_un) * QCH; };
+  auto load_item = [&](int i, ChunkRegs2 &r) {
+    const int pr = item_pair(i);
+    load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, item_q0(i), tid, r);
+  };
   const int prow = row_perm(ln);
   // Query chunks double-buffered in LDS: step n + 1 is loaded into registers
   // while step n is computed, then stored to the other buffer; one barrier
   // per step.
   ChunkRegs2 nxt;
   if (n_it > 0) {
-    const int pr = j * ppk;
-    load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin, tid, nxt);
-    store_chunk2(smb[0], nxt, tid, q_begin, S, fE, kap);
+    load_item(0, nxt);
+    store_chunk2(smb[0], nxt, tid, item_q0(0), S, fE, kap);
   }
   __syncthreads();
   // One (pair, chunk) step; MASKED applies the key-range and causal masks,
@@ -783,12 +793,9 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
   auto step = [&](auto masked, int it) {
     constexpr bool MASKED = decltype(masked)::value;
     SmemC &sm = smb[it & 1];
-    const int q0 = q_begin + (it % n_ch) * QCH;
+    const int q0 = item_q0(it);
     const bool more = it + 1 < n_it;
-    if (more) {
-      const int pr = j * ppk + (it + 1) / n_ch;
-      load_chunk2(p, w, b, pr, ((int64_t)b * P + pr) * S, q_begin + ((it + 1) % n_ch) * QCH, tid, nxt);
-    }
+    if (more) load_item(it + 1, nxt);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int qs = q0 + sub * 32;
@@ -833,13 +840,184 @@ __global__ __launch_bounds__(NT, 1) void v2b_dkdv_kernel(V2BwdParams p, Ws2 w) {
         }
       }
     }
-    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid, q_begin + ((it + 1) % n_ch) * QCH, S, fE, kap);
+    if (more) store_chunk2(smb[(it + 1) & 1], nxt, tid, item_q0(it + 1), S, fE, kap);
     __syncthreads();
   };
-  const int n_mask = kb + KVB > S ? n_ch : (causal ? min(n_ch, KVB / QCH) : 0);
-  for (int pp = 0, it = 0; pp < ppk; ++pp) {
-    for (int ci = 0; ci < n_mask; ++ci, ++it) step(std::true_type{}, it);
-    for (int ci = n_mask; ci < n_ch; ++ci, ++it) step(std::false_type{}, it);
+  for (int it = 0; it < M; ++it) step(std::true_type{}, it);
+
+  // The unmasked chunks (steps M ..) run as a software pipeline over their
+  // 32-query sub-chunks, as in the V1 key-outer kernel: step jp issues the
+  // score and dP products of sub-chunk jp beside the dV weights and dS of
+  // sub-chunk jp - 1 (from its carried exponentials and dP), then the dV, dK
+  // products of jp - 1 beside the exponentials of jp; one matrix instruction
+  // and a share of the vector work at a time behind scheduling fences.  Two
+  // LDS buffers (step i in buffer i % 2): chunk c + 1 goes into the buffer of
+  // chunk c - 1, which sub-chunk 2c last reads, so every step ends with a
+  // barrier; it is loaded at the start of step 2c and stored at the start of
+  // step 2c + 1.
+  const int JP = 2 * (n_it - M);
+  if (JP > 0) {
+    typedef DA_LDS const char lchar;
+    const int hq = 8 * h, jj = lane & 15, half16 = (lane >> 4) & 1;
+    const uint32_t laQ = (prow * QST + hq) * 2, laG = (prow * GST + hq) * 2;
+    const uint32_t lcQ = ((hq + (jj >> 2)) * QST + 16 * half16 + 4 * (jj & 3)) * 2;
+    const uint32_t lcG = ((hq + (jj >> 2)) * GST + 16 * half16 + 4 * (jj & 3)) * 2;
+    const uint32_t lst = hq * 4;
+    constexpr uint32_t OQE = offsetof(SmemC, qe), OQO = offsetof(SmemC, qo), OG = offsetof(SmemC, g);
+    constexpr uint32_t OLE = offsetof(SmemC, le), OLO = offsetof(SmemC, lo), OEE = offsetof(SmemC, ee),
+                       OEO = offsetof(SmemC, eo);
+    auto lptr = [&](int buf, uint32_t lane_off) -> lchar * {
+      lchar *q = (lchar *)(smb + buf) + lane_off;
+      asm volatile("" : "+v"(q));
+      return q;
+    };
+    auto tr8 = [&](lchar *q, uint32_t off, int stride) -> f16x8 {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(q + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(q + off + 8 * stride));
+      const f16x4 a = __builtin_bit_cast(f16x4, lo), bb = __builtin_bit_cast(f16x4, hi);
+      return f16x8{a[0], a[1], a[2], a[3], bb[0], bb[1], bb[2], bb[3]};
+    };
+    struct Carry {
+      float pe[16], po[16];  // P_e 2^kappa, sigma P_o 2^kappa
+      f32x16 dp;
+    };
+    Carry cr[2];
+    f16x8 wb[2], be[2], bo[2];  // dV / dK operands of the previous sub-chunk
+
+    auto pstep = [&](auto has_prev, auto has_cur, auto parity, int jp, const Carry &prv, Carry &cur) {
+      constexpr bool HP = decltype(has_prev)::value;  // sub-chunk jp - 1 exists
+      constexpr bool HJ = decltype(has_cur)::value;   // sub-chunk jp exists
+      constexpr int SUB = decltype(parity)::value;    // jp % 2
+      constexpr int SUBP = 1 - SUB;
+      const int ic = M + (jp >> 1);                   // step of sub-chunk jp
+      lchar *pAq = nullptr, *pAg = nullptr, *pS = nullptr, *pCq = nullptr, *pCg = nullptr, *pSp = nullptr;
+      if constexpr (HJ) {
+        pAq = lptr(ic & 1, laQ);
+        pAg = lptr(ic & 1, laG);
+        pS = lptr(ic & 1, lst);
+      }
+      if constexpr (HP) {
+        const int bc = (M + ((jp - 1) >> 1)) & 1;
+        pCq = lptr(bc, lcQ);
+        pCg = lptr(bc, lcG);
+        pSp = lptr(bc, lst);
+      }
+      // Staging: the even step loads step ic + 1, the odd step stores it into
+      // the other buffer (free since the barrier that ended the even step).
+      if constexpr (HJ && SUB == 0) {
+        if (ic + 1 < n_it) load_item(ic + 1, nxt);
+      }
+      if constexpr (HJ && SUB == 1) {
+        if (ic + 1 < n_it) store_chunk2(smb[(ic + 1) & 1], nxt, tid, item_q0(ic + 1), S, fE, kap);
+      }
+      auto rbyte = [&](int sub, int g) -> uint32_t { return (sub * 32 + ((g & 2) << 3) + (g & 1) * 4) * 4; };
+      // Product m (0..23) of sub-chunk jp: kc = m / 3; Q_e, Q_o or g' row
+      // columns 16 kc against K, K, V.
+      auto fa = [&](int m) -> f16x8 {
+        const int kc = m / 3, kind = m % 3;
+        if (kind == 2) return *(const DA_LDS f16x8 *)(pAg + OG + (SUB * 32 * GST + kc * 16) * 2);
+        return *(const DA_LDS f16x8 *)(pAq + (kind ? OQO : OQE) + (SUB * 32 * QST + kc * 16) * 2);
+      };
+      // dV / dK product m (0..23) of sub-chunk jp - 1: kc2 = m / 12; then
+      // channel tile ct and g' (dV), Q_e, Q_o (dK).
+      auto fc = [&](int m) -> f16x8 {
+        const int kc2 = m / 12, ct = (m % 12) / 3, kind = m % 3, r0 = SUBP * 32 + kc2 * 16;
+        if (kind == 0) return tr8(pCg, OG + (r0 * GST + ct * 32) * 2, GST);
+        return tr8(pCq, (kind == 1 ? OQE : OQO) + (r0 * QST + ct * 32) * 2, QST);
+      };
+      f16x8 oa[24], oc[24];
+      f32x4 se[4][2], sl[4][2];  // E_e', E_o' of jp - 1; le', lo' of jp (four rows per group)
+      auto fetch_e = [&](int g) {
+        se[g][0] = *(const DA_LDS f32x4 *)(pSp + OEE + rbyte(SUBP, g));
+        se[g][1] = *(const DA_LDS f32x4 *)(pSp + OEO + rbyte(SUBP, g));
+      };
+      auto fetch_l = [&](int g) {
+        sl[g][0] = *(const DA_LDS f32x4 *)(pS + OLE + rbyte(SUB, g));
+        sl[g][1] = *(const DA_LDS f32x4 *)(pS + OLO + rbyte(SUB, g));
+      };
+      f32x16 s_e = {}, s_o = {};
+      if constexpr (HJ) {
+        oa[0] = fa(0);
+        oa[1] = fa(1);
+        cur.dp = f32x16{};
+      }
+      if constexpr (HP) {
+        fetch_e(0);
+        fetch_e(1);
+      }
+      // Half 1: products of jp with the dV weights and dS of jp - 1.
+      float pv[2][3];  // one pair of results awaiting conversion
+#pragma unroll
+      for (int m = 0; m < 24; ++m) {
+        if constexpr (HJ) {
+          if (m + 2 < 24) oa[m + 2] = fa(m + 2);
+          const int kc = m / 3, kind = m % 3;
+          if (kind == 0) s_e = mfma32(oa[m], kf[kc], s_e);
+          else if (kind == 1) s_o = mfma32(oa[m], kf[kc], s_o);
+          else cur.dp = mfma32(oa[m], vf[kc], cur.dp);
+          if (m == 20) fetch_l(0);
+          if (m == 22) fetch_l(1);
+        }
+        if constexpr (HP) {
+          if (m >= 22) oc[m - 22] = fc(m - 22);
+          if (m < 16) {
+            if ((m & 3) == 0 && m / 4 + 2 < 4) fetch_e(m / 4 + 2);
+            const int r = m;
+            const float pe = prv.pe[r], po = prv.po[r], dpr = prv.dp[r];
+            pv[r & 1][0] = (pe - po) * fW2;
+            pv[r & 1][1] = pe * (dpr - se[r >> 2][0][r & 3]);
+            pv[r & 1][2] = po * (se[r >> 2][1][r & 3] - dpr);
+            if (r & 1) {
+              const int kc2 = r >> 3, e = r & 7;
+              f16x2 a = __builtin_convertvector((f32x2{pv[0][0], pv[1][0]}), f16x2);
+              f16x2 bb = __builtin_convertvector((f32x2{pv[0][1], pv[1][1]}), f16x2);
+              f16x2 d = __builtin_convertvector((f32x2{pv[0][2], pv[1][2]}), f16x2);
+              asm volatile("" : "+v"(a), "+v"(bb), "+v"(d));  // computed here, not at first use
+              wb[kc2][e - 1] = a[0];
+              wb[kc2][e] = a[1];
+              be[kc2][e - 1] = bb[0];
+              be[kc2][e] = bb[1];
+              bo[kc2][e - 1] = d[0];
+              bo[kc2][e] = d[1];
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Half 2: dV, dK products of jp - 1 with the exponentials of jp.
+#pragma unroll
+      for (int m = 0; m < 24; ++m) {
+        if constexpr (HP) {
+          if (m + 2 < 24) oc[m + 2] = fc(m + 2);
+          const int kc2 = m / 12, ct = (m % 12) / 3, kind = m % 3;
+          if (kind == 0) dv[ct] = mfma32(oc[m], wb[kc2], dv[ct]);
+          else if (kind == 1) dk[ct] = mfma32(oc[m], be[kc2], dk[ct]);
+          else dk[ct] = mfma32(oc[m], bo[kc2], dk[ct]);
+        }
+        if constexpr (HJ) {
+          if (m < 16) {
+            if ((m & 3) == 0 && m / 4 + 2 < 4) fetch_l(m / 4 + 2);
+            const int r = m;
+            cur.pe[r] = fast_exp2(fmaf(s_e[r], c, -sl[r >> 2][0][r & 3]));
+            cur.po[r] = fast_exp2(fmaf(s_o[r], c, -sl[r >> 2][1][r & 3]));
+            asm volatile("" : "+v"(cur.pe[r]), "+v"(cur.po[r]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using T = std::true_type;
+    using F = std::false_type;
+    pstep(F{}, T{}, P0{}, 0, cr[1], cr[0]);
+    for (int jp = 1; jp < JP - 1; jp += 2) {
+      pstep(T{}, T{}, P1{}, jp, cr[0], cr[1]);
+      pstep(T{}, T{}, P0{}, jp + 1, cr[1], cr[0]);
+    }
+    pstep(T{}, T{}, P1{}, JP - 1, cr[0], cr[1]);
+    pstep(T{}, F{}, P0{}, JP, cr[1], cr[0]);  // the last sub-chunk's dV weights, dS and products
   }
 
   // Epilogue: lane = key, registers = channels 8 (r/4) + 4 h + r%4 of each tile.
