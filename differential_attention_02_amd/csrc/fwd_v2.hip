@@ -27,6 +27,9 @@
 // computed transposed (S^T = K Q^T, lane = query); K rows are read in the
 // permuted order of the shared tile helpers so a lane's score registers are
 // the k-slots of the PV step; V^T comes through LDS transpose reads.
+#include <cstddef>
+#include <type_traits>
+
 #include "attn_tile.h"
 #include "kernels.h"
 #include "vrange.h"
@@ -159,7 +162,9 @@ __device__ __forceinline__ void pass2_tile(const SmemV2 &sm, int kbase, int krow
 // g . A_t of each head consistent with that head's probabilities.
 template <bool SAVE>
 __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p) {
-  __shared__ SmemV2 sm[2];
+  // With SAVE (one workgroup per CU) a third buffer lets pass 2 run as a
+  // software pipeline (see there).
+  __shared__ SmemV2 sm[SAVE ? 3 : 2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave tests become scalar branches
   const int ln = lane & 31, h = lane >> 5;
@@ -245,22 +250,173 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
   ld.load(0, true, nxt);
   store_tile(sm[0], nxt, tid, true, vsc);
   __syncthreads();
-  for (int kt = 0; kt < n_full; ++kt) {
-    ld.load((kt + 1) * BN, true, nxt);
-    if constexpr (!SAVE) sched_fence();
-    pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
-                            my_q);
-    if constexpr (!SAVE) sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
-    __syncthreads();
+  constexpr int NB = SAVE ? 3 : 2;  // pass-2 buffers: tile kt in buffer kt % NB
+  if constexpr (!SAVE) {
+    for (int kt = 0; kt < n_full; ++kt) {
+      ld.load((kt + 1) * BN, true, nxt);
+      sched_fence();
+      pass2_tile<false, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal,
+                              qw, my_q);
+      sched_fence();
+      store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
+      __syncthreads();
+    }
+  } else if (n_full > 0) {
+    // The unmasked tiles as a software pipeline over 32-key sub-tiles.  Step
+    // j, in two halves: the score products of sub-tile j beside the weights
+    // of sub-tile j - 1 (from its carried exponentials), then the three PV
+    // products of j - 1 beside the exponentials of j; one matrix instruction
+    // and a share of the vector work at a time behind scheduling fences (the
+    // single wave on each SIMD issues in order, so that order is what
+    // overlaps the two units).  LDS operands are read two instructions ahead
+    // from per-step base addresses.  Staging: the even step 2m stores the K
+    // half of tile m + 1, the odd step its V half (then a barrier); each then
+    // loads the same half of tile m + 2.  Tile m is complete from the end of
+    // step 2m - 1 and last read in step 2m + 2.
+    typedef DA_LDS const char lchar;
+    const int jj = lane & 15, half16 = (lane >> 4) & 1;
+    const uint32_t laK = (krow * KST + 8 * h) * 2;
+    const uint32_t lcV = ((8 * h + (jj >> 2)) * VST + 16 * half16 + 4 * (jj & 3)) * 2;
+    constexpr uint32_t OK = offsetof(SmemV2, k), OV = offsetof(SmemV2, v);
+    auto lptr = [&](int buf, uint32_t lane_off) -> lchar * {
+      lchar *q = (lchar *)(sm + buf) + lane_off;
+      asm volatile("" : "+v"(q));
+      return q;
+    };
+    // Staging halves: K (part 0, bf16 as loaded) and V (part 1, to fp16).
+    auto load_part = [&](int t, int part, u32x4 *r) {
+      const uint32_t tb = (uint32_t)(t * BN) * ld.step;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(part == 0 ? ld.rk : ld.rv, (int)(ld.off[i] + tb), 0, 0));
+    };
+    auto store_part = [&](int t, int part, const u32x4 *r) {
+      SmemV2 &st = sm[t % NB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (tid >> 4) + 16 * i, col = (tid & 15) * 8;
+        if (part == 0) *(u32x4 *)(st.k + row * KST + col) = r[i];
+        else *(u32x4 *)(st.v + row * VST + col) = bf16x8_to_f16x8_scaled(r[i], vsc);
+      }
+    };
+    u32x4 hreg[2][4];
+    if (1 < n_kt) {
+      load_part(1, 0, hreg[0]);
+      load_part(1, 1, hreg[1]);
+    }
+    struct Carry {
+      float xe[16], xo[16];  // each head's weight, exp2(s c - L)
+    };
+    Carry cr[2];
+    f16x8 wb[2], web[2], wob[2];  // PV operands of the previous sub-tile
+
+    auto step = [&](auto has_prev, auto has_cur, auto parity, int j, const Carry &prv, Carry &cur) {
+      constexpr bool HP = decltype(has_prev)::value;  // sub-tile j - 1 exists
+      constexpr bool HJ = decltype(has_cur)::value;   // sub-tile j exists
+      constexpr int SUB = decltype(parity)::value;    // j % 2
+      constexpr int SUBP = 1 - SUB;
+      const int t = j >> 1;
+      lchar *pK = nullptr, *pV = nullptr;
+      if constexpr (HJ) pK = lptr(t % NB, laK);
+      if constexpr (HP) pV = lptr(((j - 1) >> 1) % NB, lcV);
+      auto fk = [&](int kc) -> bf16x8 { return *(const DA_LDS bf16x8 *)(pK + OK + (SUB * 32 * KST + kc * 16) * 2); };
+      // PV operand i (0..7) of sub-tile j - 1: keys 16 (i / 4), channels 32 (i % 4).
+      auto fv = [&](int i) -> f16x8 {
+        const uint32_t off = OV + ((SUBP * 32 + (i >> 2) * 16) * VST + (i & 3) * 32) * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(pV + off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DA_LDS i16x4 *)(pV + off + 8 * VST));
+        const f16x4 a = __builtin_bit_cast(f16x4, lo), bb = __builtin_bit_cast(f16x4, hi);
+        return f16x8{a[0], a[1], a[2], a[3], bb[0], bb[1], bb[2], bb[3]};
+      };
+      bf16x8 ok_[8];
+      f16x8 ov[8];
+      f32x16 se = {}, so = {};
+      if constexpr (HJ) {
+        ok_[0] = fk(0);
+        ok_[1] = fk(1);
+      }
+      // Half 1: score products of j (K operand m / 2, heads alternating) with
+      // the weights of j - 1.
+      float pw[2][3];  // one pair of weights awaiting conversion
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        if constexpr (HJ) {
+          const int kc = m >> 1;
+          if (!(m & 1) && kc + 2 < 8) ok_[kc + 2] = fk(kc + 2);
+          if (m & 1) so = mfma32(ok_[kc], qo[kc], so);
+          else se = mfma32(ok_[kc], qe[kc], se);
+        }
+        if constexpr (HP) {
+          if (m >= 14) ov[m - 14] = fv(m - 14);
+          const int r = m;
+          const float xe = prv.xe[r], xo = prv.xo[r];
+          pw[r & 1][0] = xe - sig * xo;
+          pw[r & 1][1] = xe * fe;
+          pw[r & 1][2] = xo * fo;
+          if (r & 1) {
+            const int kc2 = r >> 3, e = r & 7;
+            f16x2 a = __builtin_convertvector((f32x2{pw[0][0], pw[1][0]}), f16x2);
+            f16x2 bb = __builtin_convertvector((f32x2{pw[0][1], pw[1][1]}), f16x2);
+            f16x2 d = __builtin_convertvector((f32x2{pw[0][2], pw[1][2]}), f16x2);
+            asm volatile("" : "+v"(a), "+v"(bb), "+v"(d));  // computed here, not at first use
+            wb[kc2][e - 1] = a[0];
+            wb[kc2][e] = a[1];
+            web[kc2][e - 1] = bb[0];
+            web[kc2][e] = bb[1];
+            wob[kc2][e - 1] = d[0];
+            wob[kc2][e] = d[1];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Half 2: the PV products of j - 1 (operand m / 3: O, A_even, A_odd)
+      // with the exponentials of j.
+#pragma unroll
+      for (int m = 0; m < 24; ++m) {
+        if constexpr (HP) {
+          const int i = m / 3, kind = m % 3, kc2 = i >> 2, ct = i & 3;
+          if (kind == 0 && i + 2 < 8) ov[i + 2] = fv(i + 2);
+          if (kind == 0) o[ct] = mfma32(ov[i], wb[kc2], o[ct]);
+          else if (kind == 1) ae[ct] = mfma32(ov[i], web[kc2], ae[ct]);
+          else ao[ct] = mfma32(ov[i], wob[kc2], ao[ct]);
+        }
+        if constexpr (HJ) {
+          if (m < 16) {
+            const int r = m;
+            cur.xe[r] = fast_exp2(fmaf(se[r], c, -Les));
+            cur.xo[r] = fast_exp2(fmaf(so[r], c, -Los));
+            asm volatile("" : "+v"(cur.xe[r]), "+v"(cur.xo[r]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (HJ) {
+        if (t + 1 < n_kt) store_part(t + 1, SUB, hreg[SUB]);
+        if constexpr (SUB == 1) __syncthreads();
+        if (t + 2 < n_kt) load_part(t + 2, SUB, hreg[SUB]);
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using T = std::true_type;
+    using F = std::false_type;
+    const int J = 2 * n_full;
+    step(F{}, T{}, P0{}, 0, cr[1], cr[0]);
+    for (int j = 1; j < J - 1; j += 2) {
+      step(T{}, T{}, P1{}, j, cr[0], cr[1]);
+      step(T{}, T{}, P0{}, j + 1, cr[1], cr[0]);
+    }
+    step(T{}, T{}, P1{}, J - 1, cr[0], cr[1]);
+    step(T{}, F{}, P0{}, J, cr[1], cr[0]);  // the last sub-tile's weights and PV products
   }
   for (int kt = n_full; kt < n_kt; ++kt) {
     ld.load((kt + 1) * BN, true, nxt);
     if constexpr (!SAVE) sched_fence();
-    pass2_tile<true, SAVE>(sm[kt & 1], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
+    pass2_tile<true, SAVE>(sm[kt % NB], kt * BN, krow, lane, qe, qo, c, sig, Les, Los, fe, fo, o, ae, ao, S, causal, qw,
                            my_q);
     if constexpr (!SAVE) sched_fence();
-    store_tile(sm[(kt + 1) & 1], nxt, tid, true, vsc);
+    store_tile(sm[(kt + 1) % NB], nxt, tid, true, vsc);
     __syncthreads();
   }
 
