@@ -32,10 +32,12 @@
 //              sum_j P_m dP' up to float32 rounding, so dS = P (dP - E) stays
 //              self-consistent where one key dominates a row and dP - E
 //              cancels; also the row's Q1 | Q2 in fp16 for the key-outer
-//              kernel's staging;
+//              kernel's staging and its K1 | K2 and V in fp16 for the
+//              query-outer kernel's (converted once here rather than once per
+//              query tile that reads them);
 //   bwd_dq     query-outer (the forward's layout): each workgroup owns 128
-//              queries and streams 64-key tiles: dS and dQ1, dQ2 accumulated
-//              in registers;
+//              queries and streams 64-key tiles through swizzled LDS tiles:
+//              dS and dQ1, dQ2 accumulated in registers;
 //   bwd_dkdv   KV-outer: each workgroup owns 128 keys (4 waves x 32) and
 //              streams 64-query chunks: recomputes P1, P2 and dP, accumulates
 //              dV, dK1, dK2 in registers; past the diagonal, one sub-chunk's
@@ -55,7 +57,6 @@
 
 #include "common.h"
 #include "kernels.h"
-#include "v1_stage.h"
 #include "vrange.h"
 
 namespace diffattn {
@@ -67,7 +68,9 @@ constexpr int GST = DV + 32;  // LDS row stride (fp16) of g / V tiles (tr16-frie
 
 struct Ws {
   f16 *gh;         // [B, H, S, DV] fp16, g * 2^sg
-  f16 *qh;         // [B, H, S, 2 D] fp16: Q1 (channels 0..63) and Q2 (64..127)
+  f16 *qh;         // [B, H, S, 2 D] fp16: Q1 (channels 0..63) and Q2 (64..127), times 2^kq
+  f16 *kh;         // [B, H, S, 2 D] fp16: K1 | K2 times 2^kk
+  f16 *vh;         // [B, H, S, DV] fp16: V times 2^kv
   float *e1, *e2;  // [B, H, S]  E_m = sum_j P_m dP (unscaled)
   float *gnorm, *vnorm, *dlam_row;  // [B, H, S]
   float *amax;     // [B, H, S][4]: the row's largest |Q1|,|Q2|; |K1|,|K2|; |V|; unused
@@ -83,6 +86,8 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
   Ws w;
   w.gh = (f16 *)p; p += align256(rows * DV * 2);
   w.qh = (f16 *)p; p += align256(rows * 2 * D * 2);
+  w.kh = (f16 *)p; p += align256(rows * 2 * D * 2);
+  w.vh = (f16 *)p; p += align256(rows * DV * 2);
   w.e1 = (float *)p; p += align256(rows * 4);
   w.e2 = (float *)p; p += align256(rows * 4);
   w.gnorm = (float *)p; p += align256(rows * 4);
@@ -96,7 +101,7 @@ __host__ __device__ inline Ws carve(void *base, int B, int S, int H) {
 
 __host__ __device__ inline size_t ws_bytes(int B, int S, int H) {
   const size_t rows = (size_t)B * H * S;
-  return align256(rows * DV * 2) + align256(rows * 2 * D * 2) + 5 * align256(rows * 4) +
+  return 2 * align256(rows * DV * 2) + 2 * align256(rows * 2 * D * 2) + 5 * align256(rows * 4) +
          align256(rows * 16) + align256((size_t)B * H * 32) + align256((size_t)B * H * 4);
 }
 
@@ -307,6 +312,16 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
                                        h * p.qs_h + qc);
     const VScale sq((int)w.scales[bh * 8 + 3]);
     *(u32x4 *)(w.qh + row * (2 * D) + c) = sq.on ? bf16x8_to_f16x8<true>(raw, sq) : bf16x8_to_f16x8<false>(raw, sq);
+    // Its key-side rows for the query-outer kernel's staging: K1 | K2 times
+    // 2^kk and V times 2^kv (the same row index: keys and queries are the
+    // same S tokens).
+    const u32x4 rk = *(const u32x4 *)((const bf16 *)(part < 8 ? p.k1 : p.k2) + b * p.ks_b + (int64_t)s * p.ks_s +
+                                      h * p.ks_h + qc);
+    const VScale sk((int)w.scales[bh * 8 + 4]);
+    *(u32x4 *)(w.kh + row * (2 * D) + c) = sk.on ? bf16x8_to_f16x8<true>(rk, sk) : bf16x8_to_f16x8<false>(rk, sk);
+    const u32x4 rv = *(const u32x4 *)((const bf16 *)p.v + b * p.vs_b + (int64_t)s * p.vs_s + h * p.vs_h + c);
+    const VScale sv((int)w.scales[bh * 8 + 5]);
+    *(u32x4 *)(w.vh + row * DV + c) = sv.on ? bf16x8_to_f16x8<true>(rv, sv) : bf16x8_to_f16x8<false>(rv, sv);
     if (part == 0) {
       const float un = exp2i(-sg);
       w.e1[row] = e1 * un;
@@ -345,6 +360,48 @@ __device__ __forceinline__ f16x8 tr_operand(const f16 *tile, int stride, int r0,
   const f16 *ptr = tile + (r0 + 8 * h + (j >> 2)) * stride + c0 + 16 * half16 + 4 * (j & 3);
   const f16x4 lo = lds_read_tr16(ptr);
   const f16x4 hi = lds_read_tr16(ptr + 4 * stride);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Swizzled tiles (no row padding): 16-byte chunk c of row r of a tile with
+// 64-half rows (K) is stored at chunk c ^ swz64(r), of a tile with 128-half
+// rows (V) at chunk c ^ swz128(r).  The matrix products read a tile two ways:
+// one chunk of 16 consecutive rows per 16 lanes (row operands, 16-byte reads)
+// and four consecutive chunks of 4 consecutive rows per 32 lanes (transpose
+// reads, 8 bytes each); with these permutations both touch each of the 64 LDS
+// banks once per 256 bytes, where a plain row padding can serve only one of
+// the two (128-half rows padded to 160 put every fourth row of a row-operand
+// read on the same banks).  Both depend on r mod 16 only.
+__device__ __forceinline__ int swz64(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz128(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Half offset of chunk c of row r in a swizzled tile with W-half rows.  For
+// c = c1 | c2 with disjoint bits, swz_off(r, c1 | c2) = swz_off(r, c1) ^ 8 c2:
+// each lane keeps one offset per access pattern and forms every read of that
+// pattern with one XOR.
+template <int W>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * W + 8 * (c ^ (W == D ? swz64(r) : swz128(r)));
+}
+
+// Lane offsets of the two transpose reads of tr_operand (rows 8 (l / 32) +
+// (l % 16) / 4 and 4 below, the lane's 8 bytes of chunks 2 ((l / 16) % 2) + 0..1).
+struct TrLane {
+  int lo, hi;
+};
+
+template <int W>
+__device__ __forceinline__ TrLane tr_lane(int lane) {
+  const int h = lane >> 5, j = lane & 15, half16 = (lane >> 4) & 1;
+  const int r = 8 * h + (j >> 2), c = 2 * half16 + ((j & 3) >> 1), w = 4 * (j & 1);
+  return TrLane{swz_off<W>(r, c) + w, swz_off<W>(r + 4, c) + w};
+}
+
+// tr_operand on a swizzled tile with W-half rows (r0 a multiple of 16, c0 of 32).
+template <int W>
+__device__ __forceinline__ f16x8 tr_operand_swz(const f16 *tile, const TrLane &t, int r0, int c0) {
+  const f16x4 lo = lds_read_tr16(tile + r0 * W + (t.lo ^ c0));
+  const f16x4 hi = lds_read_tr16(tile + r0 * W + (t.hi ^ c0));
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -828,55 +885,57 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdParams p, Ws w) {
 
 // ---------------------------------------------------------------------------
 // bwd_dq: query-outer.  Workgroup = 128 queries of one (b, h); wave w owns
-// queries q0 + 32 w + 0..31 (lane l % 32).  Streams 64-key tiles of K1, K2, V
-// twice: pass 1 accumulates E_m = sum_j P_m dP, pass 2 forms dS and dQ.
+// queries q0 + 32 w + 0..31 (lane l % 32).  Streams 64-key tiles of the fp16
+// K1, K2, V rows once, forming dS and dQ (E_m comes from bwd_gconv).
 constexpr int QB = 128, KT = 64;
 
-struct SmemB {
-  f16 k1[KT * QST];
-  f16 k2[KT * QST];
-  f16 v[KT * GST];
+struct SmemB {  // swizzled tiles
+  f16 k1[KT * D];
+  f16 k2[KT * D];
+  f16 v[KT * DV];
 };
 
 // A key tile is staged global -> registers -> LDS in two halves, each loaded
-// while one 32-key sub-tile of the previous tile is computed: K1 and K2, then
-// V (v1s::TileLoader's half-tile loads: bounded buffer loads, so keys past
-// the end read as zeros).
-// Registers -> LDS: fp16 times the slices' range shifts.
-__device__ __forceinline__ void store_k12(SmemB &sm, const u32x4 (&r)[4], int tid, const VScale &sck) {
+// while one 32-key sub-tile of the previous tile is computed: the fp16 K1 | K2
+// rows, then the fp16 V rows (both formed once per row by bwd_gconv, range
+// shifts included; bounded buffer loads, so keys past the end read as zeros).
+// Thread tid holds 16-byte pieces tid + NT k (k = 0..3) of the 64 rows of 256
+// bytes: row (tid + NT k) / 16, chunk (tid + NT k) % 16.
+__device__ __forceinline__ void store_k12(SmemB &sm, const u32x4 (&r)[4], int tid) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + NT * j, row = i >> 3, col = (i & 7) * 8;
-    *(f16x8 *)(sm.k1 + row * QST + col) = to_f16x8(r[j], sck);
-    *(f16x8 *)(sm.k2 + row * QST + col) = to_f16x8(r[2 + j], sck);
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k, row = i >> 4, ch = i & 15;
+    *(u32x4 *)(ch < 8 ? sm.k1 + swz_off<D>(row, ch) : sm.k2 + swz_off<D>(row, ch - 8)) = r[k];
   }
 }
 
-__device__ __forceinline__ void store_v(SmemB &sm, const u32x4 (&r)[4], int tid, const VScale &scv) {
+__device__ __forceinline__ void store_v(SmemB &sm, const u32x4 (&r)[4], int tid) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = tid + NT * j, row = i >> 4, col = (i & 15) * 8;
-    *(f16x8 *)(sm.v + row * GST + col) = to_f16x8(r[j], scv);
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + NT * k;
+    *(u32x4 *)(sm.v + swz_off<DV>(i >> 4, i & 15)) = r[k];
   }
 }
 
 // S1^T, S2^T and dP'^T of one 32-key sub-tile (lane = query, registers = keys).
-__device__ __forceinline__ void dq_products(const SmemB &sm, int sub, int krow, int h, const f16x8 *qf1,
+__device__ __forceinline__ void dq_products(const SmemB &sm, int sub, int lk, int lv, const f16x8 *qf1,
                                             const f16x8 *qf2, const f16x8 *gf, f32x16 &s1, f32x16 &s2,
                                             f32x16 &dp) {
   s1 = f32x16{};
   s2 = f32x16{};
   dp = f32x16{};
-  const f16 *ka1 = sm.k1 + (sub * 32 + krow) * QST + 8 * h;
-  const f16 *ka2 = sm.k2 + (sub * 32 + krow) * QST + 8 * h;
-  const f16 *va = sm.v + (sub * 32 + krow) * GST + 8 * h;
+  // Row krow of each 32-row sub-tile, chunk h + 2 kc: lk = swz_off<D>(krow, h),
+  // lv = swz_off<DV>(krow, h) (sub * 32 keeps the row mod 16).
+  const f16 *ka1 = sm.k1 + sub * 32 * D;
+  const f16 *ka2 = sm.k2 + sub * 32 * D;
+  const f16 *va = sm.v + sub * 32 * DV;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
-    s1 = mfma32(*(const f16x8 *)(ka1 + kc * 16), qf1[kc], s1);
-    s2 = mfma32(*(const f16x8 *)(ka2 + kc * 16), qf2[kc], s2);
+    s1 = mfma32(*(const f16x8 *)(ka1 + (lk ^ (16 * kc))), qf1[kc], s1);
+    s2 = mfma32(*(const f16x8 *)(ka2 + (lk ^ (16 * kc))), qf2[kc], s2);
   }
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(va + kc * 16), gf[kc], dp);
+  for (int kc = 0; kc < 8; ++kc) dp = mfma32(*(const f16x8 *)(va + (lv ^ (16 * kc))), gf[kc], dp);
 }
 
 // Elementwise part of one 32 x 32 block of the query-outer kernel (lane =
@@ -911,7 +970,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const int q0 = qt * QB, qw = q0 + wave * 32, my_q = qw + ln;
   const float sg = w.scales[bh * 8 + 0], kap = w.scales[bh * 8 + 1];
   const float kq = w.scales[bh * 8 + 3], kk = w.scales[bh * 8 + 4], kv = w.scales[bh * 8 + 5];
-  const VScale scq((int)kq), sck((int)kk), scv((int)kv);
+  const VScale scq((int)kq);
   // fp16 Q, K, V are Q 2^kq, K 2^kk, V 2^kv: S' = S 2^(kq + kk), dP' = dP 2^(sg + kv).
   const float c = p.scale * kLog2e * exp2i(-(kq + kk));
   const int64_t statb = (int64_t)bh * S;
@@ -940,10 +999,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   const int kend = p.causal ? min(S, q0 + QB) : S;
   const int n_kt = (kend + KT - 1) / KT;
   const int krow = row_perm(ln);
+  const int lk = swz_off<D>(krow, h), lv = swz_off<DV>(krow, h);
+  const TrLane trk = tr_lane<D>(lane);
   const int q_last = qw + 31;
-  const bf16 *k1g = (const bf16 *)p.k1 + b * p.ks_b + hd * p.ks_h;
-  const bf16 *k2g = (const bf16 *)p.k2 + b * p.ks_b + hd * p.ks_h;
-  const bf16 *vg = (const bf16 *)p.v + b * p.vs_b + hd * p.vs_h;
 
   // Last key this query sees (the masks as one threshold per block).
   const int key_lim = p.causal ? min(my_q, S - 1) : S - 1;
@@ -957,13 +1015,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
   // Key tiles double-buffered in LDS; tile kt + 1 is staged in two halves
   // (K1 and K2 during sub-tile 0 of tile kt, V during sub-tile 1), so only
   // one half is held in registers at a time; one barrier per tile.
-  v1s::TileLoader ld;
-  ld.init(k1g, k2g, vg, p.ks_s, p.vs_s, S, tid);
+  const __amdgpu_buffer_rsrc_t rsk = row_rsrc(w.kh + statb * (2 * D), S), rsv = row_rsrc(w.vh + statb * DV, S);
   u32x4 nx[4];
-  ld.load_k12(0, nx);
-  store_k12(smb[0], nx, tid, sck);
-  ld.load_v(0, nx);
-  store_v(smb[0], nx, tid, scv);
+  load_rows(rsk, 0, tid, nx);
+  store_k12(smb[0], nx, tid);
+  load_rows(rsv, 0, tid, nx);
+  store_v(smb[0], nx, tid);
   __syncthreads();
   // One key tile; MASKED applies the causal and key-range masks, which only
   // the tiles from the query tile's start on (causal) and a partial last tile
@@ -976,13 +1033,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       if (more) {
-        if (sub == 0) ld.load_k12((kt + 1) * KT, nx);
-        else ld.load_v((kt + 1) * KT, nx);
+        load_rows(sub == 0 ? rsk : rsv, (kt + 1) * KT, tid, nx);
       }
       const int sb = kt * KT + sub * 32;
       if (sb < S && !(p.causal && sb > q_last)) {
       f32x16 s1, s2, dp;
-      dq_products(sm, sub, krow, h, qf1, qf2, gf, s1, s2, dp);
+      dq_products(sm, sub, lk, lv, qf1, qf2, gf, s1, s2, dp);
       float ds1[16], ds2[16];
       dq_elem<MASKED>(s1, s2, dp, h, c, L1, L2, e1, e2, fold.sig, key_lim - sb, ds1, ds2);
 #pragma unroll
@@ -991,14 +1047,14 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
         const int r0 = sub * 32 + kc2 * 16;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          dq1[dt] = mfma32(tr_operand(sm.k1, QST, r0, dt * 32, lane), b1, dq1[dt]);
-          dq2[dt] = mfma32(tr_operand(sm.k2, QST, r0, dt * 32, lane), b2, dq2[dt]);
+          dq1[dt] = mfma32(tr_operand_swz<D>(sm.k1, trk, r0, dt * 32), b1, dq1[dt]);
+          dq2[dt] = mfma32(tr_operand_swz<D>(sm.k2, trk, r0, dt * 32), b2, dq2[dt]);
         }
       }
       }
       if (more) {
-        if (sub == 0) store_k12(sn, nx, tid, sck);
-        else store_v(sn, nx, tid, scv);
+        if (sub == 0) store_k12(sn, nx, tid);
+        else store_v(sn, nx, tid);
       }
     }
     __syncthreads();
