@@ -13,15 +13,16 @@
 //   dQ_t = s dS_t K,  dK = s sum_t dS_t^T Q_t (over every head reading j)
 //
 // Kernels, in launch order:
-//   v2b_pre    per (batch, pair, token) row: |g| and dlam from the
-//              float32 g and the saved A_o (and |V| of the row's key when the
-//              pair is the first on its KV head);
+//   v2b_pre    per (batch, pair, token) row: |g| and the largest |Q_e|,
+//              |Q_o| (and |K|, |V| of the row's key when the pair is the
+//              first on its KV head);
 //   v2b_scales one workgroup per (batch, KV head): power-of-two scales that
 //              keep the fp16 operands below 2^13: g by the largest row norm
 //              of the pairs on the head, dS by the bound
 //              |dS| <= 2 max|g| max|V| (|A_t| <= max|V|), W = P_e - sigma P_o
 //              (|W| <= 1) by a fixed 2^12;
-//   v2b_gconv  per row: g' = fp16(g 2^sg) and E_t = g' . A_t from that same
+//   v2b_gconv  per row: dlam from the float32 g and the saved A_o;
+//              g' = fp16(g 2^sg) and E_t = g' . A_t from that same
 //              fp16 g' and A_t accumulated with head t's own weights (so
 //              dS = P (dP - E) stays self-consistent where one key dominates a
 //              row and dP - E cancels); also Q_e | Q_o in fp16 for the
@@ -102,30 +103,24 @@ __global__ __launch_bounds__(NT) void v2b_pre_kernel(V2BwdParams p, Ws2 w) {
   const int s = row % p.S;
   const int bp = row / p.S, b = bp / P, pr = bp % P;
   const int c = part * 8;
-  float g[8], ao[8], qe[8], qo[8];
+  float g[8], qe[8], qo[8];
   bf16x8_f32(*(const u32x4 *)((const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + pr * p.ds_h + c), g);
-  const int64_t srow = (((int64_t)b * p.S + s) * P + pr) * D;
-  load_f32x8(p.a_odd + srow + c, ao);
   // Largest magnitudes of the row's Q_e, Q_o (and, once per KV head, K and V):
   // their fp16 copies are scaled by powers of two chosen from these (vrange.h).
   const bf16 *qp = (const bf16 *)p.q + b * p.qs_b + (int64_t)s * p.qs_s + 2 * pr * p.qs_h + c;
   bf16x8_f32(*(const u32x4 *)qp, qe);
   bf16x8_f32(*(const u32x4 *)(qp + p.qs_h), qo);
-  float gg = 0.f, ga = 0.f, qmx = 0.f;
+  float gg = 0.f, qmx = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     gg = fmaf(g[i], g[i], gg);
-    ga = fmaf(g[i], ao[i], ga);
     qmx = fmaxf(qmx, fmaxf(fabsf(qe[i]), fabsf(qo[i])));
   }
   gg = row_sum(gg);
-  ga = row_sum(ga);
   qmx = row_max(qmx);
   if (part == 0) {
-    const float sg = sigmoid_of(p, b, s, pr);
     w.gn[row] = sqrtf(gg);
     w.qm[row] = qmx;
-    p.dlam[((int64_t)b * p.S + s) * P + pr] = -sg * (1.f - sg) * ga;
   }
   const int ppk = p.Hq / p.Hkv / 2, j = pr / ppk;
   if (pr % ppk == 0) {  // uniform over the row's 16 lanes
@@ -218,7 +213,7 @@ __global__ __launch_bounds__(NTS) void v2b_scales_kernel(V2BwdParams p, Ws2 w) {
 }
 
 // ---------------------------------------------------------------------------
-// v2b_gconv: per (b, pair, s) row, g' = fp16(g 2^sg) and E_e = g' . A_e,
+// v2b_gconv: per (b, pair, s) row, dlam, g' = fp16(g 2^sg) and E_e = g' . A_e,
 // E_o = g' . A_o, stored unscaled; also the row's Q_e | Q_o in fp16.
 __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
   const int part = threadIdx.x & (kRowLanes - 1);
@@ -235,6 +230,12 @@ __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
   const int64_t srow = (((int64_t)b * p.S + s) * P + pr) * D;
   load_f32x8(p.a_even + srow + c, ae);
   load_f32x8(p.a_odd + srow + c, ao);
+  // dlam = -sigma (1 - sigma) g . A_o from the float32 g (the fp16 g' would
+  // cost dlam most of its precision where the sum cancels).
+  float ga = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ga = fmaf(g[i], ao[i], ga);
+  ga = row_sum(ga);
   f16x8 gh;
 #pragma unroll
   for (int i = 0; i < 8; ++i) gh[i] = (f16)(g[i] * f);
@@ -258,6 +259,8 @@ __global__ __launch_bounds__(NT) void v2b_gconv_kernel(V2BwdParams p, Ws2 w) {
     const float un = fast_exp2(-sg);
     w.ee[row] = ee * un;
     w.eo[row] = eo * un;
+    const float sig = sigmoid_of(p, b, s, pr);
+    p.dlam[((int64_t)b * p.S + s) * P + pr] = -sig * (1.f - sig) * ga;
   }
 }
 
