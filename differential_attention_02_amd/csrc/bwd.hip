@@ -16,17 +16,17 @@
 //   dlq2 = -dlam e^be lk2, dlk2 = -dlam e^be lq2.
 //
 // Kernels, in launch order:
-//   bwd_pre    per query row: |g|, |V_row| and the row's share -g.A2 of
-//              dL/dlambda from float32 g (formed from dY, the saved O and
-//              rstd; never stored) and the forward's float32 A2 (the sum over
-//              rows cancels by orders of magnitude, so it takes float32 g
-//              rather than the fp16 copy the matrix products use);
+//   bwd_pre    per query row: |g| (g formed from dY, the saved O and rstd;
+//              never stored), |V_row| and the row's largest |Q|, |K|, |V|;
 //   bwd_scales one workgroup per (batch, head): power-of-two scales that keep
 //              the fp16 operands below 2^13 (g by its largest row norm; dS by
 //              the bound |dS| <= max(1,|lambda|) (|g| |V| + |E|) <= 2 max(1,|lambda|)
-//              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|), and the
-//              (batch, head) sum of the rows' dL/dlambda shares (fixed order);
-//   bwd_gconv  per row: g formed again as in bwd_pre, g' = fp16(g 2^sg) and
+//              max|g| max|V|; W = P1 - lambda P2 by 1 + |lambda|);
+//   bwd_gconv  per row: g formed again as in bwd_pre; the row's share -g.A2
+//              of dL/dlambda from that float32 g and the forward's float32 A2
+//              (the sum over rows cancels by orders of magnitude, so it takes
+//              float32 g rather than the fp16 copy the matrix products use);
+//              g' = fp16(g 2^sg) and
 //              E_m = g' . A_m (A2 saved by the forward, A1 = O + lambda A2):
 //              from the same fp16 g' the matrix products use, E equals
 //              sum_j P_m dP' up to float32 rounding, so dS = P (dP - E) stays
@@ -44,8 +44,10 @@
 //              elementwise work runs under the matrix products of its
 //              neighbours.  Recomputing rather than accumulating dQ with
 //              atomics keeps every result deterministic;
-//   bwd_lambda one workgroup: dL/dlambda = sum of the row shares in a fixed
-//              order, then the chain rule into the four lambda vectors.
+//   bwd_dlsum  one workgroup per (batch, head): the sum of its rows' shares
+//              in a fixed order;
+//   bwd_lambda one workgroup: dL/dlambda = sum of the (batch, head) sums in a
+//              fixed order, then the chain rule into the four lambda vectors.
 // Matrix-core operands are fp16 with float32 accumulation: bf16 rounding of g,
 // W and dS alone would spend most of the bf16 error budget.  Q, K and V enter
 // fp16 times powers of two 2^kq, 2^kk, 2^kv chosen per (batch, head) from
@@ -136,7 +138,7 @@ __device__ __forceinline__ void row_grad(const BwdParams &p, int b, int h, int s
 }
 
 // bwd_pre: row norms of g (the gradient reaching the pre-norm output O) and
-// V, the row's lambda share -g . A2, and the row's largest |Q|, |K|, |V|
+// V, and the row's largest |Q|, |K|, |V|
 // (their fp16 copies are scaled by powers of two chosen from these, vrange.h).
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   const int part = threadIdx.x & (kRowLanes - 1);
@@ -148,19 +150,17 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   const int bh = row / p.S;
   const int b = bh / p.H, h = bh % p.H;
   const int c = part * 8;
-  float dy[8], v[8], o[8], a2[8], g[8];
+  float dy[8], v[8], o[8], g[8];
   bf16x8_f32(*(const u32x4 *)((const bf16 *)p.dout + b * p.ds_b + (int64_t)s * p.ds_s + h * p.ds_h + c), dy);
   bf16x8_f32(*(const u32x4 *)((const bf16 *)p.v + b * p.vs_b + (int64_t)s * p.vs_s + h * p.vs_h + c), v);
   const int64_t srow = ((int64_t)b * p.S + s) * p.H + h;   // saves are [B, S, H, DV]
   load_f32x8(p.o_pre + srow * DV + c, o);
-  load_f32x8(p.a2 + srow * DV + c, a2);
   row_grad(p, b, h, s, dy, o, g);
-  float gn = 0.f, vn = 0.f, ga = 0.f, vm = 0.f;
+  float gn = 0.f, vn = 0.f, vm = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     gn = fmaf(g[i], g[i], gn);
     vn = fmaf(v[i], v[i], vn);
-    ga = fmaf(g[i], a2[i], ga);
     vm = fmaxf(vm, fabsf(v[i]));
   }
   // Q1 | Q2 and K1 | K2: lanes 0..7 the first (64 channels), 8..15 the second.
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
   }
   gn = row_sum(gn);
   vn = row_sum(vn);
-  ga = row_sum(ga);
   qm = row_max(qm);
   km = row_max(km);
   vm = row_max(vm);
@@ -186,7 +185,6 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdParams p, Ws w) {
     if (part == 0) {
       w.gnorm[row] = sqrtf(gn);
       w.vnorm[row] = sqrtf(vn);
-      w.dlam_row[row] = -ga;
       *(f32x4 *)(w.amax + row * 4) = f32x4{qm, km, vm, 0.f};
     }
   }
@@ -217,32 +215,29 @@ __device__ __forceinline__ float tree_max(const float *v) {
 }
 
 __global__ __launch_bounds__(NTS) void bwd_scales_kernel(BwdParams p, Ws w) {
-  __shared__ float red[6][NWS];
+  __shared__ float red[5][NWS];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float lam = wave_lambda(p.lq1, p.lk1, p.lq2, p.lk2, p.lambda_dim, p.lambda_fixed, p.lambda_init);
   const int64_t base = (int64_t)bh * p.S;
-  float gm = 0.f, vm = 0.f, dl = 0.f;
+  float gm = 0.f, vm = 0.f;
   f32x4 am = {0.f, 0.f, 0.f, 0.f};
   for (int s = tid; s < p.S; s += NTS) {
     gm = fmaxf(gm, w.gnorm[base + s]);
     vm = fmaxf(vm, w.vnorm[base + s]);
-    dl += w.dlam_row[base + s];
     const f32x4 a = *(const f32x4 *)(w.amax + (base + s) * 4);
     am = f32x4{fmaxf(am[0], a[0]), fmaxf(am[1], a[1]), fmaxf(am[2], a[2]), 0.f};
   }
   for (int o = 32; o > 0; o >>= 1) {
     gm = fmaxf(gm, __shfl_xor(gm, o));
     vm = fmaxf(vm, __shfl_xor(vm, o));
-    dl += __shfl_xor(dl, o);
 #pragma unroll
     for (int i = 0; i < 3; ++i) am[i] = fmaxf(am[i], __shfl_xor(am[i], o));
   }
   if (lane == 0) {
     red[0][wave] = gm;
     red[1][wave] = vm;
-    red[2][wave] = dl;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) red[3 + i][wave] = am[i];
+    for (int i = 0; i < 3; ++i) red[2 + i][wave] = am[i];
   }
   __syncthreads();
   if (tid == 0) {
@@ -250,8 +245,7 @@ __global__ __launch_bounds__(NTS) void bwd_scales_kernel(BwdParams p, Ws w) {
     vm = tree_max(red[1]);
     float ks[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) ks[i] = (float)v_shift_of_max(__float_as_uint(tree_max(red[3 + i])) >> 16);
-    w.dlam_bh[bh] = tree_sum(red[2]);
+    for (int i = 0; i < 3; ++i) ks[i] = (float)v_shift_of_max(__float_as_uint(tree_max(red[2 + i])) >> 16);
     const float al = fmaxf(1.f, fabsf(lam));
     const float sg = gm > 0.f ? fminf(fmaxf(floorf(13.f - log2f(gm)), -60.f), 60.f) : 0.f;
     const float x = 2.f * al * gm * vm;  // bound on |dS| before scaling by 2^sg
@@ -291,6 +285,12 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
   load_f32x8(p.o_pre + srow * DV + c, o);
   load_f32x8(p.a2 + srow * DV + c, a2);
   row_grad(p, b, h, s, dy, o, g);
+  // The row's share -g . A2 of dL/dlambda, from the float32 g (the sum over
+  // rows cancels by orders of magnitude; the fp16 g' would not do).
+  float ga = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ga = fmaf(g[i], a2[i], ga);
+  ga = row_sum(ga);
   f16x8 gh;
 #pragma unroll
   for (int i = 0; i < 8; ++i) gh[i] = (f16)(g[i] * f);
@@ -326,6 +326,7 @@ __global__ __launch_bounds__(NT) void bwd_gconv_kernel(BwdParams p, Ws w) {
       const float un = exp2i(-sg);
       w.e1[row] = e1 * un;
       w.e2[row] = e2 * un;
+      w.dlam_row[row] = -ga;
     }
   }
 }
@@ -1081,8 +1082,24 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdParams p, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
+// bwd_dlsum: one workgroup of NTS threads per (b, h): the (batch, head) sum of
+// the rows' dL/dlambda shares, in a fixed order (strided per thread, then the
+// wave, then the waves' tree).
+__global__ __launch_bounds__(NTS) void bwd_dlsum_kernel(BwdParams p, Ws w) {
+  __shared__ float red[NWS];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t base = (int64_t)bh * p.S;
+  float dl = 0.f;
+  for (int s = tid; s < p.S; s += NTS) dl += w.dlam_row[base + s];
+  for (int o = 32; o > 0; o >>= 1) dl += __shfl_xor(dl, o);
+  if (lane == 0) red[wave] = dl;
+  __syncthreads();
+  if (tid == 0) w.dlam_bh[bh] = tree_sum(red);
+}
+
+// ---------------------------------------------------------------------------
 // bwd_lambda: one workgroup; dL/dlambda = sum of the (batch, head) sums that
-// bwd_scales formed, in a fixed order, then the chain rule into the four
+// bwd_dlsum formed, in a fixed order, then the chain rule into the four
 // lambda vectors.
 __global__ __launch_bounds__(NT) void bwd_lambda_kernel(BwdParams p, Ws w) {
   __shared__ float red[NT / 64];
@@ -1133,6 +1150,7 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t st) {
   const int n_qt = (p.S + QB - 1) / QB;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_qt * p.B * p.H), dim3(NT), 0, st, p, w);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.S + KVB - 1) / KVB * p.B * p.H), dim3(NT), 0, st, p, w);
+  hipLaunchKernelGGL(bwd_dlsum_kernel, dim3(p.B * p.H), dim3(NTS), 0, st, p, w);
   hipLaunchKernelGGL(bwd_lambda_kernel, dim3(1), dim3(NT), 0, st, p, w);
   return hipGetLastError();
 }
