@@ -463,7 +463,9 @@ __global__ __launch_bounds__(NT, SAVE ? 1 : 2) void fwd_v2_kernel(V2FwdParams p)
 // mask inside them), every other weight being zero.  Entries outside the
 // sequence, past the query tile (causal) or not above the previous accepted
 // entry are skipped; a row that sees no key gets zeros.  Same two passes
-// and staging as the dense kernel, walking the list instead of 0..n.
+// and staging as the dense kernel, walking the list instead of 0..n: the
+// listed tiles that no row of the workgroup needs masked first, without mask
+// arithmetic, then the rest.
 __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   __shared__ SmemV2 sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -509,19 +511,27 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   const int krow = k_row_perm(ln);
   // The valid list entries (tile index in [0, kt_lim)), compacted into LDS.
   __shared__ int tiles[kMaxBlocks];
-  __shared__ int n_tiles;
+  __shared__ int n_tiles, n_open;
+  // Tiles below n_full need no mask for any row of the workgroup (as in the
+  // dense kernel); being ascending, they lead the compacted list.
+  const int n_full = min(causal ? (q0 + 1) / BN : n_ktot, S / BN);
   for (int i = tid; i < cnt; i += NT) tiles[i] = lst[i];  // all threads fetch, one thread compacts in place
   __syncthreads();
   if (tid == 0) {  // ascending, in range; entries not above the last accepted one are ignored
-    int n = 0, last = -1;
+    int n = 0, last = -1, m = 0;
     for (int i = 0; i < cnt; ++i) {
       const int t = tiles[i];
-      if (t > last && t < kt_lim) tiles[n++] = last = t;
+      if (t > last && t < kt_lim) {
+        tiles[n++] = last = t;
+        m += t < n_full;
+      }
     }
     n_tiles = n;
+    n_open = m;
   }
   __syncthreads();
   const int n_valid = __builtin_amdgcn_readfirstlane(n_tiles);
+  const int n_unm = __builtin_amdgcn_readfirstlane(n_open);
   // fp16 V is V 2^vk over every key row the list may name (see vrange.h).
   const int vk = v_shift(p.vpart + ((int64_t)b * p.Hkv + j) * vrange_chunks(S), vrange_chunks(min(S, kt_lim * BN)));
   const VScale vsc(vk);
@@ -532,15 +542,21 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   ld.load((n_valid > 0 ? tiles[0] : 0) * BN, false, nxt);
   store_tile(sm[0], nxt, tid, false, vsc);
   __syncthreads();
-  for (int n = 0; n < n_valid; ++n) {
+  auto p1 = [&](auto masked, int n) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
     const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
     ld.load(nk * BN, false, nxt);
     sched_fence();
-    pass1_tile<true>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
+    pass1_tile<MASKED>(sm[n & 1], cur * BN, krow, h, qe, qo, c, me, le, mo, lo, S, causal, qw, my_q);
     sched_fence();
     store_tile(sm[(n + 1) & 1], nxt, tid, false, vsc);
     __syncthreads();
+  };
+  {
+    int n = 0;
+    for (; n < n_unm; ++n) p1(std::false_type{}, n);
+    for (; n < n_valid; ++n) p1(std::true_type{}, n);
   }
   float Me, Le, Mo, Lo;
   lse_finish(me, le, Me, Le);
@@ -556,16 +572,22 @@ __global__ __launch_bounds__(NT, 2) void fwd_v2_sparse_kernel(V2FwdParams p) {
   ld.load((n_valid > 0 ? tiles[0] : 0) * BN, true, nxt);
   store_tile(sm[0], nxt, tid, true, vsc);
   __syncthreads();
-  for (int n = 0; n < n_valid; ++n) {
+  auto p2 = [&](auto masked, int n) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = __builtin_amdgcn_readfirstlane(tiles[n]);
     const int nk = __builtin_amdgcn_readfirstlane(n + 1 < n_valid ? tiles[n + 1] : cur);
     ld.load(nk * BN, true, nxt);
     sched_fence();
-    pass2_tile<true, false>(sm[n & 1], cur * BN, krow, lane, qe, qo, c, sig, Les, Los, 1.f, 1.f, o, dummy, dummy, S,
-                            causal, qw, my_q);
+    pass2_tile<MASKED, false>(sm[n & 1], cur * BN, krow, lane, qe, qo, c, sig, Les, Los, 1.f, 1.f, o, dummy, dummy,
+                              S, causal, qw, my_q);
     sched_fence();
     store_tile(sm[(n + 1) & 1], nxt, tid, true, vsc);
     __syncthreads();
+  };
+  {
+    int n = 0;
+    for (; n < n_unm; ++n) p2(std::false_type{}, n);
+    for (; n < n_valid; ++n) p2(std::true_type{}, n);
   }
 
   if (qok) {
