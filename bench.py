@@ -78,7 +78,7 @@ _CSRC = "differential_attention_02_amd/csrc/"
 FWD_SOURCES = [_CSRC + f for f in ("fwd_onepass.hip", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
 V2P_SOURCES = [_CSRC + f for f in ("fwd_v2.hip", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
 DEC_SOURCES = [_CSRC + f for f in ("decode.hip", "common.h")]
-FP8_SOURCES = [_CSRC + f for f in ("fwd_fp8.hip", "v1_stage.h", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
+FP8_SOURCES = [_CSRC + f for f in ("fwd_fp8.hip", "vrange.hip", "vrange.h", "attn_tile.h", "common.h")]
 BWD_SOURCES = [_CSRC + f for f in ("bwd.hip", "vrange.h", "common.h")]
 V2B_SOURCES = [_CSRC + f for f in ("bwd_v2.hip", "vrange.h", "common.h")]
 # fp8 leg: per pair, the two score products (256 flop) run at the fp8 peak and the PV products
